@@ -1,0 +1,134 @@
+"""CPU fp64 oracle for the gated delta rule -- TEST INFRASTRUCTURE ONLY.
+
+Only the test suite, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The GPU library never loads it, and it
+imports nothing from the GPU library: the two share no code.
+
+The arithmetic lives in ``gdn_oracle.c`` (plain C, fp64, the sequential
+per-token recurrence of the Qwen3.5-9B-npu model page, "How it works" ->
+"Gated DeltaNet on the NPU").  This module only marshals arrays: it upcasts
+whatever it is given (bf16/fp32 tensors or arrays) to contiguous fp64 and calls
+the C code through ctypes.
+
+Parity pins for every function here are in ``tests/test_oracle_pins.py``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH, build as _build
+
+__all__ = ["prefill", "decode", "default_threads", "load"]
+
+_lib = None
+
+
+def load():
+    """Load (building once if absent) the oracle's shared library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        _build()
+    lib = ctypes.CDLL(LIB_PATH)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int64)
+    i64 = ctypes.c_int64
+    lib.gdn_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, ip, i64, i64, i64,
+                                       i64, i64, dp, dp, ctypes.c_int]
+    lib.gdn_oracle_prefill.restype = ctypes.c_int
+    lib.gdn_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
+                                      i64, dp, ctypes.c_int]
+    lib.gdn_oracle_decode.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    """Threads the oracle uses by default: every core this process may run on."""
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover - non-Linux
+        return os.cpu_count() or 1
+
+
+def _f64(x):
+    """Exact fp64 copy of a numpy array or a (CPU or device) torch tensor."""
+    if x is None:
+        return None
+    if not isinstance(x, np.ndarray) and hasattr(x, "detach"):
+        x = x.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a, ctype=ctypes.c_double):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads=None):
+    """Run the per-token recurrence over whole sequences.
+
+    q, k: [B, T, H, dk]; v: [B, T, H, dv]; g, beta: [B, T, H].
+    S0: [N, H, dk, dv] or None (zero state).
+    cu_seqlens: None (N = B sequences of length T) or [N+1] int offsets into
+    the packed token axis (then B must be 1 and T = cu_seqlens[-1]).
+    Returns (O [B, T, H, dv], S_T [N, H, dk, dv]) as fp64 numpy arrays.
+    """
+    q, k, v, g, beta, S0 = map(_f64, (q, k, v, g, beta, S0))
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != (B, T, H) or g.shape != (B, T, H) \
+            or beta.shape != (B, T, H):
+        raise ValueError("oracle.prefill: inconsistent shapes")
+    cu = None
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("oracle.prefill: packed batches need B == 1")
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu().numpy() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int64))
+        N = cu.shape[0] - 1
+    else:
+        N = B
+    if S0 is not None and S0.shape != (N, H, dk, dv):
+        raise ValueError("oracle.prefill: S0 must be [N, H, dk, dv]")
+    O = np.zeros((B, T, H, dv), dtype=np.float64)
+    S_T = np.zeros((N, H, dk, dv), dtype=np.float64)
+    rc = load().gdn_oracle_prefill(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+        _ptr(cu, ctypes.c_int64), N, T, H, dk, dv, _ptr(O), _ptr(S_T),
+        nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle.prefill failed with code {rc}")
+    return O, S_T
+
+
+def decode(q, k, v, g, beta, S, nthreads=None):
+    """Run consecutive one-token steps on a batch of states.
+
+    q, k: [steps, B, H, dk] (or [B, H, dk] for one step); v likewise with dv;
+    g, beta: [steps, B, H] (or [B, H]); S: [B, H, dk, dv].
+    Returns (o with v's shape, S after the last step) as fp64 numpy arrays;
+    the input S is not modified.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    S = _f64(S).copy()
+    single = q.ndim == 3
+    if single:
+        q, k, v, g, beta = (x[None] for x in (q, k, v, g, beta))
+    steps, B, H, dk = q.shape
+    dv = v.shape[-1]
+    if S.shape != (B, H, dk, dv) or g.shape != (steps, B, H) or beta.shape != g.shape:
+        raise ValueError("oracle.decode: inconsistent shapes")
+    o = np.zeros((steps, B, H, dv), dtype=np.float64)
+    rc = load().gdn_oracle_decode(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S), steps, B, H, dk,
+        dv, _ptr(o), nthreads or default_threads())
+    if rc != 0:
+        raise ValueError(f"oracle.decode failed with code {rc}")
+    return (o[0] if single else o), S

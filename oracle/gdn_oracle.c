@@ -1,0 +1,232 @@
+/*
+ * gdn_oracle.c -- CPU reference (the oracle) for the gated delta rule.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the GPU product path may link, load
+ * or call this file; only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code with the HIP library.
+ *
+ * What it computes: the sequential per-token gated delta rule as the
+ * Qwen3.5-9B-npu model page states it ("How it works", paragraph
+ * "Gated DeltaNet on the NPU", the four-line per-token update that the
+ * exported Loop applies):
+ *
+ *     S   <- S * exp(g_t)                 (decay the whole state first)
+ *     kv  <- S^T k_t                      (read with the decayed state)
+ *     S   <- S + k_t (outer) ((v_t - kv) * beta_t)
+ *     o_t <- S^T q_t                      (read after the write)
+ *
+ * S is dk x dv, row index over the key dimension and column index over the
+ * value dimension (kv = S^T k has dv entries).  Everything is IEEE fp64 with
+ * plain loops: no BLAS, no SIMD intrinsics, no fast-math, no reordering of the
+ * four steps.  The chunkwise-parallel prompt form and the one-token matrix form
+ * on the same page reach this same result up to rounding order; the oracle is
+ * deliberately the plain definition, not either faster form.
+ *
+ * Parallelism: independent (sequence, head) units are handed to a pthread pool
+ * through an atomic counter.  Each unit is computed start to finish by one
+ * thread, so the result does not depend on the thread count.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* One token of the recurrence on a dk x dv state (row-major, S[i*dv + j]).
+ * kv is caller scratch of dv doubles. */
+static void gdn_token(double *S, int64_t dk, int64_t dv,
+                      const double *q, const double *k, const double *v,
+                      double g, double beta, double *o, double *kv)
+{
+    const double decay = exp(g);
+    for (int64_t i = 0; i < dk; ++i)            /* S <- S * exp(g_t) */
+        for (int64_t j = 0; j < dv; ++j)
+            S[i * dv + j] *= decay;
+
+    for (int64_t j = 0; j < dv; ++j) {          /* kv <- S^T k_t */
+        double acc = 0.0;
+        for (int64_t i = 0; i < dk; ++i)
+            acc += S[i * dv + j] * k[i];
+        kv[j] = acc;
+    }
+
+    for (int64_t i = 0; i < dk; ++i)            /* S <- S + k_t (x) ((v_t - kv) beta_t) */
+        for (int64_t j = 0; j < dv; ++j)
+            S[i * dv + j] += k[i] * ((v[j] - kv[j]) * beta);
+
+    for (int64_t j = 0; j < dv; ++j) {          /* o_t <- S^T q_t */
+        double acc = 0.0;
+        for (int64_t i = 0; i < dk; ++i)
+            acc += S[i * dv + j] * q[i];
+        o[j] = acc;
+    }
+}
+
+/* A unit is one (sequence, head): a run of ntok tokens read with fixed strides
+ * (in elements) between consecutive tokens, and the state it carries. */
+typedef struct {
+    const double *q, *k, *v, *g, *beta;
+    double *o;
+    int64_t ntok;
+    int64_t s_qk, s_v, s_gb;   /* token strides for q/k, v/o, g/beta */
+    const double *S_in;        /* NULL: zero initial state */
+    double *S_out;             /* dk x dv; may equal S_in */
+} unit_t;
+
+typedef struct {
+    unit_t *units;
+    int64_t nunits, dk, dv;
+    int64_t next;              /* atomic work counter */
+    int failed;
+} pool_t;
+
+static void run_unit(const unit_t *u, int64_t dk, int64_t dv, double *S, double *kv)
+{
+    if (u->S_in)
+        memcpy(S, u->S_in, (size_t)(dk * dv) * sizeof(double));
+    else
+        memset(S, 0, (size_t)(dk * dv) * sizeof(double));
+    for (int64_t t = 0; t < u->ntok; ++t)
+        gdn_token(S, dk, dv, u->q + t * u->s_qk, u->k + t * u->s_qk,
+                  u->v + t * u->s_v, u->g[t * u->s_gb], u->beta[t * u->s_gb],
+                  u->o + t * u->s_v, kv);
+    memcpy(u->S_out, S, (size_t)(dk * dv) * sizeof(double));
+}
+
+static void *worker(void *arg)
+{
+    pool_t *p = (pool_t *)arg;
+    double *S = (double *)malloc((size_t)(p->dk * p->dv) * sizeof(double));
+    double *kv = (double *)malloc((size_t)p->dv * sizeof(double));
+    if (!S || !kv) {
+        __atomic_store_n(&p->failed, 1, __ATOMIC_SEQ_CST);
+        free(S);
+        free(kv);
+        return NULL;
+    }
+    for (;;) {
+        int64_t u = __atomic_fetch_add(&p->next, 1, __ATOMIC_SEQ_CST);
+        if (u >= p->nunits)
+            break;
+        run_unit(&p->units[u], p->dk, p->dv, S, kv);
+    }
+    free(S);
+    free(kv);
+    return NULL;
+}
+
+static int run_pool(unit_t *units, int64_t nunits, int64_t dk, int64_t dv, int nthreads)
+{
+    pool_t p = {units, nunits, dk, dv, 0, 0};
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > nunits)
+        nthreads = nunits > 0 ? (int)nunits : 1;
+    pthread_t *th = (pthread_t *)malloc((size_t)nthreads * sizeof(pthread_t));
+    if (!th)
+        return -2;
+    int started = 0;
+    for (int i = 0; i < nthreads; ++i) {
+        if (pthread_create(&th[i], NULL, worker, &p) != 0)
+            break;
+        ++started;
+    }
+    if (started == 0)
+        worker(&p);    /* no threads available: run inline */
+    for (int i = 0; i < started; ++i)
+        pthread_join(th[i], NULL);
+    free(th);
+    return p.failed ? -2 : 0;
+}
+
+/*
+ * Whole-sequence run (the prompt case).
+ *   q, k : [B, T, H, dk]      v, O : [B, T, H, dv]      g, beta : [B, T, H]
+ *   S0   : [N, H, dk, dv] or NULL (zero state)           S_T : [N, H, dk, dv]
+ * Without cu_seqlens there are N = B sequences of T tokens each.  With
+ * cu_seqlens ([N+1] offsets, non-decreasing, cu_seqlens[N] = T) the tokens are
+ * one packed batch (B = 1) and sequence n owns tokens cu_seqlens[n] ..
+ * cu_seqlens[n+1]-1; each sequence starts from its own S0 slice.
+ * S_T may equal S0 (in-place update).  Returns 0, -1 for bad arguments, -2 for
+ * an allocation failure.
+ */
+int gdn_oracle_prefill(const double *q, const double *k, const double *v,
+                       const double *g, const double *beta, const double *S0,
+                       const int64_t *cu_seqlens, int64_t N, int64_t T,
+                       int64_t H, int64_t dk, int64_t dv, double *O,
+                       double *S_T, int nthreads)
+{
+    if (N < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || !S_T)
+        return -1;
+    if (cu_seqlens) {
+        if (cu_seqlens[0] != 0 || cu_seqlens[N] != T)
+            return -1;
+        for (int64_t n = 0; n < N; ++n)
+            if (cu_seqlens[n + 1] < cu_seqlens[n])
+                return -1;
+    }
+    const int64_t nunits = N * H;
+    unit_t *units = (unit_t *)calloc((size_t)(nunits > 0 ? nunits : 1), sizeof(unit_t));
+    if (!units)
+        return -2;
+    for (int64_t n = 0; n < N; ++n) {
+        /* first token of the sequence, counted in rows of H heads */
+        const int64_t start = cu_seqlens ? cu_seqlens[n] : n * T;
+        const int64_t len = cu_seqlens ? cu_seqlens[n + 1] - cu_seqlens[n] : T;
+        for (int64_t h = 0; h < H; ++h) {
+            unit_t *u = &units[n * H + h];
+            u->q = q + (start * H + h) * dk;
+            u->k = k + (start * H + h) * dk;
+            u->v = v + (start * H + h) * dv;
+            u->o = O + (start * H + h) * dv;
+            u->g = g + start * H + h;
+            u->beta = beta + start * H + h;
+            u->ntok = len;
+            u->s_qk = H * dk;
+            u->s_v = H * dv;
+            u->s_gb = H;
+            u->S_in = S0 ? S0 + (n * H + h) * dk * dv : NULL;
+            u->S_out = S_T + (n * H + h) * dk * dv;
+        }
+    }
+    int rc = run_pool(units, nunits, dk, dv, nthreads);
+    free(units);
+    return rc;
+}
+
+/*
+ * Consecutive one-token steps on a batch of states (the decode case).
+ *   q, k : [steps, B, H, dk]   v, o : [steps, B, H, dv]   g, beta : [steps, B, H]
+ *   S    : [B, H, dk, dv], updated in place across all steps.
+ * Step s of unit (b, h) reads token s of that unit; this is the same update as
+ * above applied once per call.
+ */
+int gdn_oracle_decode(const double *q, const double *k, const double *v,
+                      const double *g, const double *beta, double *S,
+                      int64_t steps, int64_t B, int64_t H, int64_t dk,
+                      int64_t dv, double *o, int nthreads)
+{
+    if (steps < 0 || B < 0 || H <= 0 || dk <= 0 || dv <= 0 || !S)
+        return -1;
+    const int64_t nunits = B * H;
+    unit_t *units = (unit_t *)calloc((size_t)(nunits > 0 ? nunits : 1), sizeof(unit_t));
+    if (!units)
+        return -2;
+    for (int64_t u = 0; u < nunits; ++u) {
+        units[u].q = q + u * dk;
+        units[u].k = k + u * dk;
+        units[u].v = v + u * dv;
+        units[u].o = o + u * dv;
+        units[u].g = g + u;
+        units[u].beta = beta + u;
+        units[u].ntok = steps;
+        units[u].s_qk = nunits * dk;
+        units[u].s_v = nunits * dv;
+        units[u].s_gb = nunits;
+        units[u].S_in = S + u * dk * dv;
+        units[u].S_out = S + u * dk * dv;
+    }
+    int rc = run_pool(units, nunits, dk, dv, nthreads);
+    free(units);
+    return rc;
+}
