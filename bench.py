@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of libgdn on one MI355X: decode state GB/s and prompt-form tokens/s.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one gdn_decode_step call over the batched-decode workload (B = 64
+sequences x H = 16 heads, bf16 q/k/v, fp32 g/beta, fp32 state [64,16,128,128]
+updated in place), each step with its own freshly drawn token.  W untimed
+steps run first; then exactly K steps are timed between two device
+synchronisations, launched as one captured HIP graph so that host launch cost
+does not pace the GPU.  `value` is the state traffic those K steps move
+(2 x 64 KiB per head-step) per second.
+
+The same run times the prompt form (gdn_chunk_prefill) on the large prefill
+(B=8, H=32, T=16384, chunk 64, bf16, zero S0) and on the long, packed
+variable-length and speculative-verify workloads, and reports their tokens/s
+and roofline fractions under "prefill".  All inputs are seeded synthetic draws
+made on the device before any timing starts.
+
+The CPU oracle is timed on a bounded sample of the decode workload (and of the
+large prefill) on this host's cores as `cpu_baseline`; it is a reported
+baseline, not a target.  One JSON line is printed.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
+BF16_PEAK = 2.5166e15        # flop/s, dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+DK = DV = 128
+STATE_BYTES = DK * DV * 4    # one fp32 head state
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(lengths, H, C):
+    """Algorithmic flops of the chunk form: per chunk of c real tokens,
+    6 c dk dv (state products and the state update) + 2 c^2 (dk + dv) (the
+    in-chunk triangular products, counted once)."""
+    total = 0
+    for L in lengths:
+        full, tail = divmod(int(L), C)
+        for c in [C] * full + ([tail] if tail else []):
+            total += 6 * c * DK * DV + 2 * c * c * (DK + DV)
+    return total * H
+
+
+def prefill_bytes(tokens, H, n_seqs, s0, esz=2):
+    """q, k, v, O rows (esz bytes per element) + g, beta (fp32) per head-token,
+    plus one state read (if S0) and one state write per (sequence, head)."""
+    per_tok = 4 * DK * esz + 8
+    return tokens * H * per_tok + n_seqs * H * STATE_BYTES * (2 if s0 else 1)
+
+
+def decode_bytes(units, esz=2):
+    """State read + write, plus q, k, v, o rows and g, beta, per head-step."""
+    return units * (2 * STATE_BYTES + 4 * DK * esz + 8)
+
+
+def roofline(bound, achieved, peak, unit, traffic=None):
+    return {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": traffic}
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "linear_attention_recurrence_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_tag, digest):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k_, v_ = line.split("=", 1)
+            vals[k_.strip()] = v_.strip()
+    if vals.get("source_digest") != digest:
+        return None
+    try:
+        return float(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def bench_decode(torch, gdn, inputs, steps, warmup, cold):
+    w = inputs.batched_decode(device="cuda", steps=steps)
+    B, H = w.meta["B"], w.meta["H"]
+    units = B * H
+    nbuf = 8 if cold else 1
+    states = [w.S0.clone() for _ in range(nbuf)]
+    outs = torch.empty_like(w.v)
+    # warmup (eager) on a scratch state
+    scratch = w.S0.clone()
+    for i in range(warmup):
+        s = i % steps
+        gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], scratch, o=outs[s])
+    torch.cuda.synchronize()
+    # capture the K steps once
+    graph = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    with torch.cuda.graph(graph, stream=cap):
+        for s in range(steps):
+            gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s],
+                                states[s % nbuf], o=outs[s])
+    torch.cuda.synchronize()
+    graph.replay()          # untimed replay (first-replay setup cost)
+    torch.cuda.synchronize()
+    for st in states:
+        st.copy_(w.S0)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    gpu_ms = e0.elapsed_time(e1)
+    # eager launches of the same K steps, for reference
+    for st in states:
+        st.copy_(w.S0)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for s in range(steps):
+        gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], states[s % nbuf],
+                            o=outs[s])
+    torch.cuda.synchronize()
+    eager = time.perf_counter() - t1
+    return dict(units=units, wall_s=wall, gpu_ms=gpu_ms, eager_s=eager, workload=w)
+
+
+def bench_prefill(torch, gdn, w, iters, warmup):
+    O = torch.empty_like(w.v)
+    N = w.q.shape[0] if w.cu_seqlens is None else w.cu_seqlens.numel() - 1
+    S_T = torch.empty((N, w.q.shape[2], DK, DV), dtype=torch.float32, device="cuda")
+    for _ in range(warmup):
+        gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
+                              O=O, S_T=S_T)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
+                              O=O, S_T=S_T)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    t = statistics.median(times)
+    H = w.q.shape[2]
+    if w.cu_seqlens is None:
+        lengths = [w.q.shape[1]] * w.q.shape[0]
+    else:
+        lengths = w.meta["lengths"]
+    tokens = sum(lengths)
+    esz = w.q.element_size()
+    flops = prefill_flops(lengths, H, w.chunk)
+    nbytes = prefill_bytes(tokens, H, len(lengths), w.S0 is not None, esz)
+    return {
+        "workload": w.name, "tokens": tokens, "heads": H, "chunk": w.chunk,
+        "seconds": t, "tokens_per_s": tokens / t,
+        "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
+        "alg_flops": flops, "alg_bytes": nbytes,
+        "roofline": roofline("hbm", nbytes / t / 1e9, HBM_PEAK / 1e9, "GB/s"),
+    }
+
+
+def cpu_baseline_decode(w, target_s=12.0):
+    """The oracle, as it stands, on the first n steps of the decode workload."""
+    import oracle
+    threads = oracle.default_threads()
+    host = lambda x, n: x[:n].cpu()
+    t0 = time.perf_counter()
+    oracle.decode(host(w.q, 1), host(w.k, 1), host(w.v, 1), host(w.g, 1), host(w.beta, 1),
+                  w.S0.cpu(), nthreads=threads)
+    one = max(time.perf_counter() - t0, 1e-3)
+    n = int(max(1, min(w.q.shape[0], target_s / one)))
+    t0 = time.perf_counter()
+    oracle.decode(host(w.q, n), host(w.k, n), host(w.v, n), host(w.g, n), host(w.beta, n),
+                  w.S0.cpu(), nthreads=threads)
+    dt = time.perf_counter() - t0
+    units = w.q.shape[1] * w.q.shape[2]
+    return {"value": n * units * 2 * STATE_BYTES / dt / 1e9, "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"first {n} steps of the B=64 x H=16 decode batch "
+                      f"({dt:.1f} s, fp64, {threads} threads)"}
+
+
+def cpu_baseline_prefill(w, target_units=None):
+    """The oracle on whole (sequence, head) units of the large prefill."""
+    import oracle
+    threads = oracle.default_threads()
+    nu = target_units or threads
+    T = w.q.shape[1]
+    heads = list(range(min(nu, w.q.shape[2])))
+    sl = lambda x: x[0:1, :, heads].cpu()
+    t0 = time.perf_counter()
+    oracle.prefill(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), None, nthreads=threads)
+    dt = time.perf_counter() - t0
+    H = w.q.shape[2]
+    return {"value": len(heads) * T / H / dt, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"sequence 0, heads 0..{len(heads) - 1} of the large prefill "
+                      f"({len(heads)} x {T} head-tokens, {dt:.1f} s), scaled to {H} heads"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill-iters", type=int, default=5)
+    ap.add_argument("--cold", action="store_true",
+                    help="rotate 8 state batches (512 MiB) so the state cannot stay in cache")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from linear_attention_recurrence_02_amd import binding as gdn
+    from linear_attention_recurrence_02_amd import inputs
+    gdn.load_library()
+    torch.cuda.set_device(0)
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name} ({getattr(props, 'gcnArchName', '?')}), "
+        f"{props.multi_processor_count} CUs")
+
+    result = {
+        "metric": "prefill tokens/s (MFMA %) and decode state GB/s (HBM %) on 1 MI355X",
+        "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 io, fp32 state/math",
+        "data": "synthetic (seeded device draws; q,k unit-norm, g=-softplus(N(0,1)), "
+                "beta=sigmoid(N(0,1)), S0~0.1*N(0,1))",
+        "config": {"workload": "batched decode step: B=64 sequences x H=16 heads, "
+                               "dk=dv=128, bf16 q/k/v, fp32 state updated in place",
+                   "global_batch": 64, "heads": 16, "seq_len": 1,
+                   "parallelism": "single GPU"},
+    }
+
+    dec = None
+    if args.only in (None, "decode"):
+        log("decode: generating inputs and capturing the step graph ...")
+        dec = bench_decode(torch, gdn, inputs, args.steps, args.warmup, args.cold)
+        K = args.steps
+        units = dec["units"]
+        state_gbs = K * units * 2 * STATE_BYTES / dec["wall_s"] / 1e9
+        avg_launch = dec["gpu_ms"] / 1e3 / K
+        alg = decode_bytes(units)
+        traffic = read_traffic("decode_bf16_b64h16", source_digest("gdn_decode.hip"))
+        result.update(value=state_gbs, ms_per_step=dec["wall_s"] * 1e3 / K)
+        result["roofline"] = roofline("hbm", alg / avg_launch / 1e9, HBM_PEAK / 1e9, "GB/s",
+                                      traffic)
+        result["decode"] = {
+            "steps_per_s": K / dec["wall_s"],
+            "avg_launch_us": avg_launch * 1e6,
+            "alg_bytes_per_launch": alg,
+            "eager_launch_state_gbs": K * units * 2 * STATE_BYTES / dec["eager_s"] / 1e9,
+            "cold_rotating_8_batches": bool(args.cold),
+        }
+        log(f"decode: {state_gbs:.1f} GB/s state, {avg_launch*1e6:.2f} us/step "
+            f"(eager {dec['eager_s']*1e6/K:.2f} us/step)")
+
+    if args.only in (None, "prefill"):
+        pre = {}
+        for make in (inputs.large_prefill, inputs.long_prefill, inputs.varlen_prefill,
+                     inputs.verify_blocks):
+            w = make(device="cuda")
+            r = bench_prefill(torch, gdn, w, args.prefill_iters, 2)
+            log(f"prefill {r['workload']}: {r['tokens_per_s']:.3e} tok/s, "
+                f"{r['seconds']*1e3:.3f} ms, MFMA {100*r['mfma_frac']:.1f}%, "
+                f"HBM {100*r['hbm_frac']:.1f}%")
+            pre[r["workload"]] = r
+            if w.name == "large_prefill" and not args.no_cpu_baseline:
+                pre[r["workload"]]["cpu_baseline"] = cpu_baseline_prefill(w)
+            del w
+            torch.cuda.empty_cache()
+        result["prefill"] = pre
+
+    if dec is not None and not args.no_cpu_baseline:
+        log("cpu baseline: timing the oracle on a sample of the decode workload ...")
+        result["cpu_baseline"] = cpu_baseline_decode(dec["workload"])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * gdn.h -- libgdn: gated delta-rule linear attention (Gated DeltaNet) on one
+ * AMD Instinct MI355X (gfx950).  Plain C ABI: device pointers, sizes, a HIP
+ * stream handle and an int status.  No allocation, no synchronisation.
+ *
+ * The operation (Qwen3.5-9B-npu model page, "How it works" -> "Gated DeltaNet
+ * on the NPU"): per head, a state S of dk x dv (row index over the key
+ * dimension, column index over the value dimension) is carried through the
+ * tokens of a sequence; for token t
+ *
+ *     S   <- S * exp(g_t)
+ *     kv  <- S^T k_t
+ *     S   <- S + k_t (outer) ((v_t - kv) * beta_t)
+ *     o_t <- S^T q_t
+ *
+ * No 1/sqrt(dk) scale and no normalisation of q or k is applied inside: the
+ * caller passes q and k as they should enter the recurrence.
+ *
+ * Conventions shared by both calls
+ *   - Shapes: dk == dv == 128 (the page's per-head state is 128 x 128); other
+ *     sizes return GDN_ERR_UNSUPPORTED.
+ *   - dtypes: q, k, v and the outputs O/o share io_dtype (GDN_F32 or GDN_BF16);
+ *     g, beta and the states are always fp32.  Outputs in bf16 are rounded to
+ *     nearest even from fp32.
+ *   - Layout: every tensor is dense and row-major in the shape given; base
+ *     pointers of q, k, v, O/o and the states must be 16-byte aligned, g and
+ *     beta 4-byte aligned.
+ *   - Ownership: every pointer is caller-owned device memory.  The library
+ *     allocates nothing, keeps no state between calls and never waits on the
+ *     device, so a call may be captured into a HIP graph.
+ *   - Streams: work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and the call returns at once.  Faults inside a kernel surface at
+ *     the caller's next synchronisation.
+ *   - Errors: arguments are validated on the host before anything is
+ *     enqueued; a rejected call enqueues nothing.  A failed launch returns
+ *     GDN_ERR_HIP.
+ *   - Preconditions not checked: g <= 0 and 0 <= beta <= 1 (the accuracy
+ *     contract assumes them), finite inputs (NaN/Inf propagate).
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, misalignment */
+    GDN_ERR_UNSUPPORTED = 2,   /* dk/dv != 128, chunk not in {16,32,64}, dtype */
+    GDN_ERR_ALIAS = 3,         /* buffers overlap in a way the call forbids */
+    GDN_ERR_HIP = 4            /* the HIP runtime refused the launch */
+} gdn_status;
+
+typedef enum {
+    GDN_F32 = 0,
+    GDN_BF16 = 1
+} gdn_dtype;
+
+/* Library ABI version (increments on any signature change). */
+int gdn_version(void);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char *gdn_status_string(int status);
+
+/*
+ * gdn_chunk_prefill -- run the recurrence over whole prompts with the
+ * chunkwise-parallel form of the same page (G = cumsum g inside each chunk;
+ * N = diag(beta)[exp(G_t - G_j) k_t.k_j]_{j<t}; D = (I+N)^-1 diag(beta)
+ * (V - diag(exp G) K S0); O = diag(exp G) Q S0 + [exp(G_t - G_j) q_t.k_j]_{j<=t} D;
+ * S_T = exp(G_last) S0 + K^T diag(exp(G_last - G)) D), which reaches the
+ * per-token result above up to rounding.  The chunks of one sequence are walked
+ * in order with the state kept on chip; the state touches device memory once
+ * on entry and once on exit.  A sequence whose length is not a multiple of
+ * `chunk` ends in a partial chunk whose missing rows act as the page's
+ * token_valid padding (g = 0, beta = 0): they leave the state untouched and
+ * produce no output rows.
+ *
+ *   q, k        [B, T, H, 128] io_dtype   (packed: [1, T, H, 128])
+ *   v           [B, T, H, 128] io_dtype
+ *   g, beta     [B, T, H] fp32
+ *   S0          [N, H, 128, 128] fp32, or NULL for a zero initial state
+ *   cu_seqlens  NULL: N = B sequences of T tokens each (B_or_N = B).
+ *               Otherwise a device array of N+1 int32 offsets (B_or_N = N) into
+ *               one packed batch of T tokens: sequence n owns tokens
+ *               cu_seqlens[n] .. cu_seqlens[n+1]-1 and starts from S0[n].  The
+ *               offsets must start at 0, never decrease and end at T; they are
+ *               read on the device and clamped to [0, T], so a bad array gives
+ *               wrong results, never an out-of-bounds access.  Zero-length
+ *               sequences are allowed (S_T[n] = S0[n], no rows of O).
+ *   chunk       16, 32 or 64 (the page's prompt-block sizes); the result does
+ *               not depend on it beyond rounding.
+ *   O           same shape and dtype as v; rows of the call's tokens are all
+ *               written.
+ *   S_T         [N, H, 128, 128] fp32, the state after each sequence's last
+ *               token.  S_T may be exactly S0 (in-place update of a prefix
+ *               state); any other overlap of S_T with S0 is GDN_ERR_ALIAS.
+ *               Keep them distinct to retain a snapshot of S0.
+ *   O must not overlap q, k, v, g, beta, S0 or S_T; S_T must not overlap the
+ *   token inputs (GDN_ERR_ALIAS).
+ */
+int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
+                      const float *g, const float *beta, const float *S0,
+                      const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                      int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                      void *O, float *S_T, void *stream);
+
+/*
+ * gdn_decode_step -- one token per (sequence, head) with the page's one-token
+ * matrix form: with d = exp(g), a = S^T k and b = S^T q read in one pass over
+ * S, delta = beta (v - d a), o = d b + (q.k) delta and S' = d S + k delta^T,
+ * written back in place.  Each state is read once and written once.
+ *
+ *   q, k     [B, H, 128] io_dtype      v  [B, H, 128] io_dtype
+ *   g, beta  [B, H] fp32
+ *   S        [B, H, 128, 128] fp32, read and overwritten in place
+ *   o        [B, H, 128] io_dtype
+ *   o must not overlap S or the inputs, and S must not overlap the inputs
+ *   (GDN_ERR_ALIAS).
+ */
+int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
+                    const float *g, const float *beta, float *S, int64_t B,
+                    int64_t H, int64_t dk, int64_t dv, void *o, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

@@ -1,0 +1,155 @@
+"""ctypes binding for libgdn's C ABI (include/gdn.h).
+
+Argument marshalling only: each function checks that the torch tensors it is
+given are device tensors of the dtype and contiguity the ABI expects, then
+passes their data pointers, the sizes and torch's current HIP stream to the
+C entry point of the same name.  Every step of the computation runs in the
+library's HIP kernels.  If ``libgdn.so`` has not been built the first call
+raises; there is no other code path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # imported first so that libgdn binds to torch's HIP runtime
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn.so")
+
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
+GDN_F32, GDN_BF16 = 0, 1
+EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_decode_step")
+
+_lib = None
+
+
+class GdnError(RuntimeError):
+    """A libgdn call returned a non-zero status."""
+
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libgdn status {status}: {msg}")
+        self.status = status
+
+
+def load_library(path: Optional[str] = None):
+    """Load libgdn.so (raises FileNotFoundError if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FileNotFoundError(
+            f"{p} not found: build it with `python -m linear_attention_recurrence_02_amd.build`")
+    lib = ctypes.CDLL(p)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    lib.gdn_version.argtypes = []
+    lib.gdn_version.restype = ctypes.c_int
+    lib.gdn_status_string.argtypes = [ctypes.c_int]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_chunk_prefill.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
+                                      i64, i64, i64, i64, vp, vp, vp]
+    lib.gdn_chunk_prefill.restype = ctypes.c_int
+    lib.gdn_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i64,
+                                    i64, vp, vp]
+    lib.gdn_decode_step.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def gdn_version() -> int:
+    return load_library().gdn_version()
+
+
+def gdn_status_string(status: int) -> str:
+    return load_library().gdn_status_string(status).decode()
+
+
+def _check(status: int):
+    if status != GDN_OK:
+        raise GdnError(status, gdn_status_string(status))
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDN_BF16
+    if t.dtype == torch.float32:
+        return GDN_F32
+    raise TypeError(f"unsupported io dtype {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor], dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
+                      O=None, S_T=None, stream=None):
+    """Chunkwise-parallel prompt form over whole sequences.
+
+    q, k, v: [B, T, H, 128] (bf16 or fp32; packed batches B = 1);
+    g, beta: [B, T, H] fp32; S0: [N, H, 128, 128] fp32 or None;
+    cu_seqlens: int32 [N+1] device offsets or None.
+    Returns (O, S_T); O/S_T may be given to write in place (S_T may be S0).
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed batches (cu_seqlens) need B == 1")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype \
+            or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape [B, T, H, d] and dtype")
+    if g.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("g and beta must be [B, T, H]")
+    if O is None:
+        O = torch.empty_like(v)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if O.dtype != q.dtype or O.shape != v.shape:
+        raise ValueError("O must match v's shape and dtype")
+    if S_T.shape != (N, H, dk, dv) or (S0 is not None and S0.shape != (N, H, dk, dv)):
+        raise ValueError("S0 / S_T must be [N, H, dk, dv]")
+    st = load_library().gdn_chunk_prefill(
+        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+        _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+        N, T, H, dk, dv, int(chunk), _ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"),
+        _stream(stream))
+    _check(st)
+    return O, S_T
+
+
+def gdn_decode_step(q, k, v, g, beta, S, *, o=None, stream=None):
+    """One token for each of B x H states, S [B, H, 128, 128] fp32 updated in
+    place.  q, k, v: [B, H, 128]; g, beta: [B, H] fp32.  Returns o [B, H, 128]."""
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:2] != (B, H) or k.dtype != q.dtype \
+            or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape [B, H, d] and dtype")
+    if g.shape != (B, H) or beta.shape != (B, H) or S.shape != (B, H, dk, dv):
+        raise ValueError("g, beta must be [B, H]; S [B, H, dk, dv]")
+    if o is None:
+        o = torch.empty_like(v)
+    st = load_library().gdn_decode_step(
+        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+        _ptr(S, torch.float32, "S"), B, H, dk, dv, _ptr(o, q.dtype, "o"), _stream(stream))
+    _check(st)
+    return o

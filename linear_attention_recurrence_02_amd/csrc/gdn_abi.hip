@@ -1,0 +1,123 @@
+// libgdn C ABI: argument validation and launch selection (see include/gdn.h).
+// Nothing here allocates or synchronises; a rejected call enqueues nothing.
+
+#include "gdn.h"
+#include "gdn_internal.hpp"
+
+#include <cstdint>
+
+namespace {
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range span_of(const void *p, int64_t bytes) {
+    uintptr_t a = reinterpret_cast<uintptr_t>(p);
+    return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) {
+    if (a.lo == a.hi || b.lo == b.hi) return false;
+    return a.lo < b.hi && b.lo < a.hi;
+}
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool dims_ok(int64_t x) { return x >= 0 && x < kMaxDim; }
+
+}  // namespace
+
+extern "C" {
+
+int gdn_version(void) { return 1; }
+
+const char *gdn_status_string(int status) {
+    switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_INVALID_ARG: return "invalid argument (null pointer, bad size or misaligned buffer)";
+    case GDN_ERR_UNSUPPORTED: return "unsupported configuration (dk/dv must be 128, chunk 16/32/64, dtype f32/bf16)";
+    case GDN_ERR_ALIAS: return "buffers overlap in a way the call forbids";
+    case GDN_ERR_HIP: return "HIP runtime error while enqueuing a kernel";
+    default: return "unknown status";
+    }
+}
+
+int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
+                      const float *g, const float *beta, const float *S0,
+                      const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                      int64_t H, int64_t dk, int64_t dv, int64_t chunk, void *O,
+                      float *S_T, void *stream) {
+    if (!dims_ok(B_or_N) || !dims_ok(T) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
+    const int64_t N = B_or_N;
+    const int64_t rows = cu_seqlens ? T : N * T;        // token rows of H heads
+    // Token buffers may be NULL only when the call has no token rows at all.
+    if (rows > 0 && (!q || !k || !v || !g || !beta || !O)) return GDN_ERR_INVALID_ARG;
+    if (!S_T) return GDN_ERR_INVALID_ARG;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (dk != gdn::kHeadDim || dv != gdn::kHeadDim) return GDN_ERR_UNSUPPORTED;
+    if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
+    for (const void *p : {q, k, v, static_cast<const void *>(O)})
+        if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    if (!aligned(S_T, 16) || (S0 && !aligned(S0, 16))) return GDN_ERR_INVALID_ARG;
+    if (!aligned(g, 4) || !aligned(beta, 4) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return GDN_ERR_INVALID_ARG;
+
+    if (N * H >= kMaxDim) return GDN_ERR_INVALID_ARG;     // one workgroup per unit
+    if (rows > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return GDN_ERR_INVALID_ARG;
+    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t tok_bytes = rows * H * gdn::kHeadDim * esz;
+    const int64_t gb_bytes = rows * H * 4;
+    const int64_t st_bytes = N * H * gdn::kHeadDim * gdn::kHeadDim * 4;
+
+    const Range rq = span_of(q, tok_bytes), rk = span_of(k, tok_bytes),
+                rv = span_of(v, tok_bytes), rg = span_of(g, gb_bytes),
+                rb = span_of(beta, gb_bytes), rO = span_of(O, tok_bytes),
+                rST = span_of(S_T, st_bytes),
+                rS0 = S0 ? span_of(S0, st_bytes) : Range{0, 0};
+    for (Range r : {rq, rk, rv, rg, rb, rS0, rST})
+        if (overlap(rO, r)) return GDN_ERR_ALIAS;
+    for (Range r : {rq, rk, rv, rg, rb})
+        if (overlap(rST, r)) return GDN_ERR_ALIAS;
+    if (S0 && overlap(rST, rS0) && rST.lo != rS0.lo) return GDN_ERR_ALIAS;
+
+    gdn::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, N, T, H,
+                       static_cast<int>(chunk), io_dtype == GDN_BF16, O, S_T};
+    if (N == 0) return GDN_OK;   // nothing to do
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = gdn::prefill_mfma_supports(a) ? gdn::launch_prefill_mfma(a, s)
+                                                 : gdn::launch_prefill_valu(a, s);
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
+                    const float *g, const float *beta, float *S, int64_t B,
+                    int64_t H, int64_t dk, int64_t dv, void *o, void *stream) {
+    if (!q || !k || !v || !g || !beta || !S || !o) return GDN_ERR_INVALID_ARG;
+    if (!dims_ok(B) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (dk != gdn::kHeadDim || dv != gdn::kHeadDim) return GDN_ERR_UNSUPPORTED;
+    for (const void *p : {q, k, v, static_cast<const void *>(o), static_cast<const void *>(S)})
+        if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    if (!aligned(g, 4) || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
+    const int64_t units = B * H;
+    if (units >= kMaxDim) return GDN_ERR_INVALID_ARG;
+    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t vec_bytes = units * gdn::kHeadDim * esz;
+    const Range rq = span_of(q, vec_bytes), rk = span_of(k, vec_bytes),
+                rv = span_of(v, vec_bytes), rg = span_of(g, units * 4),
+                rb = span_of(beta, units * 4), ro = span_of(o, vec_bytes),
+                rS = span_of(S, units * gdn::kHeadDim * gdn::kHeadDim * 4);
+    for (Range r : {rq, rk, rv, rg, rb, rS})
+        if (overlap(ro, r)) return GDN_ERR_ALIAS;
+    for (Range r : {rq, rk, rv, rg, rb})
+        if (overlap(rS, r)) return GDN_ERR_ALIAS;
+    if (units == 0) return GDN_OK;
+    gdn::DecodeArgs a{q, k, v, g, beta, S, units, io_dtype == GDN_BF16, o};
+    hipError_t e = gdn::launch_decode(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // extern "C"

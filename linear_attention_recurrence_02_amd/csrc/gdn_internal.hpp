@@ -1,0 +1,71 @@
+// Internal declarations shared by the translation units of libgdn (not part of
+// the public ABI; see include/gdn.h for that).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <cstdint>
+
+namespace gdn {
+
+constexpr int kHeadDim = 128;   // dk == dv == 128: the page's per-head state size
+
+// A validated prompt-form call.  Token rows are counted in units of H heads:
+// the element (row r, head h, dim i) of q/k/v/O sits at ((r * H) + h) * 128 + i.
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    const float *S0;            // may be null (zero state)
+    const int32_t *cu_seqlens;  // may be null (uniform batch)
+    int64_t N;                  // sequences
+    int64_t T;                  // tokens per sequence (uniform) or total (packed)
+    int64_t H;                  // heads
+    int chunk;                  // 16, 32 or 64
+    bool bf16;                  // io dtype of q/k/v/O
+    void *O;
+    float *S_T;
+};
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta;
+    float *S;
+    int64_t units;              // B * H
+    bool bf16;
+    void *o;
+};
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
+bool prefill_mfma_supports(const PrefillArgs &a);
+
+// ---- small device helpers -------------------------------------------------
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__hip_bfloat16 x) { return __bfloat162float(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(float x) {
+    return __float2bfloat16(x);   // round to nearest even
+}
+
+// Sequence span of unit n: first token row and length.  Offsets from the
+// device are clamped into [0, T] so that a malformed array cannot make a
+// kernel read or write outside the caller's buffers.
+__device__ __forceinline__ void sequence_span(const int32_t *cu, int64_t n, int64_t T,
+                                              int64_t &start, int64_t &len) {
+    if (cu) {
+        int64_t a = cu[n], b = cu[n + 1];
+        a = a < 0 ? 0 : (a > T ? T : a);
+        b = b < a ? a : (b > T ? T : b);
+        start = a;
+        len = b - a;
+    } else {
+        start = n * T;
+        len = T;
+    }
+}
+
+}  // namespace gdn

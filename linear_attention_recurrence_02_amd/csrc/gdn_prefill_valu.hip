@@ -1,0 +1,170 @@
+// Chunkwise-parallel prompt form on the vector ALUs, all arithmetic in fp32
+// (the in-chunk cumulative log-decay in fp64).  This kernel serves fp32 inputs
+// and the 16/32-token chunk sizes; bf16 inputs at 64-token chunks go to the
+// matrix-core kernel.
+//
+// The form (Qwen3.5-9B-npu model page, "How it works" -> "Gated DeltaNet on
+// the NPU"), per chunk of C tokens with incoming state S:
+//     G   = cumsum(g)                                   (inclusive)
+//     N   = diag(beta) [exp(G_t - G_j) k_t.k_j]_{j<t}    (strictly lower)
+//     D   = (I + N)^-1 diag(beta) (V - diag(exp G) K S)
+//     O   = diag(exp G) Q S + [exp(G_t - G_j) q_t.k_j]_{j<=t} D
+//     S  <- exp(G_last) S + K^T diag(exp(G_last - G)) D
+// Rows past the end of a sequence carry g = 0, beta = 0 and zero q/k/v (the
+// page's token_valid padding), so a partial last chunk leaves S exactly as after
+// the last real token.
+//
+// Work split: one 128-thread workgroup per (sequence, head); thread j owns
+// column j of the state (128 fp32 registers, S[i][j] for all i) and of D, so the
+// forward substitution for D runs down one column per thread with no barrier.
+// The chunk's K and Q (fp32, rows padded to 129 words so that the Gram phase's
+// row-strided reads hit distinct LDS banks), D, N and the masked decayed
+// QK^T live in LDS.
+
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+constexpr int kThreads = 128;
+constexpr int kRow = kHeadDim + 1;   // padded LDS row stride for K and Q
+
+template <typename IO, int C>
+__global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
+    const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta,
+    const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t T,
+    int64_t H, IO *__restrict__ O, float *__restrict__ S_T) {
+    __shared__ float sK[C * kRow], sQ[C * kRow];
+    __shared__ float sD[C * kHeadDim];
+    __shared__ float sN[C * C], sA[C * C];
+    __shared__ double sG[C];
+    __shared__ float sg[C], sB[C], sEG[C], sEC[C];
+
+    const int64_t unit = blockIdx.x;
+    const int64_t n = unit / H, h = unit % H;
+    const int j = threadIdx.x;
+    int64_t start, len;
+    sequence_span(cu_seqlens, n, T, start, len);
+
+    float S[kHeadDim];
+    const float *S0u = S0 ? S0 + unit * (kHeadDim * kHeadDim) : nullptr;
+#pragma unroll
+    for (int i = 0; i < kHeadDim; ++i) S[i] = S0u ? S0u[i * kHeadDim + j] : 0.f;
+
+    for (int64_t c0 = 0; c0 < len; c0 += C) {
+        const int nv = static_cast<int>(len - c0 < C ? len - c0 : C);
+        const int64_t row0 = start + c0;   // first token row of this chunk
+
+        for (int idx = j; idx < C * kHeadDim; idx += kThreads) {
+            const int t = idx / kHeadDim, i = idx % kHeadDim;
+            float kv = 0.f, qv = 0.f;
+            if (t < nv) {
+                const int64_t off = ((row0 + t) * H + h) * kHeadDim + i;
+                kv = to_f32(k[off]);
+                qv = to_f32(q[off]);
+            }
+            sK[t * kRow + i] = kv;
+            sQ[t * kRow + i] = qv;
+        }
+        if (j < C) {
+            const bool ok = j < nv;
+            sg[j] = ok ? g[(row0 + j) * H + h] : 0.f;
+            sB[j] = ok ? beta[(row0 + j) * H + h] : 0.f;
+        }
+        __syncthreads();
+        if (j == 0) {
+            double acc = 0.0;
+            for (int t = 0; t < C; ++t) {
+                acc += static_cast<double>(sg[t]);
+                sG[t] = acc;
+            }
+        }
+        __syncthreads();
+        if (j < C) {
+            sEG[j] = static_cast<float>(exp(sG[j]));
+            sEC[j] = static_cast<float>(exp(sG[C - 1] - sG[j]));
+        }
+        // Gram entries (t, s) for s <= t, with the decay applied on the fp32 sums.
+        for (int e = j; e < C * C; e += kThreads) {
+            const int t = e / C, s = e % C;
+            float nn = 0.f, aa = 0.f;
+            if (s <= t) {
+                float kk = 0.f, qk = 0.f;
+                const float *kt = &sK[t * kRow], *qt = &sQ[t * kRow], *ks = &sK[s * kRow];
+#pragma unroll 16
+                for (int i = 0; i < kHeadDim; ++i) {
+                    kk += kt[i] * ks[i];
+                    qk += qt[i] * ks[i];
+                }
+                const float E = expf(static_cast<float>(sG[t] - sG[s]));
+                aa = E * qk;
+                nn = s < t ? sB[t] * (E * kk) : 0.f;
+            }
+            sN[e] = nn;
+            sA[e] = aa;
+        }
+        __syncthreads();
+
+        // Column j: right-hand side, forward substitution, output rows.
+        for (int t = 0; t < C; ++t) {
+            float ks = 0.f, qs = 0.f;
+            const float *kt = &sK[t * kRow], *qt = &sQ[t * kRow];
+#pragma unroll
+            for (int i = 0; i < kHeadDim; ++i) {
+                ks += kt[i] * S[i];
+                qs += qt[i] * S[i];
+            }
+            const float vt = t < nv ? to_f32(v[((row0 + t) * H + h) * kHeadDim + j]) : 0.f;
+            float r = sB[t] * (vt - sEG[t] * ks);
+            for (int s = 0; s < t; ++s) r -= sN[t * C + s] * sD[s * kHeadDim + j];
+            sD[t * kHeadDim + j] = r;
+            float o = sEG[t] * qs;
+            for (int s = 0; s <= t; ++s) o += sA[t * C + s] * sD[s * kHeadDim + j];
+            if (t < nv) O[((row0 + t) * H + h) * kHeadDim + j] = from_f32<IO>(o);
+        }
+
+        // Carry the state to the end of the chunk.
+        const float eC = sEG[C - 1];
+#pragma unroll
+        for (int i = 0; i < kHeadDim; ++i) S[i] *= eC;
+        for (int t = 0; t < C; ++t) {
+            const float wt = sEC[t] * sD[t * kHeadDim + j];
+            const float *kt = &sK[t * kRow];
+#pragma unroll
+            for (int i = 0; i < kHeadDim; ++i) S[i] += kt[i] * wt;
+        }
+        __syncthreads();   // LDS is rewritten by the next chunk
+    }
+
+    float *STu = S_T + unit * (kHeadDim * kHeadDim);
+#pragma unroll
+    for (int i = 0; i < kHeadDim; ++i) STu[i * kHeadDim + j] = S[i];
+}
+
+template <typename IO, int C>
+hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(kThreads);
+    prefill_valu_kernel<IO, C><<<grid, block, 0, stream>>>(
+        static_cast<const IO *>(a.q), static_cast<const IO *>(a.k),
+        static_cast<const IO *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
+        static_cast<IO *>(a.O), a.S_T);
+    return hipGetLastError();
+}
+
+template <typename IO>
+hipError_t launch_chunk(const PrefillArgs &a, hipStream_t stream) {
+    switch (a.chunk) {
+    case 16: return launch_typed<IO, 16>(a, stream);
+    case 32: return launch_typed<IO, 32>(a, stream);
+    default: return launch_typed<IO, 64>(a, stream);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream) {
+    return a.bf16 ? launch_chunk<__hip_bfloat16>(a, stream) : launch_chunk<float>(a, stream);
+}
+
+}  // namespace gdn

@@ -6,9 +6,12 @@ the gated delta rule's arithmetic.  Both the GPU path and the CPU oracle are
 fed from here, and neither computes its inputs itself.
 
 Recipe (the same for every workload):
-  * one CPU ``torch.Generator`` seeded with ``seed``; float32 ``randn`` draws in
-    the fixed order: sequence lengths (packed batches only), q, k, v, g_raw,
-    beta_raw, S0;
+  * sequence lengths (packed batches only) come from a CPU ``torch.Generator``
+    seeded with ``seed``; the tensors come from a ``torch.Generator`` on the
+    target device seeded with ``seed`` (float32 ``randn`` in the fixed order q,
+    k, v, g_raw, beta_raw, S0).  Drawing on the device keeps the multi-GB
+    workloads quick to make; a workload is reproducible for a given device
+    type and torch build;
   * q and k are divided by their L2 norm over the head dimension (in fp32),
     then cast to the io dtype; v is cast as drawn;
   * g = -softplus(g_raw) (a log-decay <= 0), beta = sigmoid(beta_raw), both fp32;
@@ -59,22 +62,29 @@ def _unit(x: torch.Tensor) -> torch.Tensor:
     return x / x.norm(dim=-1, keepdim=True)
 
 
+def _generator(seed: int, device) -> torch.Generator:
+    return torch.Generator(device=torch.device(device)).manual_seed(seed)
+
+
 def _draw(gen, lead, dk, dv, io_dtype, n_states, s0: bool):
     """Draw q, k, v, g, beta, S0 in the fixed order for token shape ``lead``."""
-    q = _unit(torch.randn(*lead, dk, generator=gen)).to(io_dtype)
-    k = _unit(torch.randn(*lead, dk, generator=gen)).to(io_dtype)
-    v = torch.randn(*lead, dv, generator=gen).to(io_dtype)
-    g = -F.softplus(torch.randn(*lead, generator=gen))
-    beta = torch.sigmoid(torch.randn(*lead, generator=gen))
-    S0 = 0.1 * torch.randn(*n_states, dk, dv, generator=gen) if s0 else None
+    dev = gen.device
+    rn = lambda *shape: torch.randn(*shape, generator=gen, device=dev)
+    q = _unit(rn(*lead, dk)).to(io_dtype)
+    k = _unit(rn(*lead, dk)).to(io_dtype)
+    v = rn(*lead, dv).to(io_dtype)
+    g = -F.softplus(rn(*lead))
+    beta = torch.sigmoid(rn(*lead))
+    S0 = 0.1 * rn(*n_states, dk, dv) if s0 else None
     return q, k, v, g, beta, S0
 
 
 def prefill_workload(B: int, T: int, H: int, *, chunk: int = 64,
                      io_dtype=torch.bfloat16, s0: bool = True, seed: int = 0,
-                     dk: int = DK, dv: int = DV, name: str = "prefill") -> Workload:
+                     dk: int = DK, dv: int = DV, name: str = "prefill",
+                     device="cpu") -> Workload:
     """B sequences of T tokens each, q/k/v laid out [B, T, H, d]."""
-    gen = torch.Generator().manual_seed(seed)
+    gen = _generator(seed, device)
     q, k, v, g, beta, S0 = _draw(gen, (B, T, H), dk, dv, io_dtype, (B, H), s0)
     return Workload(name, q, k, v, g, beta, S0, None, chunk,
                     dict(B=B, T=T, H=H, seed=seed, tokens=B * T))
@@ -83,66 +93,73 @@ def prefill_workload(B: int, T: int, H: int, *, chunk: int = 64,
 def varlen_workload(lengths=None, *, n_seqs: int = 32, lo: int = 17, hi: int = 8192,
                     H: int = 16, chunk: int = 64, io_dtype=torch.bfloat16,
                     s0: bool = True, seed: int = 0, dk: int = DK, dv: int = DV,
-                    name: str = "varlen") -> Workload:
+                    name: str = "varlen", device="cpu") -> Workload:
     """A packed batch: sequence lengths drawn uniformly from [lo, hi] (integers,
     both ends inclusive) unless given, laid out [1, sum(L), H, d] with
     cu_seqlens offsets and one S0 slice per sequence."""
-    gen = torch.Generator().manual_seed(seed)
     if lengths is None:
-        lengths = torch.randint(lo, hi + 1, (n_seqs,), generator=gen)
+        lengths = torch.randint(lo, hi + 1, (n_seqs,), generator=_generator(seed, "cpu"))
+    gen = _generator(seed, device)
     lengths = torch.as_tensor(lengths, dtype=torch.int64)
     cu = torch.zeros(lengths.numel() + 1, dtype=torch.int64)
     cu[1:] = torch.cumsum(lengths, 0)
     total = int(cu[-1])
     q, k, v, g, beta, S0 = _draw(gen, (1, total, H), dk, dv, io_dtype,
                                  (lengths.numel(), H), s0)
-    return Workload(name, q, k, v, g, beta, S0, cu.to(torch.int32), chunk,
+    return Workload(name, q, k, v, g, beta, S0, cu.to(torch.int32).to(device), chunk,
                     dict(N=lengths.numel(), T=total, H=H, seed=seed, tokens=total,
                          lengths=lengths.tolist()))
 
 
 def verify_workload(n_seqs: int = 256, block: int = 16, H: int = 16, *, chunk: int = 64,
-                    io_dtype=torch.bfloat16, seed: int = 0) -> Workload:
+                    io_dtype=torch.bfloat16, seed: int = 0, device="cpu") -> Workload:
     """Speculative-verify blocks: ``n_seqs`` sequences of ``block`` tokens each,
     packed with cu_seqlens, each starting from its own snapshotted state."""
     return varlen_workload([block] * n_seqs, H=H, chunk=chunk, io_dtype=io_dtype,
-                           s0=True, seed=seed, name="verify")
+                           s0=True, seed=seed, name="verify", device=device)
 
 
 def decode_workload(steps: int, B: int, H: int, *, io_dtype=torch.bfloat16,
-                    seed: int = 0, dk: int = DK, dv: int = DV) -> Workload:
+                    seed: int = 0, dk: int = DK, dv: int = DV, device="cpu") -> Workload:
     """``steps`` consecutive single-token steps for a batch of B x H states:
     q/k/v are [steps, B, H, d], g/beta [steps, B, H], S0 the [B, H, dk, dv]
     state the first step starts from."""
-    gen = torch.Generator().manual_seed(seed)
+    gen = _generator(seed, device)
     q, k, v, g, beta, S0 = _draw(gen, (steps, B, H), dk, dv, io_dtype, (B, H), True)
     return Workload("decode", q, k, v, g, beta, S0, None, 1,
                     dict(steps=steps, B=B, H=H, seed=seed))
 
 
 # The five workloads, named by what they are.
-def tiny_prefill(seed=0):
+def tiny_prefill(seed=0, device="cpu"):
+    """B=1, H=2, T=256, chunk 16, fp32 inputs, nonzero S0."""
     return prefill_workload(1, 256, 2, chunk=16, io_dtype=torch.float32, s0=True,
-                            seed=seed, name="tiny_prefill")
+                            seed=seed, name="tiny_prefill", device=device)
 
 
-def long_prefill(seed=0):
+def long_prefill(seed=0, device="cpu"):
+    """B=1, H=16, T=4096, chunk 64, bf16 inputs, nonzero S0."""
     return prefill_workload(1, 4096, 16, chunk=64, s0=True, seed=seed,
-                            name="long_prefill")
+                            name="long_prefill", device=device)
 
 
-def large_prefill(seed=0):
+def large_prefill(seed=0, device="cpu"):
+    """B=8, H=32, T=16384, chunk 64, bf16 inputs, zero S0."""
     return prefill_workload(8, 16384, 32, chunk=64, s0=False, seed=seed,
-                            name="large_prefill")
+                            name="large_prefill", device=device)
 
 
-def batched_decode(seed=0, steps=1000):
-    return decode_workload(steps, 64, 16, seed=seed)
+def batched_decode(seed=0, steps=1000, device="cpu"):
+    """B=64 sequences x H=16 heads, one bf16 token each per step."""
+    return decode_workload(steps, 64, 16, seed=seed, device=device)
 
 
-def varlen_prefill(seed=0):
-    return varlen_workload(n_seqs=32, lo=17, hi=8192, H=16, seed=seed)
+def varlen_prefill(seed=0, device="cpu"):
+    """32 sequences, lengths uniform in [17, 8192], H=16, chunk 64, bf16,
+    per-sequence nonzero S0."""
+    return varlen_workload(n_seqs=32, lo=17, hi=8192, H=16, seed=seed, device=device)
 
 
-def verify_blocks(seed=0):
-    return verify_workload(256, 16, 16, seed=seed)
+def verify_blocks(seed=0, device="cpu"):
+    """256 sequences x 16-token verify blocks, H=16, from snapshotted states."""
+    return verify_workload(256, 16, 16, seed=seed, device=device)

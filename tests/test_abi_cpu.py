@@ -1,0 +1,116 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/gdn.h declares, and rejects malformed calls with the documented status
+before anything is enqueued (every call below fails validation, so no HIP call
+is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_attention_recurrence_02_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+A = 0x10000          # fake, 16-byte aligned device addresses (never dereferenced)
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load_library()
+
+
+def test_header_declares_expected_calls():
+    assert declared_functions() == sorted(binding.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.gdn_version() == 1
+    for s in range(5):
+        assert lib.gdn_status_string(s)
+    assert b"unknown" in lib.gdn_status_string(99)
+
+
+def prefill(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB,
+            beta=A + 200 * MB, S0=A + 256 * MB, cu=None, N=2, T=64, H=2, dk=128,
+            dv=128, chunk=64, O=A + 512 * MB, S_T=A + 768 * MB):
+    return lib.gdn_chunk_prefill(q, k, v, dtype, g, beta, S0, cu, N, T, H, dk, dv, chunk,
+                                 O, S_T, None)
+
+
+def decode(lib, q=A, k=A + MB, v=A + 2 * MB, dtype=1, g=A + 3 * MB, beta=A + 4 * MB,
+           S=A + 8 * MB, B=4, H=2, dk=128, dv=128, o=A + 64 * MB):
+    return lib.gdn_decode_step(q, k, v, dtype, g, beta, S, B, H, dk, dv, o, None)
+
+
+def test_prefill_rejects_null_and_bad_sizes(lib):
+    assert prefill(lib, q=None) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, O=None) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, S_T=None) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, N=-1) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, T=-5) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, H=0) == binding.GDN_ERR_INVALID_ARG
+
+
+def test_prefill_rejects_unsupported(lib):
+    assert prefill(lib, dk=64) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, dv=256) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, chunk=48) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, chunk=128) == binding.GDN_ERR_UNSUPPORTED
+    assert prefill(lib, dtype=7) == binding.GDN_ERR_UNSUPPORTED
+
+
+def test_prefill_rejects_misaligned(lib):
+    assert prefill(lib, q=A + 2) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, S_T=A + 768 * MB + 4) == binding.GDN_ERR_INVALID_ARG
+    assert prefill(lib, g=A + 192 * MB + 1) == binding.GDN_ERR_INVALID_ARG
+
+
+def test_prefill_aliasing_rules(lib):
+    assert prefill(lib, O=A) == binding.GDN_ERR_ALIAS                   # O over q
+    assert prefill(lib, O=A + 256 * MB) == binding.GDN_ERR_ALIAS        # O over S0
+    assert prefill(lib, S_T=A + 256 * MB + 4096) == binding.GDN_ERR_ALIAS  # partial S0
+    assert prefill(lib, S_T=A + 64 * MB) == binding.GDN_ERR_ALIAS       # S_T over k
+    # an empty batch is accepted without enqueueing anything
+    assert prefill(lib, N=0) == binding.GDN_OK
+    assert prefill(lib, N=0, S_T=A + 256 * MB) == binding.GDN_OK        # S_T == S0
+
+
+def test_decode_rejects_bad_calls(lib):
+    assert decode(lib, S=None) == binding.GDN_ERR_INVALID_ARG
+    assert decode(lib, B=-1) == binding.GDN_ERR_INVALID_ARG
+    assert decode(lib, dk=64) == binding.GDN_ERR_UNSUPPORTED
+    assert decode(lib, dtype=3) == binding.GDN_ERR_UNSUPPORTED
+    assert decode(lib, S=A + 8 * MB + 8) == binding.GDN_ERR_INVALID_ARG
+    assert decode(lib, o=A + 8 * MB) == binding.GDN_ERR_ALIAS            # o over S
+    assert decode(lib, S=A) == binding.GDN_ERR_ALIAS                     # S over q
+    assert decode(lib, B=0) == binding.GDN_OK
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 4, 1, 128)
+    g = torch.zeros(1, 4, 1)
+    with pytest.raises(ValueError):
+        binding.gdn_chunk_prefill(x, x, x, g, g)
+
+
+def test_package_import_does_not_load_library():
+    import subprocess
+    import sys
+    code = ("import sys, linear_attention_recurrence_02_amd as m; "
+            "assert 'linear_attention_recurrence_02_amd.binding' not in sys.modules")
+    subprocess.run([sys.executable, "-c", code], check=True, cwd=ROOT)

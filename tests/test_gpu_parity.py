@@ -1,0 +1,250 @@
+"""GPU parity: libgdn (through its C ABI) against the fp64 CPU oracle.
+
+Every test here runs the HIP kernels on the GPU and compares them with the
+oracle on the same seeded inputs (the oracle receives exact fp64 copies of the
+device-dtype values).  Tolerances: per-slice normwise error <= 1e-5 for fp32
+inputs and <= 2e-3 for bf16 inputs, with a bf16 output's own rounding allowed
+for elementwise (see metrics.py).  At the full workload sizes the oracle
+checks sampled (sequence, head) units in full.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_02_amd import inputs
+from linear_attention_recurrence_02_amd.binding import (GdnError, gdn_chunk_prefill,
+                                                        gdn_decode_step)
+from metrics import (TOL_BF16, TOL_F32, bf16_output_ok, spans_of, worst_slice_error)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_prefill(w, **kw):
+    O, S_T = gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk, **kw)
+    torch.cuda.synchronize()
+    return O, S_T
+
+
+def check_prefill(w, O, S_T, Or, Sr, spans=None, H=None, label=""):
+    """Compare GPU outputs with oracle outputs on the given spans."""
+    H = H or w.q.shape[2]
+    spans = spans or spans_of(w.q.shape[0], w.q.shape[1], w.cu_seqlens)
+    eo = worst_slice_error(O, Or, spans, H)
+    es = worst_slice_error(S_T, Sr)
+    say(f"[{label}] worst slice error O={eo:.3e} S_T={es:.3e}")
+    if w.q.dtype == torch.float32:
+        assert eo <= TOL_F32 and es <= TOL_F32, (eo, es)
+    else:
+        ok, ratio = bf16_output_ok(O, Or, TOL_BF16, spans, H)
+        assert ok, f"bf16 O exceeds bound by x{ratio:.3f} (raw {eo:.3e})"
+        assert es <= TOL_BF16, es
+
+
+def oracle_units(w, seqs, heads):
+    """Oracle on selected sequences and heads of a workload (full length)."""
+    spans = spans_of(w.q.shape[0], w.q.shape[1], w.cu_seqlens)
+    outs = []
+    for n in seqs:
+        b, s, e = spans[n]
+        sl = lambda x: x[b:b + 1, s:e][:, :, heads]
+        S0 = None if w.S0 is None else w.S0[n:n + 1, heads]
+        O, S = oracle.prefill(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), S0)
+        outs.append((n, O, S))
+    return outs
+
+
+def check_units(w, O, S_T, seqs, heads, label):
+    spans = spans_of(w.q.shape[0], w.q.shape[1], w.cu_seqlens)
+    for n, Or, Sr in oracle_units(w, seqs, heads):
+        b, s, e = spans[n]
+        Og = O[b:b + 1, s:e][:, :, heads]
+        Sg = S_T[n:n + 1, heads]
+        check_prefill(w, Og, Sg, Or, Sr, spans=[(0, 0, e - s)], H=len(heads),
+                      label=f"{label} seq {n}")
+
+
+# --- the five workloads ------------------------------------------------------
+
+def test_tiny_prefill_fp32_full():
+    w = inputs.tiny_prefill(device=DEV)
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    check_prefill(w, O, S_T, Or, Sr, label="tiny")
+
+
+def test_long_prefill_bf16_full():
+    w = inputs.long_prefill(device=DEV)
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    check_prefill(w, O, S_T, Or, Sr, label="long")
+
+
+def test_large_prefill_bf16_sampled_units():
+    w = inputs.large_prefill(device=DEV)
+    O, S_T = run_prefill(w)
+    check_units(w, O, S_T, seqs=[0, 5], heads=[0, 13, 31], label="large")
+    assert torch.isfinite(S_T).all() and torch.isfinite(O.float()).all()
+
+
+def test_varlen_prefill_bf16_sampled_sequences():
+    w = inputs.varlen_prefill(device=DEV)
+    lengths = w.meta["lengths"]
+    O, S_T = run_prefill(w)
+    pick = sorted({int(np.argmax(lengths)), int(np.argmin(lengths)), 3, 17})
+    check_units(w, O, S_T, seqs=pick, heads=list(range(16)), label="varlen")
+
+
+def test_verify_blocks_from_snapshot_full():
+    w = inputs.verify_blocks(device=DEV)
+    snap = w.S0.clone()
+    O, S_T = run_prefill(w)
+    assert torch.equal(w.S0, snap), "the snapshot S0 must be left untouched"
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, cu_seqlens=w.cu_seqlens)
+    check_prefill(w, O, S_T, Or, Sr, label="verify")
+
+
+def test_batched_decode_1000_steps():
+    steps = 1000
+    w = inputs.batched_decode(device=DEV, steps=steps)
+    S = w.S0.clone()
+    o_first = o_last = None
+    for s in range(steps):
+        o = gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], S)
+        if s == 0:
+            o_first = o.clone()
+            S_first = S.clone()
+        o_last = o
+    torch.cuda.synchronize()
+    bsel = [0, 21, 63]
+    sub = lambda x: x[:, bsel]
+    o1, S1 = oracle.decode(sub(w.q)[:1], sub(w.k)[:1], sub(w.v)[:1], sub(w.g)[:1],
+                           sub(w.beta)[:1], w.S0[bsel])
+    on, Sn = oracle.decode(sub(w.q), sub(w.k), sub(w.v), sub(w.g), sub(w.beta), w.S0[bsel])
+    H = w.q.shape[2]
+    spans = [(b, 0, 1) for b in range(len(bsel))]
+    # outputs as [sequence, 1 token, H, 128]
+    for name, got, ref in (("o step 1", o_first[bsel][:, None], o1[0][:, None]),
+                           ("o step 1000", o_last[bsel][:, None], on[-1][:, None])):
+        ok, ratio = bf16_output_ok(got, ref, TOL_BF16, spans, H)
+        say(f"[decode] {name}: bound ratio {ratio:.3f}")
+        assert ok, (name, ratio)
+    e1 = worst_slice_error(S_first[bsel], S1)
+    en = worst_slice_error(S[bsel], Sn)
+    say(f"[decode] S after step 1: {e1:.3e}; after step 1000: {en:.3e}")
+    assert e1 <= TOL_BF16 and en <= TOL_BF16
+
+
+def test_decode_fp32_io():
+    w = inputs.decode_workload(20, 8, 4, io_dtype=torch.float32, device=DEV, seed=3)
+    S = w.S0.clone()
+    outs = []
+    for s in range(20):
+        outs.append(gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], S))
+    torch.cuda.synchronize()
+    o_ref, S_ref = oracle.decode(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    o = torch.stack(outs)
+    assert worst_slice_error(o.reshape(20, 32, 1, 128), o_ref.reshape(20, 32, 1, 128)) <= TOL_F32
+    assert worst_slice_error(S, S_ref) <= TOL_F32
+
+
+# --- edge cases --------------------------------------------------------------
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 130])
+def test_prefill_tails_bf16(chunk, T):
+    w = inputs.prefill_workload(2, T, 3, chunk=chunk, seed=T + chunk, device=DEV)
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    check_prefill(w, O, S_T, Or, Sr, label=f"tail T={T} C={chunk}")
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_prefill_fp32_chunk_sizes(chunk):
+    w = inputs.prefill_workload(2, 200, 2, chunk=chunk, io_dtype=torch.float32, seed=7,
+                                device=DEV)
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    check_prefill(w, O, S_T, Or, Sr, label=f"fp32 C={chunk}")
+
+
+def test_prefill_slow_decay_carries_state_across_chunks():
+    # g close to 0 keeps the state alive across many chunks (the workloads'
+    # decay forgets within a few tokens, which would hide carry errors)
+    w = inputs.prefill_workload(1, 512, 4, chunk=64, seed=11, device=DEV)
+    w.g = w.g * 0.01
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    check_prefill(w, O, S_T, Or, Sr, label="slow decay")
+
+
+def test_prefill_zero_state_and_empty_sequences():
+    w = inputs.varlen_workload([5, 0, 70, 0, 1], H=2, seed=4, device=DEV)
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, cu_seqlens=w.cu_seqlens)
+    check_prefill(w, O, S_T, Or, Sr, label="empty seqs")
+    assert torch.equal(S_T[1], w.S0[1]) and torch.equal(S_T[3], w.S0[3])
+    w0 = inputs.prefill_workload(2, 40, 2, s0=False, seed=5, device=DEV)
+    O, S_T = run_prefill(w0)
+    Or, Sr = oracle.prefill(w0.q, w0.k, w0.v, w0.g, w0.beta, None)
+    check_prefill(w0, O, S_T, Or, Sr, label="S0=None")
+
+
+def test_prefill_zero_tokens_copies_state():
+    w = inputs.prefill_workload(2, 0, 2, seed=6, device=DEV)
+    O, S_T = run_prefill(w)
+    assert torch.equal(S_T, w.S0)
+
+
+def test_prefill_in_place_state():
+    w = inputs.prefill_workload(2, 100, 2, seed=8, device=DEV)
+    S = w.S0.clone()
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    O, S_T = gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, S, None, 64, S_T=S)
+    torch.cuda.synchronize()
+    assert S_T.data_ptr() == S.data_ptr()
+    check_prefill(w, O, S, Or, Sr, label="in place")
+
+
+def test_prefill_is_deterministic():
+    w = inputs.prefill_workload(2, 300, 4, seed=9, device=DEV)
+    a = run_prefill(w)
+    b = run_prefill(w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_prefill_one_token_matches_decode_step():
+    w = inputs.prefill_workload(8, 1, 4, seed=10, device=DEV)
+    O, S_T = run_prefill(w)
+    S = w.S0.clone()
+    o = gdn_decode_step(w.q[:, 0], w.k[:, 0], w.v[:, 0], w.g[:, 0], w.beta[:, 0], S)
+    torch.cuda.synchronize()
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    check_prefill(w, O, S_T, Or, Sr, label="T=1 prefill")
+    check_prefill(w, o[:, None], S, Or, Sr, label="T=1 decode")
+
+
+def test_split_resume_matches_one_call():
+    w = inputs.prefill_workload(1, 300, 2, seed=12, device=DEV)
+    O, S_T = run_prefill(w)
+    cut = 131
+    O1, S1 = gdn_chunk_prefill(w.q[:, :cut].contiguous(), w.k[:, :cut].contiguous(),
+                               w.v[:, :cut].contiguous(), w.g[:, :cut].contiguous(),
+                               w.beta[:, :cut].contiguous(), w.S0, None, 64)
+    O2, S2 = gdn_chunk_prefill(w.q[:, cut:].contiguous(), w.k[:, cut:].contiguous(),
+                               w.v[:, cut:].contiguous(), w.g[:, cut:].contiguous(),
+                               w.beta[:, cut:].contiguous(), S1, None, 64)
+    torch.cuda.synchronize()
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0)
+    check_prefill(w, torch.cat([O1, O2], 1), S2, Or, Sr, label="split+resume")
+
+
+def test_bad_call_raises_without_enqueueing():
+    w = inputs.prefill_workload(1, 8, 1, seed=13, device=DEV)
+    with pytest.raises(GdnError):
+        gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, None, 48)
