@@ -30,19 +30,19 @@
 //     and fill in T's off-diagonal blocks with T_ij = -T_ii sum_k N_ik T_kj
 //     (one wave per column block).
 //   Each chunk period has three barrier-separated phases:
-//     A: consumers K S, R               | producers write K(c+1), decay scan
-//     B: consumers T R, Q S, A D -> O   | producers write V(c+1); Gram; T_ii
+//     A: consumers K S, Q S, R          | producers write K(c+1), scan its decay;
+//                                       |   A(c) from Q(c) K(c)^T
+//     B: consumers T R, A D -> O        | producers write V(c+1); N(c+1); T_ii
 //     C: consumers state update         | producers write Q(c+1); T_ij, i > j
-//   K, T, A and the per-token scalars are double-buffered; V is read by the
-//   consumers only in phase A and Q only in phase B, so one buffer each serves.
+//   K, T, A and the per-token scalars are double-buffered; Q and V are read by
+//   the consumers only in phase A, so one buffer each serves.
 //   The two roles run as two separate loops under a wave-uniform branch; both
 //   execute exactly three barriers per period (and three for the period in
 //   which the producers prepare chunk 0), so their live registers never
 //   overlap and each fits the 256 registers that two waves per SIMD allow.
 // fp32 quantities that feed a bf16 MFMA (S, R, T, A, D and the decayed D) are
-// split x = hi + lo into two bf16 parts and multiplied as hi*hi + hi*lo + lo*hi
-// (or hi + lo against an exact bf16 operand), which keeps every product at
-// ~2^-16 relative accuracy.  Where a row's scale factor (exp(G_t) for K S and
+// split x = hi + lo into two bf16 parts (both rounded to nearest) and multiplied as hi*hi + hi*lo + lo*hi (or hi + lo against an
+// exact bf16 operand), which keeps every product at ~2^-16 relative accuracy.  Where a row's scale factor (exp(G_t) for K S and
 // Q S, exp(G_C - G_t) for the state update) stays below 2^-8 over a whole
 // 16/32-row block, the lo term's contribution is below 2^-17 of the product
 // and is not issued.
@@ -59,26 +59,22 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;             // chunk length
 constexpr int D = kHeadDim;       // 128
-constexpr int FS = C + 4;         // fp32 row stride of the N scratch
-constexpr int DS = 17;            // fp32 row stride of the 16x16 diagonal inverses
+constexpr int RS = D + 8;         // bf16 row stride of K, Q, V tiles (272 B)
+constexpr int TS = C + 8;         // bf16 row stride of T and A tiles (144 B)
 constexpr float kLoSkip = 1.0f / 256.0f;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Row-swizzled LDS tiles: a 128-wide bf16 row is 16 chunks of 16 bytes and
-// chunk c of row r is stored at chunk c ^ (r & 15); a 64-wide row is 8 chunks
-// stored at c ^ ((r >> 1) & 7).  Both keep the 16 rows a lane group reads in
-// one instruction on distinct LDS banks.
-__device__ __forceinline__ int sw128(int r, int i) { return r * D + ((((i >> 3) ^ (r & 15))) << 3) + (i & 7); }
-__device__ __forceinline__ int sw64(int r, int j) { return r * C + ((((j >> 3) ^ ((r >> 1) & 7))) << 3) + (j & 7); }
-
-struct Smem {
-    bf16 K[2][C * D];             // chunk keys, double-buffered (sw128)
-    bf16 Q[C * D];                // chunk queries (sw128)
-    bf16 V[C * D];                // chunk values (sw128)
-    bf16 T[2][2][C * C];          // [buffer][hi, lo] T = (I+N)^-1 (sw64)
-    bf16 A[2][2][C * C];          // [buffer][hi, lo] decayed masked Q K^T (sw64)
-    float N[C * FS];              // fp32 N of the chunk being prepared
-    float Td[4 * 16 * DS];        // fp32 diagonal blocks of T
+// Rows are padded by 16 bytes so that the 16 rows a lane group touches in one
+// instruction start on different LDS banks, and every address a lane forms is
+// one per-lane base plus a compile-time offset.
+struct __attribute__((aligned(16))) Smem {
+    bf16 K[2][C * RS];            // chunk keys, double-buffered
+    bf16 Q[C * RS];               // chunk queries
+    bf16 V[C * RS];               // chunk values
+    bf16 T[2][2][C * TS];         // [buffer][hi, lo] T = (I+N)^-1
+    bf16 A[2][2][C * TS];         // [buffer][hi, lo] decayed masked Q K^T
+    float NdT[4][16 * 20];        // fp32 diagonal blocks of N, transposed: [j][t]
+    bf16 No[6][2][16 * 24];       // off-diagonal blocks (bi > bj) of N as hi/lo, [t][j]
     float G2[2][C];               // cumsum(g) * log2(e)
     float EG[2][C];               // exp(G_t)
     float EC[2][C];               // exp(G_last - G_t)
@@ -86,6 +82,10 @@ struct Smem {
     int lo_ks[2][4];              // per 16-token tile: max exp(G_t) >= 2^-8
     int lo_kd[2][2];              // per 32-token step: max exp(G_last - G_t) >= 2^-8
 };
+
+// index of the off-diagonal block (bi, bj), bi > bj, of N in Smem::No
+__device__ __forceinline__ constexpr int oblk(int bi, int bj) { return bi * (bi - 1) / 2 + bj; }
+constexpr int NOS = 24;           // bf16 row stride of an off-diagonal block (48 B)
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -96,68 +96,75 @@ __device__ __forceinline__ f32x4 mfma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 b
     return mfma(al, bh, c);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
-
-// A zero the compiler cannot see through.  Lane indices are re-derived from it
-// at the top of every loop iteration so that the many swizzled LDS addresses
-// are recomputed in the loop (a few VALU ops) instead of being hoisted out of
-// it and held in registers for the whole walk.
-__device__ __forceinline__ int opaque_zero() {
-    int z;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-    return z;
-}
 __device__ __forceinline__ bf16 bz() { return static_cast<bf16>(0.f); }
 
 __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
     return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+__device__ __forceinline__ bf16x8 half4(bf16x4 a) {
+    bf16x4 z;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z[e] = bz();
+    return cat4(a, z);
+}
 
-// A operand in the permuted k order from a sw128 tile: row `row`, k step
-// starting at column kb (multiple of 32).
-__device__ __forceinline__ bf16x8 pk128(const bf16 *m, int row, int kb, int q) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(&m[sw128(row, kb + 4 * q)]);
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(&m[sw128(row, kb + 16 + 4 * q)]);
-    return cat4(a, b);
+// A operand in the permuted k order: row `row` of a row-major tile with row
+// stride rs, k step starting at column kb; lane group q reads kb+4q..+3 and
+// kb+16+4q..+3.
+__device__ __forceinline__ bf16x8 rd_pk(const bf16 *m, int rs, int row, int kb, int q) {
+    const bf16 *p = m + row * rs + kb + 4 * q;
+    return cat4(*reinterpret_cast<const bf16x4 *>(p), *reinterpret_cast<const bf16x4 *>(p + 16));
 }
-// Same from a sw64 tile.
-__device__ __forceinline__ bf16x8 pk64(const bf16 *m, int row, int kb, int q) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4 *>(&m[sw64(row, kb + 4 * q)]);
-    const bf16x4 b = *reinterpret_cast<const bf16x4 *>(&m[sw64(row, kb + 16 + 4 * q)]);
-    return cat4(a, b);
-}
-// K^T as an A operand (rows = dk index `row`, k = tokens in the permuted
-// order of step kb), gathered from the row-major sw128 key tile.
-__device__ __forceinline__ bf16x8 pkT128(const bf16 *m, int row, int kb, int q) {
+// K^T as an A operand (row = dk index, k = tokens in the permuted order of
+// step kb), gathered from the row-major key tile.
+__device__ __forceinline__ bf16x8 rd_pkT(const bf16 *m, int row, int kb, int q) {
+    const bf16 *p = m + (kb + 4 * q) * RS + row;
     bf16x8 r;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        r[e] = m[sw128(kb + 4 * q + e, row)];
-        r[e + 4] = m[sw128(kb + 16 + 4 * q + e, row)];
+        r[e] = p[e * RS];
+        r[e + 4] = p[(16 + e) * RS];
     }
     return r;
 }
 
+// x = hi + lo with hi = x rounded to bf16 and lo the rounded remainder:
+// |x - hi - lo| <= 2^-17 |x|.  Two values are split at a time: one packed
+// conversion gives the hi pair, whose halves are widened back by a shift and a
+// mask to form the remainders.
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float a, float b, uint32_t *hi, uint32_t *lo) {
+    bf16x2 h;
+    h[0] = static_cast<bf16>(a);
+    h[1] = static_cast<bf16>(b);
+    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
+    bf16x2 r;
+    r[0] = static_cast<bf16>(a - __builtin_bit_cast(float, hb << 16));
+    r[1] = static_cast<bf16>(b - __builtin_bit_cast(float, hb & 0xffff0000u));
+    *hi = hb;
+    *lo = __builtin_bit_cast(uint32_t, r);
+}
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 // hi/lo split of two result tiles (rows kb..kb+15 -> elements 0..3, rows
 // kb+16..kb+31 -> elements 4..7): a B operand in the permuted k order.
 __device__ __forceinline__ void split_pk(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 ha = static_cast<bf16>(a[e]), hb = static_cast<bf16>(b[e]);
-        hi[e] = ha;
-        hi[e + 4] = hb;
-        lo[e] = static_cast<bf16>(a[e] - static_cast<float>(ha));
-        lo[e + 4] = static_cast<bf16>(b[e] - static_cast<float>(hb));
-    }
+    uint32_t h[4], o[4];
+    split2(a[0], a[1], &h[0], &o[0]);
+    split2(a[2], a[3], &h[1], &o[1]);
+    split2(b[0], b[1], &h[2], &o[2]);
+    split2(b[2], b[3], &h[3], &o[3]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
-// hi/lo split of one result tile used as a 16-deep operand (elements 4..7 zero).
+// hi/lo split of one tile used as a 16-deep operand (elements 4..7 zero).
 __device__ __forceinline__ void split_half(f32x4 a, bf16x8 &hi, bf16x8 &lo) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const bf16 h = static_cast<bf16>(a[e]);
-        hi[e] = h;
-        lo[e] = static_cast<bf16>(a[e] - static_cast<float>(h));
-        hi[e + 4] = lo[e + 4] = bz();
-    }
+    uint32_t h[2], o[2];
+    split2(a[0], a[1], &h[0], &o[0]);
+    split2(a[2], a[3], &h[1], &o[1]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], 0u, 0u});
+    lo = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], 0u, 0u});
 }
 __device__ __forceinline__ void store_hilo(bf16 *hi, bf16 *lo, int idx, float x) {
     const bf16 h = static_cast<bf16>(x);
@@ -165,34 +172,34 @@ __device__ __forceinline__ void store_hilo(bf16 *hi, bf16 *lo, int idx, float x)
     lo[idx] = static_cast<bf16>(x - static_cast<float>(h));
 }
 
-// Rows of one 16-token block of a chunk held by a producer lane (row 16p+r16,
-// k step s covers columns 32s+8q..+7, the natural MFMA operand layout), kept as
-// four 16-byte entries of the shared register block.
+// Rows of one 16-token block held by a producer lane: row 16p+r16, k step s
+// covers columns 32s+8q..+7 (the natural MFMA operand layout), as 16-byte
+// entries.
 __device__ __forceinline__ bf16x8 as_bf(f32x4 x) { return __builtin_bit_cast(bf16x8, x); }
-__device__ __forceinline__ f32x4 as_f(bf16x8 x) { return __builtin_bit_cast(f32x4, x); }
 
-__device__ __forceinline__ void load_rows(f32x4 *dst, const bf16 *src, int64_t row0, int r,
-                                          int nv, int64_t H, int64_t h, int q) {
-    if (r < nv) {
-        const bf16 *p = src + ((row0 + r) * H + h) * D + 8 * q;
+// Loads are always issued (rows past the chunk read the sequence's first row
+// and are replaced by zeros) so that every period issues the same load
+// sequence and the wait counts before each use stay exact.
+__device__ __forceinline__ void load_rows(f32x4 *dst, const bf16 *src, int64_t start, int64_t row0,
+                                          int r, int nv, int64_t H, int64_t h, int q) {
+    const bool ok = r < nv;
+    const bf16 *p = src + ((ok ? row0 + r : start) * H + h) * D + 8 * q;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) dst[s] = *reinterpret_cast<const f32x4 *>(p + 32 * s);
-    } else {
-#pragma unroll
-        for (int s = 0; s < 4; ++s) dst[s] = zero4();
+    for (int s = 0; s < 4; ++s) {
+        const f32x4 x = *reinterpret_cast<const f32x4 *>(p + 32 * s);
+        dst[s] = ok ? x : zero4();
     }
 }
 __device__ __forceinline__ void store_rows(bf16 *tile, const f32x4 *src, int r, int q) {
 #pragma unroll
     for (int s = 0; s < 4; ++s)
-        *reinterpret_cast<f32x4 *>(&tile[sw128(r, 32 * s + 8 * q)]) = src[s];
+        *reinterpret_cast<f32x4 *>(&tile[r * RS + 32 * s + 8 * q]) = src[s];
 }
 
 struct Unit {
     const bf16 *q, *k, *v;
     const float *g, *beta;
     int64_t start, len, H, h;
-    int nch;
     __device__ int rows_in(int pc) const {
         const int64_t rem = len - int64_t(pc) * C;
         return static_cast<int>(rem < C ? rem : C);
@@ -202,22 +209,25 @@ struct Unit {
 
 // Producer waves 4..7 (row block p): prepare chunk pc in buffer set nb over the
 // three phases of one period.  Rows of the chunk are prefetched into pK, pQ,
-// pV (rows 16p+r16) one period ahead.
+// pV (rows 16p+r16) a period ahead.
 struct Producer {
     f32x4 pK[4], pQ[4], pV[4];
     float pg, pb;
 
+    // chunk pc may lie past the sequence (nothing valid is read then); the
+    // sequence has at least one token whenever these are called.
     __device__ void prefetch_kv(const Unit &u, int pc, int p, int l, int r16, int qd) {
         const int nv = u.rows_in(pc);
-        load_rows(pK, u.k, u.row0(pc), 16 * p + r16, nv, u.H, u.h, qd);
-        load_rows(pV, u.v, u.row0(pc), 16 * p + r16, nv, u.H, u.h, qd);
-        if (p == 0) {
-            pg = l < nv ? u.g[(u.row0(pc) + l) * u.H + u.h] : 0.f;
-            pb = l < nv ? u.beta[(u.row0(pc) + l) * u.H + u.h] : 0.f;
-        }
+        load_rows(pK, u.k, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, qd);
+        load_rows(pV, u.v, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, qd);
+        const bool ok = l < nv;
+        const int64_t gi = (ok ? u.row0(pc) + l : u.start) * u.H + u.h;
+        const float gv = u.g[gi], bv = u.beta[gi];
+        pg = ok ? gv : 0.f;
+        pb = ok ? bv : 0.f;
     }
     __device__ void prefetch_q(const Unit &u, int pc, int p, int r16, int qd) {
-        load_rows(pQ, u.q, u.row0(pc), 16 * p + r16, u.rows_in(pc), u.H, u.h, qd);
+        load_rows(pQ, u.q, u.start, u.row0(pc), 16 * p + r16, u.rows_in(pc), u.H, u.h, qd);
     }
 
     // phase A: stage K; scan the log-decay (wave p = 0)
@@ -247,67 +257,110 @@ struct Producer {
         }
     }
 
-    // phase B: stage V; Gram tiles; diagonal block p of T
-    __device__ void phase_b(Smem &sm, int nb, int p, int r16, int qd) {
-        store_rows(sm.V, pV, 16 * p + r16, qd);
+    // Q K^T tiles of chunk pc (its K and Q are in LDS, buffers nb) -> A (hi/lo).
+    // The ten lower 16x16 tiles are dealt out to the four waves: wave P takes
+    // tiles P, P+4, P+8 of (0,0), (1,0), (1,1), (2,0), (2,1), (2,2), (3,0), ...
+    template <int P>
+    __device__ void gram_qk(Smem &sm, int nb, int r16, int qd) {
+        constexpr int NT = P < 2 ? 3 : 2;
+        constexpr int TI[4][3] = {{0, 2, 3}, {1, 2, 3}, {1, 3, 0}, {2, 3, 0}};
+        constexpr int TJ[4][3] = {{0, 1, 2}, {0, 2, 3}, {1, 0, 0}, {0, 1, 0}};
         const bf16 *Kn = sm.K[nb];
         const float *G2 = sm.G2[nb];
-        const float *Bt = sm.Bt[nb];
-        // K K^T tiles (p, mj >= p): their transposes are the N tiles (mj, p).
-        for (int mj = p; mj < 4; ++mj) {
-            f32x4 acc = zero4();
+        f32x4 acc[NT];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 b = mj == p ? as_bf(pK[s])
-                                         : *reinterpret_cast<const bf16x8 *>(&Kn[sw128(16 * mj + r16, 32 * s + 8 * qd)]);
-                acc = mfma(as_bf(pK[s]), b, acc);
-            }
-            // acc[e] = k_j . k_t with j = 16p+4q+e (row), t = 16mj+r16 (column)
-            const int t = 16 * mj + r16;
-            const float g2t = G2[t], bt = Bt[t];
-            f32x4 out;
+        for (int i = 0; i < NT; ++i) acc[i] = zero4();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int j = 16 * p + 4 * qd + e;
-                out[e] = j < t ? bt * (__builtin_amdgcn_exp2f(g2t - G2[j]) * acc[e]) : 0.f;
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int i = 0; i < NT; ++i) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&sm.Q[(16 * TI[P][i] + r16) * RS + 32 * s + 8 * qd]);
+                const bf16x8 b = *reinterpret_cast<const bf16x8 *>(&Kn[(16 * TJ[P][i] + r16) * RS + 32 * s + 8 * qd]);
+                acc[i] = mfma(a, b, acc[i]);
             }
-            *reinterpret_cast<f32x4 *>(&sm.N[t * FS + 16 * p + 4 * qd]) = out;
         }
-        // Q K^T tiles (p, mj <= p) -> A (hi/lo)
+        // acc[i][e] = q_t . k_j, t = 16 mi + 4q + e, j = 16 mj + r16
         bf16 *An = sm.A[nb][0], *Anl = sm.A[nb][1];
-        for (int mj = 0; mj <= p; ++mj) {
-            f32x4 acc = zero4();
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 b = mj == p ? as_bf(pK[s])
-                                         : *reinterpret_cast<const bf16x8 *>(&Kn[sw128(16 * mj + r16, 32 * s + 8 * qd)]);
-                acc = mfma(as_bf(pQ[s]), b, acc);
-            }
-            const int j = 16 * mj + r16;
+        for (int i = 0; i < NT; ++i) {
+            const int j = 16 * TJ[P][i] + r16;
             const float g2j = G2[j];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int t = 16 * p + 4 * qd + e;
-                const float a = j <= t ? __builtin_amdgcn_exp2f(G2[t] - g2j) * acc[e] : 0.f;
-                store_hilo(An, Anl, sw64(t, j), a);
+                const int t = 16 * TI[P][i] + 4 * qd + e;
+                const float a = j <= t ? __builtin_amdgcn_exp2f(G2[t] - g2j) * acc[i][e] : 0.f;
+                store_hilo(An, Anl, t * TS + j, a);
             }
         }
-        // Diagonal block p of T by forward substitution (lane r16 = column j).
+    }
+
+    // phase B: stage V; K K^T tiles -> N; diagonal block P of T.  Compiled
+    // once per row block P so that every tile loop is unrolled.
+    template <int P>
+    __device__ void phase_b(Smem &sm, int nb, int r16, int qd) {
+        store_rows(sm.V, pV, 16 * P + r16, qd);
+        const bf16 *Kn = sm.K[nb];
+        const float *G2 = sm.G2[nb];
+        const float *Bt = sm.Bt[nb];
+        // K K^T tiles of row block P: (P, mj >= P).
+        f32x4 kk[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) kk[m] = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+            for (int mj = P; mj < 4; ++mj) {
+                const bf16x8 b = mj == P ? as_bf(pK[s])
+                                         : *reinterpret_cast<const bf16x8 *>(&Kn[(16 * mj + r16) * RS + 32 * s + 8 * qd]);
+                kk[mj] = mfma(as_bf(pK[s]), b, kk[mj]);
+            }
+        }
+        // kk[mj][e] = k_j . k_t with j = 16P+4q+e (row), t = 16mj+r16 (column):
+        // the transpose of N's block (mj, P).
+        {
+            const int t = 16 * P + r16;
+            const float g2t = G2[t], bt = Bt[t];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * qd + e;          // local row of the diagonal block
+                const float nv = j < r16 ? bt * (__builtin_amdgcn_exp2f(g2t - G2[16 * P + j]) * kk[P][e]) : 0.f;
+                sm.NdT[P][j * 20 + r16] = nv;      // N^T[j][t]
+            }
+        }
+#pragma unroll
+        for (int mj = P + 1; mj < 4; ++mj) {
+            const int t = 16 * mj + r16;
+            const float g2t = G2[t], bt = Bt[t];
+            f32x4 nv;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                nv[e] = bt * (__builtin_amdgcn_exp2f(g2t - G2[16 * P + 4 * qd + e]) * kk[mj][e]);
+            bf16x8 h, lo;
+            split_half(nv, h, lo);
+            bf16 *blk = sm.No[oblk(mj, P)][0];
+            *reinterpret_cast<bf16x4 *>(&blk[r16 * NOS + 4 * qd]) = h.lo;
+            *reinterpret_cast<bf16x4 *>(&sm.No[oblk(mj, P)][1][r16 * NOS + 4 * qd]) = lo.lo;
+        }
+        // Diagonal block P of T by forward substitution (lane r16 = column j):
+        // once x_t is final, x_u -= N_ut x_t for every u > t.
         const int j = r16;
+        const float *Nt = sm.NdT[P];
         float x[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) x[t] = t == j ? 1.f : 0.f;
 #pragma unroll
-        for (int t = 0; t < 16; ++t)
+        for (int t = 0; t < 15; ++t) {
+            f32x4 col[4];
 #pragma unroll
-            for (int u = t + 1; u < 16; ++u) x[u] -= sm.N[(16 * p + u) * FS + 16 * p + t] * x[t];
+            for (int v4 = 0; v4 < 4; ++v4)
+                if (4 * v4 + 3 > t) col[v4] = *reinterpret_cast<const f32x4 *>(&Nt[t * 20 + 4 * v4]);
+#pragma unroll
+            for (int u = t + 1; u < 16; ++u) x[u] -= col[u >> 2][u & 3] * x[t];
+        }
         if (qd == 0) {
             bf16 *Tn = sm.T[nb][0], *Tnl = sm.T[nb][1];
 #pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                sm.Td[(p * 16 + t) * DS + j] = x[t];
-                store_hilo(Tn, Tnl, sw64(16 * p + t, 16 * p + j), x[t]);
-            }
+            for (int t = 0; t < 16; ++t) store_hilo(Tn, Tnl, (16 * P + t) * TS + 16 * P + j, x[t]);
         }
     }
 
@@ -325,29 +378,35 @@ struct Producer {
 #pragma unroll
             for (int kk = 0; kk < 3; ++kk) {
                 if (kk < j || kk >= i) continue;
-                bf16x8 ah, al, bh, bl;
-                split_half(*reinterpret_cast<const f32x4 *>(&sm.N[(16 * i + r16) * FS + 16 * kk + 4 * qd]), ah, al);
+                bf16x8 bh, bl;
+                const bf16x8 ah = half4(*reinterpret_cast<const bf16x4 *>(&sm.No[oblk(i, kk)][0][r16 * NOS + 4 * qd]));
+                const bf16x8 al = half4(*reinterpret_cast<const bf16x4 *>(&sm.No[oblk(i, kk)][1][r16 * NOS + 4 * qd]));
                 if (kk == j) {
-                    f32x4 tj;
+                    // B = T_jj (rows 4q+e, column r16) straight from its hi/lo parts
+                    bf16x4 th, tl;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) tj[e] = sm.Td[(j * 16 + 4 * qd + e) * DS + r16];
-                    split_half(tj, bh, bl);
+                    for (int e = 0; e < 4; ++e) {
+                        th[e] = Tn[(16 * j + 4 * qd + e) * TS + 16 * j + r16];
+                        tl[e] = Tnl[(16 * j + 4 * qd + e) * TS + 16 * j + r16];
+                    }
+                    bh = half4(th);
+                    bl = half4(tl);
                 } else {
                     split_half(Tc[kk], bh, bl);
                 }
                 Z = mfma3(ah, al, bh, bl, Z);
             }
-            bf16x8 ah, al, bh, bl;
-            f32x4 ti;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) ti[e] = sm.Td[(i * 16 + r16) * DS + 4 * qd + e];
-            split_half(ti, ah, al);
+            // A = T_ii (row r16, columns 4q..4q+3) from its hi/lo parts
+            const int ti = (16 * i + r16) * TS + 16 * i + 4 * qd;
+            const bf16x8 ah = half4(*reinterpret_cast<const bf16x4 *>(&Tn[ti]));
+            const bf16x8 al = half4(*reinterpret_cast<const bf16x4 *>(&Tnl[ti]));
+            bf16x8 bh, bl;
             split_half(Z, bh, bl);
             f32x4 Tij = mfma3(ah, al, bh, bl, zero4());
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 Tij[e] = -Tij[e];
-                store_hilo(Tn, Tnl, sw64(16 * i + 4 * qd + e, 16 * j + r16), Tij[e]);
+                store_hilo(Tn, Tnl, (16 * i + 4 * qd + e) * TS + 16 * j + r16, Tij[e]);
             }
             Tc[i] = Tij;
         }
@@ -370,11 +429,11 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     u.H = H;
     u.h = unit % H;
     sequence_span(cu_seqlens, unit / H, T, u.start, u.len);
-    u.nch = static_cast<int>((u.len + C - 1) / C);
-    const int nch = u.nch;
+    const int nch = static_cast<int>((u.len + C - 1) / C);
 
-    // T and A tiles above the diagonal blocks are never written: zero them once.
-    for (int i = tid * 8; i < 4 * C * C; i += 512 * 8) {
+    // T and A entries above the diagonal blocks are never written: zero both
+    // buffers once.
+    for (int i = tid * 8; i < 4 * C * TS; i += 512 * 8) {
         *reinterpret_cast<f32x4 *>(&sm.T[0][0][i]) = zero4();
         *reinterpret_cast<f32x4 *>(&sm.A[0][0][i]) = zero4();
     }
@@ -392,18 +451,30 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         for (int c = -1; c < nch; ++c) {
             const int pc = c + 1, nb = pc & 1;   // chunk being prepared, its buffers
             const bool work = pc < nch;
-            const int z = opaque_zero();
-            const int r16 = l + z - (l & ~15), qd = (l >> 4) + z;
             if (work) pr.phase_a(sm, nb, w, l, r16, qd);
+            if (c >= 0) {
+                // A of chunk c, whose K and Q were staged in the previous period
+                switch (w) {
+                case 0: pr.gram_qk<0>(sm, c & 1, r16, qd); break;
+                case 1: pr.gram_qk<1>(sm, c & 1, r16, qd); break;
+                case 2: pr.gram_qk<2>(sm, c & 1, r16, qd); break;
+                default: pr.gram_qk<3>(sm, c & 1, r16, qd); break;
+                }
+            }
             __syncthreads();
             if (work) {
-                pr.phase_b(sm, nb, w, r16, qd);
-                if (pc + 1 < nch) pr.prefetch_kv(u, pc + 1, w, l, r16, qd);
+                switch (w) {
+                case 0: pr.phase_b<0>(sm, nb, r16, qd); break;
+                case 1: pr.phase_b<1>(sm, nb, r16, qd); break;
+                case 2: pr.phase_b<2>(sm, nb, r16, qd); break;
+                default: pr.phase_b<3>(sm, nb, r16, qd); break;
+                }
+                pr.prefetch_kv(u, pc + 1, w, l, r16, qd);
             }
             __syncthreads();
             if (work) {
                 pr.phase_c(sm, nb, w, r16, qd);
-                if (pc + 1 < nch) pr.prefetch_q(u, pc + 1, w, r16, qd);
+                pr.prefetch_q(u, pc + 1, w, r16, qd);
             }
             __syncthreads();
         }
@@ -412,7 +483,6 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 
     // ======================= consumer waves =======================
     // S[2i+c] holds state rows 16i+4q+e, column 32w+16c+r16.
-    const int l16 = r16, q4 = qd;
     f32x4 S[16];
     if (S0) {
         const float *S0u = S0 + unit * (D * D);
@@ -433,43 +503,61 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     __syncthreads();
     __syncthreads();
 
+    const uint32_t HD = static_cast<uint32_t>(H) * D;
     for (int c = 0; c < nch; ++c) {
         const int cur = c & 1;
         const int cnv = u.rows_in(c);
-        const int z = opaque_zero();
-        const int r16 = l16 + z, qd = q4 + z;
-        bf16x8 Rhi[2][2], Rlo[2][2], Phi[2][2], Plo[2][2];
-        // outputs of this chunk: uniform base plus 32-bit lane offsets
-        bf16 *obase = O + (u.row0(c) * H + u.h) * D + 32 * w;
-        const uint32_t HD = static_cast<uint32_t>(H) * D;
+        bf16x8 Rhi[2][2], Rlo[2][2];
+        f32x4 QS[4][2];
 
-        // ================= phase A: K S, R =================
+        // ================= phase A: K S, Q S (one split of S); R =================
         {
             const bf16 *Kc = sm.K[cur];
             f32x4 KS[4][2];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) KS[m][cc] = zero4();
-            bool lo[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) lo[m] = sm.lo_ks[cur][m];
+                for (int cc = 0; cc < 2; ++cc) KS[m][cc] = QS[m][cc] = zero4();
+            // the lo part of S is needed for tile 0 in practice; other tiles
+            // only when the decay is slow
+            const bool full = sm.lo_ks[cur][1] | sm.lo_ks[cur][2] | sm.lo_ks[cur][3];
+            const bool lo0 = sm.lo_ks[cur][0];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 bf16x8 sh[2], sl[2];
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) split_pk(S[4 * s + cc], S[4 * s + 2 + cc], sh[cc], sl[cc]);
+                bf16x8 ak[4], aq[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const bf16x8 ak = pk128(Kc, 16 * m + r16, 32 * s, qd);
+                    ak[m] = rd_pk(Kc, RS, 16 * m + r16, 32 * s, qd);
+                    aq[m] = rd_pk(sm.Q, RS, 16 * m + r16, 32 * s, qd);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) {
-                        KS[m][cc] = mfma(ak, sh[cc], KS[m][cc]);
-                        if (lo[m]) KS[m][cc] = mfma(ak, sl[cc], KS[m][cc]);
+                        KS[m][cc] = mfma(ak[m], sh[cc], KS[m][cc]);
+                        QS[m][cc] = mfma(aq[m], sh[cc], QS[m][cc]);
+                    }
+                if (lo0 | full) {
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        KS[0][cc] = mfma(ak[0], sl[cc], KS[0][cc]);
+                        QS[0][cc] = mfma(aq[0], sl[cc], QS[0][cc]);
                     }
                 }
+                if (full) {
+#pragma unroll
+                    for (int m = 1; m < 4; ++m)
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc) {
+                            KS[m][cc] = mfma(ak[m], sl[cc], KS[m][cc]);
+                            QS[m][cc] = mfma(aq[m], sl[cc], QS[m][cc]);
+                        }
+                }
             }
-            // R = beta (V - exp(G) K S), in place of K S
+            // R = beta (V - exp(G) K S), in place of K S; exp(G) Q S
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -478,8 +566,9 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     const float bt = sm.Bt[cur][t], eg = sm.EG[cur][t];
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) {
-                        const float vt = static_cast<float>(sm.V[sw128(t, 32 * w + 16 * cc + r16)]);
+                        const float vt = static_cast<float>(sm.V[t * RS + 32 * w + 16 * cc + r16]);
                         KS[m][cc][e] = bt * (vt - eg * KS[m][cc][e]);
+                        QS[m][cc][e] *= eg;
                     }
                 }
 #pragma unroll
@@ -491,6 +580,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         __syncthreads();
 
         // ================= phase B: D = T R; O = exp(G) Q S + A D =================
+        bf16x8 Phi[2][2], Plo[2][2];
         {
             f32x4 Dt[4][2];
             const bf16 *Th = sm.T[cur][0], *Tl = sm.T[cur][1];
@@ -501,18 +591,19 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     if (s > m / 2) continue;
-                    const bf16x8 th = pk64(Th, 16 * m + r16, 32 * s, qd);
-                    const bf16x8 tl = pk64(Tl, 16 * m + r16, 32 * s, qd);
+                    const bf16x8 th = rd_pk(Th, TS, 16 * m + r16, 32 * s, qd);
+                    const bf16x8 tl = rd_pk(Tl, TS, 16 * m + r16, 32 * s, qd);
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc)
                         Dt[m][cc] = mfma3(th, tl, Rhi[s][cc], Rlo[s][cc], Dt[m][cc]);
                 }
             }
-            // decayed deltas (state update operand), then D's own hi/lo parts
+            // D's hi/lo parts, and the decayed deltas for the state update
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
+                    split_pk(Dt[2 * s][cc], Dt[2 * s + 1][cc], Rhi[s][cc], Rlo[s][cc]);   // now D
                     f32x4 a = Dt[2 * s][cc], b = Dt[2 * s + 1][cc];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -520,43 +611,16 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                         b[e] *= sm.EC[cur][32 * s + 16 + 4 * qd + e];
                     }
                     split_pk(a, b, Phi[s][cc], Plo[s][cc]);
-                    split_pk(Dt[2 * s][cc], Dt[2 * s + 1][cc], Rhi[s][cc], Rlo[s][cc]);   // now D
                 }
-            f32x4 QS[4][2];
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) QS[m][cc] = zero4();
-            bool lo[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) lo[m] = sm.lo_ks[cur][m];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                bf16x8 sh[2], sl[2];
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) split_pk(S[4 * s + cc], S[4 * s + 2 + cc], sh[cc], sl[cc]);
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const bf16x8 aq = pk128(sm.Q, 16 * m + r16, 32 * s, qd);
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        QS[m][cc] = mfma(aq, sh[cc], QS[m][cc]);
-                        if (lo[m]) QS[m][cc] = mfma(aq, sl[cc], QS[m][cc]);
-                    }
-                }
-            }
             const bf16 *Ah = sm.A[cur][0], *Al = sm.A[cur][1];
+            bf16 *obase = O + (u.row0(c) * H + u.h) * D + 32 * w;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) QS[m][cc][e] *= sm.EG[cur][16 * m + 4 * qd + e];
-#pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     if (s > m / 2) continue;
-                    const bf16x8 ah = pk64(Ah, 16 * m + r16, 32 * s, qd);
-                    const bf16x8 al = pk64(Al, 16 * m + r16, 32 * s, qd);
+                    const bf16x8 ah = rd_pk(Ah, TS, 16 * m + r16, 32 * s, qd);
+                    const bf16x8 al = rd_pk(Al, TS, 16 * m + r16, 32 * s, qd);
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc) QS[m][cc] = mfma3(ah, al, Rhi[s][cc], Rlo[s][cc], QS[m][cc]);
                 }
@@ -579,20 +643,25 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             const float eC = sm.EG[cur][C - 1];
             const bool lo0 = sm.lo_kd[cur][0], lo1 = sm.lo_kd[cur][1];
 #pragma unroll
+            for (int i = 0; i < 16; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) S[i][e] *= eC;
+#pragma unroll
             for (int i = 0; i < 8; ++i) {
+                const bf16x8 a0 = rd_pkT(Kc, 16 * i + r16, 0, qd);
+                const bf16x8 a1 = rd_pkT(Kc, 16 * i + r16, 32, qd);
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
+                for (int cc = 0; cc < 2; ++cc) {
+                    S[2 * i + cc] = mfma(a0, Phi[0][cc], S[2 * i + cc]);
+                    S[2 * i + cc] = mfma(a1, Phi[1][cc], S[2 * i + cc]);
+                }
+                if (lo1) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) S[2 * i + cc][e] *= eC;
+                    for (int cc = 0; cc < 2; ++cc) S[2 * i + cc] = mfma(a1, Plo[1][cc], S[2 * i + cc]);
+                }
+                if (lo0) {
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    const bf16x8 a = pkT128(Kc, 16 * i + r16, 32 * s, qd);
-                    const bool lo = s ? lo1 : lo0;
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        S[2 * i + cc] = mfma(a, Phi[s][cc], S[2 * i + cc]);
-                        if (lo) S[2 * i + cc] = mfma(a, Plo[s][cc], S[2 * i + cc]);
-                    }
+                    for (int cc = 0; cc < 2; ++cc) S[2 * i + cc] = mfma(a0, Plo[0][cc], S[2 * i + cc]);
                 }
             }
         }
