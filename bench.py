@@ -185,15 +185,17 @@ def bench_prefill(torch, gdn, w, iters, warmup):
 
 
 def cpu_baseline_decode(w, target_s=12.0):
-    """The oracle, as it stands, on the first n steps of the decode workload."""
+    """The oracle, as it stands, on the first n steps of the decode workload,
+    n sized from a timed probe so that the sample takes about target_s."""
     import oracle
     threads = oracle.default_threads()
     host = lambda x, n: x[:n].cpu()
+    probe = min(20, w.q.shape[0])
     t0 = time.perf_counter()
-    oracle.decode(host(w.q, 1), host(w.k, 1), host(w.v, 1), host(w.g, 1), host(w.beta, 1),
-                  w.S0.cpu(), nthreads=threads)
-    one = max(time.perf_counter() - t0, 1e-3)
-    n = int(max(1, min(w.q.shape[0], target_s / one)))
+    oracle.decode(host(w.q, probe), host(w.k, probe), host(w.v, probe), host(w.g, probe),
+                  host(w.beta, probe), w.S0.cpu(), nthreads=threads)
+    per_step = max(time.perf_counter() - t0, 1e-3) / probe
+    n = int(max(1, min(w.q.shape[0], target_s / per_step)))
     t0 = time.perf_counter()
     oracle.decode(host(w.q, n), host(w.k, n), host(w.v, n), host(w.g, n), host(w.beta, n),
                   w.S0.cpu(), nthreads=threads)
@@ -205,22 +207,33 @@ def cpu_baseline_decode(w, target_s=12.0):
                       f"({dt:.1f} s, fp64, {threads} threads)"}
 
 
-def cpu_baseline_prefill(w, target_units=None):
-    """The oracle on whole (sequence, head) units of the large prefill."""
+def cpu_baseline_prefill(w, target_s=12.0):
+    """The oracle on whole (sequence, head) units of the large prefill: a probe
+    of one unit sizes a sample of about target_s, run on all threads."""
     import oracle
     threads = oracle.default_threads()
-    nu = target_units or threads
-    T = w.q.shape[1]
-    heads = list(range(min(nu, w.q.shape[2])))
-    sl = lambda x: x[0:1, :, heads].cpu()
+    B, T, H = w.q.shape[0], w.q.shape[1], w.q.shape[2]
+    sl = lambda x, b, hs: x[b:b + 1, :, hs].cpu()
     t0 = time.perf_counter()
-    oracle.prefill(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), None, nthreads=threads)
-    dt = time.perf_counter() - t0
-    H = w.q.shape[2]
-    return {"value": len(heads) * T / H / dt, "unit": "tokens/s", "cores": threads,
+    oracle.prefill(sl(w.q, 0, [0]), sl(w.k, 0, [0]), sl(w.v, 0, [0]), sl(w.g, 0, [0]),
+                   sl(w.beta, 0, [0]), None, nthreads=1)
+    per_unit = max(time.perf_counter() - t0, 1e-3)
+    n_units = int(max(1, min(B * H, target_s * threads / per_unit)))
+    n_units = max(threads, (n_units // threads) * threads) if n_units >= threads else n_units
+    n_units = min(n_units, B * H)
+    done, dt = 0, 0.0
+    while done < n_units:
+        b, h0 = divmod(done, H)
+        hs = list(range(h0, min(H, h0 + n_units - done)))
+        t0 = time.perf_counter()
+        oracle.prefill(sl(w.q, b, hs), sl(w.k, b, hs), sl(w.v, b, hs), sl(w.g, b, hs),
+                       sl(w.beta, b, hs), None, nthreads=threads)
+        dt += time.perf_counter() - t0
+        done += len(hs)
+    return {"value": n_units * T / H / dt, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"sequence 0, heads 0..{len(heads) - 1} of the large prefill "
-                      f"({len(heads)} x {T} head-tokens, {dt:.1f} s), scaled to {H} heads"}
+            "sample": f"{n_units} (sequence, head) units x {T} tokens of the large prefill "
+                      f"({dt:.1f} s of oracle time), scaled to tokens of {H} heads"}
 
 
 def main():
@@ -233,6 +246,9 @@ def main():
                     help="rotate 8 state batches (512 MiB) so the state cannot stay in cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run a plain device-to-device copy of this many MiB "
+                         "(5 times), to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -240,6 +256,16 @@ def main():
         sys.exit(2)
 
     import torch
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration_copy_bytes": 4 * n, "dispatches": 5}), flush=True)
+        return
 
     from linear_attention_recurrence_02_amd import binding as gdn
     from linear_attention_recurrence_02_amd import inputs
@@ -295,8 +321,11 @@ def main():
                 f"{r['seconds']*1e3:.3f} ms, MFMA {100*r['mfma_frac']:.1f}%, "
                 f"HBM {100*r['hbm_frac']:.1f}%")
             pre[r["workload"]] = r
-            if w.name == "large_prefill" and not args.no_cpu_baseline:
-                pre[r["workload"]]["cpu_baseline"] = cpu_baseline_prefill(w)
+            if w.name == "large_prefill":
+                r["roofline"]["traffic"] = read_traffic(
+                    "prefill_large", source_digest("gdn_prefill_mfma.hip"))
+                if not args.no_cpu_baseline:
+                    r["cpu_baseline"] = cpu_baseline_prefill(w)
             del w
             torch.cuda.empty_cache()
         result["prefill"] = pre

@@ -103,7 +103,7 @@ int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
         if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
     if (!aligned(g, 4) || !aligned(beta, 4)) return GDN_ERR_INVALID_ARG;
     const int64_t units = B * H;
-    if (units >= kMaxDim) return GDN_ERR_INVALID_ARG;
+    if (units >= kMaxDim / 2) return GDN_ERR_INVALID_ARG;   // two workgroups per head
     const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
     const int64_t vec_bytes = units * gdn::kHeadDim * esz;
     const Range rq = span_of(q, vec_bytes), rk = span_of(k, vec_bytes),
