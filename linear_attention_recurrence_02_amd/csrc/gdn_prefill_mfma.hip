@@ -130,39 +130,49 @@ __device__ __forceinline__ bf16x8 rd_pkT(const bf16 *m, int row, int kb, int q) 
 
 // x = hi + lo with hi = x rounded to bf16 and lo the rounded remainder:
 // |x - hi - lo| <= 2^-17 |x|.  Two values are split at a time: one packed
-// conversion gives the hi pair, whose halves are widened back by a shift and a
-// mask to form the remainders.
-__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+// conversion gives the hi pair; v_dot2_f32_bf16 against (-1, 0) or (0, -1)
+// subtracts one bf16 half from its fp32 source exactly, giving the remainders
+// in one instruction each; a second packed conversion rounds them.  The two
+// multiplier pairs are held in SGPRs that the compiler cannot see through (as
+// folded inline constants the bf16 pair encodings are not preserved).
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ void split2(float a, float b, uint32_t *hi, uint32_t *lo) {
-    bf16x2 h;
-    h[0] = static_cast<bf16>(a);
-    h[1] = static_cast<bf16>(b);
-    const uint32_t hb = __builtin_bit_cast(uint32_t, h);
-    bf16x2 r;
-    r[0] = static_cast<bf16>(a - __builtin_bit_cast(float, hb << 16));
-    r[1] = static_cast<bf16>(b - __builtin_bit_cast(float, hb & 0xffff0000u));
-    *hi = hb;
-    *lo = __builtin_bit_cast(uint32_t, r);
-}
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+struct Splitter {
+    bf16x2 m_lo, m_hi;            // (-1, 0) and (0, -1)
+    __device__ static Splitter make() {
+        uint32_t a, b;
+        asm volatile("s_mov_b32 %0, 0x0000bf80" : "=s"(a));
+        asm volatile("s_mov_b32 %0, 0xbf800000" : "=s"(b));
+        return Splitter{__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b)};
+    }
+    __device__ void split2(float a, float b, uint32_t *hi, uint32_t *lo) const {
+        bf16x2 h;
+        h[0] = static_cast<bf16>(a);
+        h[1] = static_cast<bf16>(b);
+        bf16x2 r;
+        r[0] = static_cast<bf16>(__builtin_amdgcn_fdot2_f32_bf16(h, m_lo, a, false));
+        r[1] = static_cast<bf16>(__builtin_amdgcn_fdot2_f32_bf16(h, m_hi, b, false));
+        *hi = __builtin_bit_cast(uint32_t, h);
+        *lo = __builtin_bit_cast(uint32_t, r);
+    }
+};
 
 // hi/lo split of two result tiles (rows kb..kb+15 -> elements 0..3, rows
 // kb+16..kb+31 -> elements 4..7): a B operand in the permuted k order.
-__device__ __forceinline__ void split_pk(f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
+__device__ __forceinline__ void split_pk(const Splitter &sp, f32x4 a, f32x4 b, bf16x8 &hi, bf16x8 &lo) {
     uint32_t h[4], o[4];
-    split2(a[0], a[1], &h[0], &o[0]);
-    split2(a[2], a[3], &h[1], &o[1]);
-    split2(b[0], b[1], &h[2], &o[2]);
-    split2(b[2], b[3], &h[3], &o[3]);
+    sp.split2(a[0], a[1], &h[0], &o[0]);
+    sp.split2(a[2], a[3], &h[1], &o[1]);
+    sp.split2(b[0], b[1], &h[2], &o[2]);
+    sp.split2(b[2], b[3], &h[3], &o[3]);
     hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
     lo = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], o[2], o[3]});
 }
 // hi/lo split of one tile used as a 16-deep operand (elements 4..7 zero).
-__device__ __forceinline__ void split_half(f32x4 a, bf16x8 &hi, bf16x8 &lo) {
+__device__ __forceinline__ void split_half(const Splitter &sp, f32x4 a, bf16x8 &hi, bf16x8 &lo) {
     uint32_t h[2], o[2];
-    split2(a[0], a[1], &h[0], &o[0]);
-    split2(a[2], a[3], &h[1], &o[1]);
+    sp.split2(a[0], a[1], &h[0], &o[0]);
+    sp.split2(a[2], a[3], &h[1], &o[1]);
     hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], 0u, 0u});
     lo = __builtin_bit_cast(bf16x8, u32x4{o[0], o[1], 0u, 0u});
 }
@@ -177,18 +187,20 @@ __device__ __forceinline__ void store_hilo(bf16 *hi, bf16 *lo, int idx, float x)
 // entries.
 __device__ __forceinline__ bf16x8 as_bf(f32x4 x) { return __builtin_bit_cast(bf16x8, x); }
 
-// Loads are always issued (rows past the chunk read the sequence's first row
-// and are replaced by zeros) so that every period issues the same load
-// sequence and the wait counts before each use stay exact.
+// Loads are always issued, rows past the chunk reading the sequence's first row
+// instead, so that every period issues the same load sequence.  Nothing here
+// consumes the loaded registers: the tail mask is applied when the rows are
+// stored (store_rows), so the loads stay in flight until then.
 __device__ __forceinline__ void load_rows(f32x4 *dst, const bf16 *src, int64_t start, int64_t row0,
                                           int r, int nv, int64_t H, int64_t h, int q) {
-    const bool ok = r < nv;
-    const bf16 *p = src + ((ok ? row0 + r : start) * H + h) * D + 8 * q;
+    const bf16 *p = src + ((r < nv ? row0 + r : start) * H + h) * D + 8 * q;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const f32x4 x = *reinterpret_cast<const f32x4 *>(p + 32 * s);
-        dst[s] = ok ? x : zero4();
-    }
+    for (int s = 0; s < 4; ++s) dst[s] = *reinterpret_cast<const f32x4 *>(p + 32 * s);
+}
+// Zero the rows past the chunk's end (the token_valid padding), in place.
+__device__ __forceinline__ void mask_rows(f32x4 *x, bool ok) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x[s] = ok ? x[s] : zero4();
 }
 __device__ __forceinline__ void store_rows(bf16 *tile, const f32x4 *src, int r, int q) {
 #pragma unroll
@@ -213,6 +225,7 @@ struct Unit {
 struct Producer {
     f32x4 pK[4], pQ[4], pV[4];
     float pg, pb;
+    Splitter sp;
 
     // chunk pc may lie past the sequence (nothing valid is read then); the
     // sequence has at least one token whenever these are called.
@@ -220,21 +233,23 @@ struct Producer {
         const int nv = u.rows_in(pc);
         load_rows(pK, u.k, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, qd);
         load_rows(pV, u.v, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, qd);
-        const bool ok = l < nv;
-        const int64_t gi = (ok ? u.row0(pc) + l : u.start) * u.H + u.h;
-        const float gv = u.g[gi], bv = u.beta[gi];
-        pg = ok ? gv : 0.f;
-        pb = ok ? bv : 0.f;
+        const int64_t gi = (l < nv ? u.row0(pc) + l : u.start) * u.H + u.h;
+        pg = u.g[gi];
+        pb = u.beta[gi];
     }
     __device__ void prefetch_q(const Unit &u, int pc, int p, int r16, int qd) {
         load_rows(pQ, u.q, u.start, u.row0(pc), 16 * p + r16, u.rows_in(pc), u.H, u.h, qd);
     }
 
-    // phase A: stage K; scan the log-decay (wave p = 0)
-    __device__ void phase_a(Smem &sm, int nb, int p, int l, int r16, int qd) {
+    // phase A: stage K (masked in place: the Gram tiles use these registers);
+    // scan the log-decay (wave p = 0)
+    __device__ void phase_a(Smem &sm, int nb, int nv, int p, int l, int r16, int qd) {
+        mask_rows(pK, 16 * p + r16 < nv);
         store_rows(sm.K[nb], pK, 16 * p + r16, qd);
         if (p == 0) {
-            float x = pg;
+            const bool ok = l < nv;
+            float x = ok ? pg : 0.f;
+            pb = ok ? pb : 0.f;
 #pragma unroll
             for (int off = 1; off < 64; off <<= 1) {
                 const float y = __shfl_up(x, off);
@@ -297,7 +312,8 @@ struct Producer {
     // phase B: stage V; K K^T tiles -> N; diagonal block P of T.  Compiled
     // once per row block P so that every tile loop is unrolled.
     template <int P>
-    __device__ void phase_b(Smem &sm, int nb, int r16, int qd) {
+    __device__ void phase_b(Smem &sm, int nb, int nv, int r16, int qd) {
+        mask_rows(pV, 16 * P + r16 < nv);
         store_rows(sm.V, pV, 16 * P + r16, qd);
         const bf16 *Kn = sm.K[nb];
         const float *G2 = sm.G2[nb];
@@ -336,7 +352,7 @@ struct Producer {
             for (int e = 0; e < 4; ++e)
                 nv[e] = bt * (__builtin_amdgcn_exp2f(g2t - G2[16 * P + 4 * qd + e]) * kk[mj][e]);
             bf16x8 h, lo;
-            split_half(nv, h, lo);
+            split_half(sp, nv, h, lo);
             bf16 *blk = sm.No[oblk(mj, P)][0];
             *reinterpret_cast<bf16x4 *>(&blk[r16 * NOS + 4 * qd]) = h.lo;
             *reinterpret_cast<bf16x4 *>(&sm.No[oblk(mj, P)][1][r16 * NOS + 4 * qd]) = lo.lo;
@@ -365,7 +381,8 @@ struct Producer {
     }
 
     // phase C: stage Q; column block p (< 3) of T: T_ip = -T_ii sum_k N_ik T_kp
-    __device__ void phase_c(Smem &sm, int nb, int p, int r16, int qd) {
+    __device__ void phase_c(Smem &sm, int nb, int nv, int p, int r16, int qd) {
+        mask_rows(pQ, 16 * p + r16 < nv);
         store_rows(sm.Q, pQ, 16 * p + r16, qd);
         if (p >= 3) return;
         const int j = p;
@@ -392,7 +409,7 @@ struct Producer {
                     bh = half4(th);
                     bl = half4(tl);
                 } else {
-                    split_half(Tc[kk], bh, bl);
+                    split_half(sp, Tc[kk], bh, bl);
                 }
                 Z = mfma3(ah, al, bh, bl, Z);
             }
@@ -401,7 +418,7 @@ struct Producer {
             const bf16x8 ah = half4(*reinterpret_cast<const bf16x4 *>(&Tn[ti]));
             const bf16x8 al = half4(*reinterpret_cast<const bf16x4 *>(&Tnl[ti]));
             bf16x8 bh, bl;
-            split_half(Z, bh, bl);
+            split_half(sp, Z, bh, bl);
             f32x4 Tij = mfma3(ah, al, bh, bl, zero4());
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -440,44 +457,57 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 
     if (wave >= 4) {
         // ======================= producer waves =======================
-        // Every iteration executes exactly three barriers, as the consumers do.
+        // Barrier count matches the consumers': 4 + 3 * nch.  The prologue
+        // prepares chunk 0, each loop period prepares chunk c+1 (and A of chunk
+        // c), the last period only A of the last chunk.  The loop body is
+        // straight-line so that the prefetch loads (K, V after phase B, Q after
+        // phase C) are consumed in the order they were issued.
+        if (nch == 0) {
+            __syncthreads();
+            __syncthreads();
+            __syncthreads();
+            __syncthreads();
+            return;
+        }
         Producer pr;
         pr.pg = pr.pb = 0.f;
-        if (nch > 0) {
-            pr.prefetch_kv(u, 0, w, l, r16, qd);
-            pr.prefetch_q(u, 0, w, r16, qd);
-        }
+        pr.sp = Splitter::make();
+        auto gram_qk = [&](int c) {
+            switch (w) {
+            case 0: pr.gram_qk<0>(sm, c & 1, r16, qd); break;
+            case 1: pr.gram_qk<1>(sm, c & 1, r16, qd); break;
+            case 2: pr.gram_qk<2>(sm, c & 1, r16, qd); break;
+            default: pr.gram_qk<3>(sm, c & 1, r16, qd); break;
+            }
+        };
+        auto prepare = [&](int pc) {          // phases A..C for chunk pc, three barriers
+            const int nb = pc & 1, pnv = u.rows_in(pc);
+            pr.phase_a(sm, nb, pnv, w, l, r16, qd);
+            __syncthreads();
+            switch (w) {
+            case 0: pr.phase_b<0>(sm, nb, pnv, r16, qd); break;
+            case 1: pr.phase_b<1>(sm, nb, pnv, r16, qd); break;
+            case 2: pr.phase_b<2>(sm, nb, pnv, r16, qd); break;
+            default: pr.phase_b<3>(sm, nb, pnv, r16, qd); break;
+            }
+            pr.prefetch_kv(u, pc + 1, w, l, r16, qd);
+            __syncthreads();
+            pr.phase_c(sm, nb, pnv, w, r16, qd);
+            pr.prefetch_q(u, pc + 1, w, r16, qd);
+            __syncthreads();
+        };
+        pr.prefetch_kv(u, 0, w, l, r16, qd);
+        pr.prefetch_q(u, 0, w, r16, qd);
         __syncthreads();
-        for (int c = -1; c < nch; ++c) {
-            const int pc = c + 1, nb = pc & 1;   // chunk being prepared, its buffers
-            const bool work = pc < nch;
-            if (work) pr.phase_a(sm, nb, w, l, r16, qd);
-            if (c >= 0) {
-                // A of chunk c, whose K and Q were staged in the previous period
-                switch (w) {
-                case 0: pr.gram_qk<0>(sm, c & 1, r16, qd); break;
-                case 1: pr.gram_qk<1>(sm, c & 1, r16, qd); break;
-                case 2: pr.gram_qk<2>(sm, c & 1, r16, qd); break;
-                default: pr.gram_qk<3>(sm, c & 1, r16, qd); break;
-                }
-            }
-            __syncthreads();
-            if (work) {
-                switch (w) {
-                case 0: pr.phase_b<0>(sm, nb, r16, qd); break;
-                case 1: pr.phase_b<1>(sm, nb, r16, qd); break;
-                case 2: pr.phase_b<2>(sm, nb, r16, qd); break;
-                default: pr.phase_b<3>(sm, nb, r16, qd); break;
-                }
-                pr.prefetch_kv(u, pc + 1, w, l, r16, qd);
-            }
-            __syncthreads();
-            if (work) {
-                pr.phase_c(sm, nb, w, r16, qd);
-                pr.prefetch_q(u, pc + 1, w, r16, qd);
-            }
-            __syncthreads();
+        prepare(0);                           // the period before the consumers start
+        for (int c = 0; c + 1 < nch; ++c) {
+            gram_qk(c);                       // A of chunk c, consumed in its phase B
+            prepare(c + 1);
         }
+        gram_qk(nch - 1);
+        __syncthreads();
+        __syncthreads();
+        __syncthreads();
         return;
     }
 
@@ -504,6 +534,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     __syncthreads();
 
     const uint32_t HD = static_cast<uint32_t>(H) * D;
+    const Splitter sp = Splitter::make();
     for (int c = 0; c < nch; ++c) {
         const int cur = c & 1;
         const int cnv = u.rows_in(c);
@@ -526,7 +557,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             for (int s = 0; s < 4; ++s) {
                 bf16x8 sh[2], sl[2];
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) split_pk(S[4 * s + cc], S[4 * s + 2 + cc], sh[cc], sl[cc]);
+                for (int cc = 0; cc < 2; ++cc) split_pk(sp, S[4 * s + cc], S[4 * s + 2 + cc], sh[cc], sl[cc]);
                 bf16x8 ak[4], aq[4];
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -575,7 +606,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc)
-                    split_pk(KS[2 * s][cc], KS[2 * s + 1][cc], Rhi[s][cc], Rlo[s][cc]);
+                    split_pk(sp, KS[2 * s][cc], KS[2 * s + 1][cc], Rhi[s][cc], Rlo[s][cc]);
         }
         __syncthreads();
 
@@ -603,14 +634,14 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
-                    split_pk(Dt[2 * s][cc], Dt[2 * s + 1][cc], Rhi[s][cc], Rlo[s][cc]);   // now D
+                    split_pk(sp, Dt[2 * s][cc], Dt[2 * s + 1][cc], Rhi[s][cc], Rlo[s][cc]);   // now D
                     f32x4 a = Dt[2 * s][cc], b = Dt[2 * s + 1][cc];
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         a[e] *= sm.EC[cur][32 * s + 4 * qd + e];
                         b[e] *= sm.EC[cur][32 * s + 16 + 4 * qd + e];
                     }
-                    split_pk(a, b, Phi[s][cc], Plo[s][cc]);
+                    split_pk(sp, a, b, Phi[s][cc], Plo[s][cc]);
                 }
             const bf16 *Ah = sm.A[cur][0], *Al = sm.A[cur][1];
             bf16 *obase = O + (u.row0(c) * H + u.h) * D + 32 * w;
