@@ -84,7 +84,6 @@ struct __attribute__((aligned(16))) Smem {
     f16 Q[2][C * KS];             // queries, double-buffered
     f16 W[D * WS];                // -W, dk-major: W[d * WS + t] = -W_td
     f16 A[C * WS];                // decayed masked Q K^T, token-major
-    f16x4 U[4][4][2][64];         // U in the result-tile layout: [wave][token block][16-col tile][lane]
     float NR[4][16 * NS];         // diagonal blocks of N, row-major
     f16 Tii[4][16 * BS];          // T_ii
     f16 P[4][16 * BS];            // T_ii diag(beta exp G)
@@ -126,6 +125,10 @@ __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
     return x;
 }
+
+// Scheduling barrier: the compiler moves no instruction across it, so the
+// reads issued above it overlap the products issued below it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // LDS transpose load: in each group of 16 lanes, lane L passes the address of
 // halves 4(L%4)..+3 of row L/4 of a 4 x 16 block and receives column L of the
@@ -186,32 +189,41 @@ struct Unit {
     __device__ int64_t row0(int pc) const { return start + int64_t(pc) * C; }
 };
 
-// Producer wave p = 4..7 - 4 (lane r16 + 16 q).  While chunk c+1 is prepared,
-// the rows 16p + r16 of chunk c+2 sit in pK, pV, pQ (and token l's g and beta
-// in pg, pb): loaded a period ahead, converted to fp16 in phase 2 and stored in
-// phases 2 (K) and 3 (V, Q, the per-token scalars).
+// Producer wave p = 4..7 - 4 (lane r16 + 16 q).  Rows 16p + r16 of chunk c+2
+// (and token l's g and beta) are loaded into pK, pV, pQ (pg, pb) a period
+// ahead; in phase 2 of period c they are converted to fp16, K is stored, and V
+// and Q wait in hV, hQ for their phases (V: phase 1 of the next period, after
+// the consumers' W/U step has read the previous V; Q and the per-token scalars:
+// phase 3, after the consumers' output step has read the previous ones).
 struct Producer {
     f32x4 pK[4], pV[4], pQ[4];
+    f32x4 hV[4], hQ[4];
     float pg, pb;
     float sg2, seg, sec, sbt;     // scan results of the staged chunk (wave p = 0)
     f16x4 Ah[4];                  // A tiles of the chunk being prepared (phase 1 -> 3)
+    f16x4 Nop[3];                 // off-diagonal N blocks of the chunk (phase 1 -> 2)
 
-    __device__ void prefetch_k(const Unit &u, int pc, int p, int r16, int q) {
-        load_rows(pK, u.k, u.start, u.row0(pc), 16 * p + r16, u.rows_in(pc), u.H, u.h, q);
-    }
-    __device__ void prefetch_vq(const Unit &u, int pc, int p, int l, int r16, int q) {
+    __device__ void prefetch(const Unit &u, int pc, int p, int l, int r16, int q) {
         const int nv = u.rows_in(pc);
+        load_rows(pK, u.k, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
         load_rows(pV, u.v, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
         load_rows(pQ, u.q, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
         const int64_t gi = (l < nv ? u.row0(pc) + l : u.start) * u.H + u.h;
         pg = u.g[gi];
         pb = u.beta[gi];
     }
-    // Convert the prefetched rows (nv valid) and scan their log-decay.
-    __device__ void convert(int nv, int p, int l, int r16) {
+    // Convert the prefetched rows (nv valid), store K in buffer set nb, keep V
+    // and Q, scan the log-decay (wave p = 0).
+    __device__ void convert(Smem &sm, int nb, int nv, int p, int l, int r16, int q) {
         to_fp16_rows(pK, 16 * p + r16, nv);
+        store_rows(sm.K[nb], pK, 16 * p + r16, q);
         to_fp16_rows(pV, 16 * p + r16, nv);
         to_fp16_rows(pQ, 16 * p + r16, nv);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            hV[s] = pV[s];
+            hQ[s] = pQ[s];
+        }
         if (p == 0) {
             const bool okl = l < nv;
             float x = okl ? pg : 0.f;
@@ -227,12 +239,9 @@ struct Producer {
             sec = __builtin_amdgcn_exp2f(last - sg2);
         }
     }
-    __device__ void store_k(Smem &sm, int nb, int p, int r16, int q) {
-        store_rows(sm.K[nb], pK, 16 * p + r16, q);
-    }
-    __device__ void store_vq(Smem &sm, int nb, int p, int l, int r16, int q) {
-        store_rows(sm.V, pV, 16 * p + r16, q);
-        store_rows(sm.Q[nb], pQ, 16 * p + r16, q);
+    __device__ void store_v(Smem &sm, int p, int r16, int q) { store_rows(sm.V, hV, 16 * p + r16, q); }
+    __device__ void store_q(Smem &sm, int nb, int p, int l, int r16, int q) {
+        store_rows(sm.Q[nb], hQ, 16 * p + r16, q);
         if (p == 0) {
             sm.G2[nb][l] = sg2;
             sm.EG[nb][l] = seg;
@@ -242,37 +251,39 @@ struct Producer {
     }
 
     // Phase 1 for the chunk in buffer set nb: the Gram tiles of row block P of
-    // K K^T (-> N) and of column block IB = 3 - P of K Q^T (-> A, kept in Ah);
-    // T_PP by back substitution; M_Pj for j < P.  Masked decay factors take
-    // exp2(-inf) = 0 rather than a branch.
+    // K K^T (-> the diagonal block of N in LDS, the off-diagonal ones kept in
+    // Nop) and of column block IB = 3 - P of K Q^T (-> A, kept in Ah).  Masked
+    // decay factors take exp2(-inf) = 0 rather than a branch.
     template <int P>
-    __device__ void phase1(Smem &sm, int nb, int r16, int q) {
+    __device__ void gram(Smem &sm, int nb, int r16, int q) {
         constexpr int IB = 3 - P;
         constexpr float kNegInf = -__builtin_huge_valf();
         r16 = opaque(r16);
         q = opaque(q);
         const f16 *Kn = sm.K[nb], *Qn = sm.Q[nb];
         const float *G2 = sm.G2[nb], *Bt = sm.Bt[nb], *EG = sm.EG[nb];
+        constexpr int JM = P > IB ? P : IB;   // K row blocks read: 0..JM
         f32x4 kk[P + 1], qa[IB + 1];
 #pragma unroll
         for (int j = 0; j <= P; ++j) kk[j] = zero4();
 #pragma unroll
         for (int j = 0; j <= IB; ++j) qa[j] = zero4();
+        f16x8 kr[2][JM + 1], qr[2];
+        auto ld = [&](int s, f16x8 *k8, f16x8 &q8) {
+            const int col = 32 * s + 8 * q;
+#pragma unroll
+            for (int jb = 0; jb <= JM; ++jb) k8[jb] = rd8(Kn + (16 * jb + r16) * KS + col);
+            q8 = rd8(Qn + (16 * IB + r16) * KS + col);
+        };
+        ld(0, kr[0], qr[0]);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            const int col = 32 * s + 8 * q;
-            const f16x8 ak = rd8(Kn + (16 * P + r16) * KS + col);
-            const f16x8 bq = rd8(Qn + (16 * IB + r16) * KS + col);
+            if (s < 3) ld(s + 1, kr[(s + 1) & 1], qr[(s + 1) & 1]);
+            fence();
 #pragma unroll
-            for (int jb = 0; jb <= P; ++jb) {
-                const f16x8 b = jb == P ? ak : rd8(Kn + (16 * jb + r16) * KS + col);
-                kk[jb] = mfma(ak, b, kk[jb]);
-            }
+            for (int jb = 0; jb <= P; ++jb) kk[jb] = mfma(kr[s & 1][P], kr[s & 1][jb], kk[jb]);
 #pragma unroll
-            for (int jb = 0; jb <= IB; ++jb) {
-                const f16x8 a = jb == P ? ak : rd8(Kn + (16 * jb + r16) * KS + col);
-                qa[jb] = mfma(a, bq, qa[jb]);
-            }
+            for (int jb = 0; jb <= IB; ++jb) qa[jb] = mfma(kr[s & 1][jb], qr[s & 1], qa[jb]);
         }
         const f32x4 g2r = *reinterpret_cast<const f32x4 *>(&G2[16 * P + 4 * q]);   // rows 16P + 4q + e
         // kk[jb][e] = k_t . k_j, t = 16P + 4q + e, j = 16jb + r16 (symmetric on
@@ -289,7 +300,6 @@ struct Producer {
         }
         // Off-diagonal blocks N_Pj (rows t, column j): the A operand of
         // M_Pj^T = N_Pj^T T_PP^T.
-        f16x4 nop[P > 0 ? P : 1];
         {
             const f32x4 btr = *reinterpret_cast<const f32x4 *>(&Bt[16 * P + 4 * q]);
 #pragma unroll
@@ -298,7 +308,7 @@ struct Producer {
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = btr[e] * (__builtin_amdgcn_exp2f(g2r[e] - g2j) * kk[jb][e]);
-                nop[jb] = h4(x);
+                Nop[jb] = h4(x);
             }
         }
         // qa[jb][e] = k_j . q_t, j = 16jb + 4q + e, t = 16IB + r16 -> A_tj
@@ -317,31 +327,61 @@ struct Producer {
                 Ah[jb] = h4(x);
             }
         }
+    }
+
+    // Phase 2 for the chunk in buffer set nb: T_PP = (I + N_PP)^-1 by back
+    // substitution (row r16 per lane; the four lane groups repeat it), T_PP,
+    // P_P and P'_P to LDS, and M_Pj = T_PP N_Pj for j < P.
+    template <int P>
+    __device__ void solve(Smem &sm, int nb, int r16, int q) {
+        r16 = opaque(r16);
+        q = opaque(q);
+        const float *Bt = sm.Bt[nb], *EG = sm.EG[nb];
         // Row r16 of T_PP = (I + N_PP)^-1 by back substitution: y (I + N) = e_t,
-        // once y_u is final, y_j -= y_u N_uj for every j < u.  The rows of N are
-        // read four at a time.
+        // once y_u is final, y_j -= y_u N_uj for every j < u.  The rows of N
+        // are read in three batches (rows 15..12, 11..8, 7..1), each issued
+        // before the previous batch is used.
         const float *Nr = sm.NR[P];
         float y[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j) y[j] = j == r16 ? 1.f : 0.f;
+        f32x4 ra[4][4], rb[4][3], rc[7][2];
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            f32x4 rows[4][4];
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int uu = 15 - 4 * bb - r;
+            for (int v4 = 0; v4 < 4; ++v4)
+                if (4 * v4 < 15 - r) ra[r][v4] = *reinterpret_cast<const f32x4 *>(&Nr[(15 - r) * NS + 4 * v4]);
+        fence();
 #pragma unroll
-                for (int v4 = 0; v4 < 4; ++v4)
-                    if (uu >= 1 && 4 * v4 < uu)
-                        rows[r][v4] = *reinterpret_cast<const f32x4 *>(&Nr[uu * NS + 4 * v4]);
-            }
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int uu = 15 - 4 * bb - r;
-                if (uu < 1) continue;
+            for (int v4 = 0; v4 < 3; ++v4)
+                if (4 * v4 < 11 - r) rb[r][v4] = *reinterpret_cast<const f32x4 *>(&Nr[(11 - r) * NS + 4 * v4]);
+        fence();
 #pragma unroll
-                for (int j = 0; j < uu; ++j) y[j] -= rows[r][j >> 2][j & 3] * y[uu];
-            }
+        for (int r = 0; r < 4; ++r) {
+            const int uu = 15 - r;
+#pragma unroll
+            for (int j = 0; j < uu; ++j) y[j] -= ra[r][j >> 2][j & 3] * y[uu];
+        }
+        fence();
+#pragma unroll
+        for (int r = 0; r < 7; ++r)
+#pragma unroll
+            for (int v4 = 0; v4 < 2; ++v4)
+                if (4 * v4 < 7 - r) rc[r][v4] = *reinterpret_cast<const f32x4 *>(&Nr[(7 - r) * NS + 4 * v4]);
+        fence();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int uu = 11 - r;
+#pragma unroll
+            for (int j = 0; j < uu; ++j) y[j] -= rb[r][j >> 2][j & 3] * y[uu];
+        }
+#pragma unroll
+        for (int r = 0; r < 7; ++r) {
+            const int uu = 7 - r;
+#pragma unroll
+            for (int j = 0; j < uu; ++j) y[j] -= rc[r][j >> 2][j & 3] * y[uu];
         }
         if (q == 0) {
             f16x8 t0, t1, p0, p1, v0, v1;
@@ -374,55 +414,8 @@ struct Producer {
             const f16x8 bt = cat(rd4(&sm.Tii[P][r16 * BS + 4 * q]), zh4());
 #pragma unroll
             for (int jb = 0; jb < P; ++jb) {
-                const f32x4 mt = mfma(cat(nop[jb], zh4()), bt, zero4());
+                const f32x4 mt = mfma(cat(Nop[jb], zh4()), bt, zero4());
                 *reinterpret_cast<f16x4 *>(&sm.M[oblk(P, jb)][r16 * BS + 4 * q]) = neg(h4(mt));
-            }
-        }
-    }
-
-    // Phase 2: columns [32p, 32p+32) of W and of U for the chunk in buffer set
-    // nb, block by block; stores -W (dk-major) and U (result-tile layout).
-    __device__ void phase2(Smem &sm, int nb, int p, int r16, int q, int lane) {
-        r16 = opaque(r16);
-        q = opaque(q);
-        lane = opaque(lane);
-        const int trk = (4 * q + (r16 >> 2)) * KS + 4 * (r16 & 3);
-        const f16 *kb = sm.K[nb] + trk + 32 * p;
-        const f16 *vb = sm.V + trk + 32 * p;
-        const int co = r16 * BS + 4 * q;
-        f16x4 Wr[3][2], Ur[3][2];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f32x4 aw[2], au[2];
-            const f16x4 m0 = i >= 1 ? rd4(&sm.M[oblk(i > 0 ? i : 1, 0)][co]) : zh4();
-            const f16x8 a0w = cat(rd4(&sm.P[i][co]), m0);
-            const f16x8 a0u = cat(rd4(&sm.Pv[i][co]), m0);
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const f16x4 kx = rd_tr(kb + 16 * i * KS + 16 * cc);
-                const f16x4 vx = rd_tr(vb + 16 * i * KS + 16 * cc);
-                aw[cc] = mfma(a0w, cat(kx, i >= 1 ? Wr[0][cc] : zh4()), zero4());
-                au[cc] = mfma(a0u, cat(vx, i >= 1 ? Ur[0][cc] : zh4()), zero4());
-            }
-            if (i >= 2) {
-                const f16x4 m1 = rd4(&sm.M[oblk(i, 1)][co]);
-                const f16x4 m2 = i == 3 ? rd4(&sm.M[oblk(3, 2)][co]) : zh4();
-                const f16x8 a1 = cat(m1, m2);
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
-                    aw[cc] = mfma(a1, cat(Wr[1][cc], i == 3 ? Wr[2][cc] : zh4()), aw[cc]);
-                    au[cc] = mfma(a1, cat(Ur[1][cc], i == 3 ? Ur[2][cc] : zh4()), au[cc]);
-                }
-            }
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                const f16x4 w16 = h4(aw[cc]), u16 = h4(au[cc]);
-                if (i < 3) {
-                    Wr[i < 3 ? i : 0][cc] = w16;
-                    Ur[i < 3 ? i : 0][cc] = u16;
-                }
-                *reinterpret_cast<f16x4 *>(&sm.W[(32 * p + 16 * cc + r16) * WS + 16 * i + 4 * q]) = neg(w16);
-                sm.U[p][i][cc][lane] = u16;
             }
         }
     }
@@ -436,6 +429,65 @@ struct Producer {
             *reinterpret_cast<f16x4 *>(&sm.A[(16 * IB + r16) * WS + 16 * jb + 4 * q]) = Ah[jb];
     }
 };
+
+// Columns [32p, 32p+32) of W and of U for the chunk in buffer set nb, block by
+// block (run by consumer wave p); stores -W (dk-major) in LDS and returns U in
+// the result-tile layout, Uo[i][cc] = U rows 16i + 4q + e, column 32p + 16cc + r16.
+__device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q, f32x4 (*Uo)[2]) {
+    r16 = opaque(r16);
+    q = opaque(q);
+    const int trk = (4 * q + (r16 >> 2)) * KS + 4 * (r16 & 3);
+    const f16 *kb = sm.K[nb] + trk + 32 * p;
+    const f16 *vb = sm.V + trk + 32 * p;
+    const int co = r16 * BS + 4 * q;
+    // Everything but the previous blocks' W and U is known before the
+    // substitution starts: read it all first.
+    f16x4 kx[4][2], vx[4][2], pw[4], pu[4], mm[6];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            kx[i][cc] = rd_tr(kb + 16 * i * KS + 16 * cc);
+            vx[i][cc] = rd_tr(vb + 16 * i * KS + 16 * cc);
+        }
+        pw[i] = rd4(&sm.P[i][co]);
+        pu[i] = rd4(&sm.Pv[i][co]);
+    }
+#pragma unroll
+    for (int b = 0; b < 6; ++b) mm[b] = rd4(&sm.M[b][co]);
+    fence();
+    f16x4 Wr[3][2], Ur[3][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f32x4 aw[2], au[2];
+        const f16x4 m0 = i >= 1 ? mm[oblk(i > 0 ? i : 1, 0)] : zh4();
+        const f16x8 a0w = cat(pw[i], m0);
+        const f16x8 a0u = cat(pu[i], m0);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            aw[cc] = mfma(a0w, cat(kx[i][cc], i >= 1 ? Wr[0][cc] : zh4()), zero4());
+            au[cc] = mfma(a0u, cat(vx[i][cc], i >= 1 ? Ur[0][cc] : zh4()), zero4());
+        }
+        if (i >= 2) {
+            const f16x8 a1 = cat(mm[oblk(i, 1)], i == 3 ? mm[oblk(3, 2)] : zh4());
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                aw[cc] = mfma(a1, cat(Wr[1][cc], i == 3 ? Wr[2][cc] : zh4()), aw[cc]);
+                au[cc] = mfma(a1, cat(Ur[1][cc], i == 3 ? Ur[2][cc] : zh4()), au[cc]);
+            }
+        }
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            const f16x4 w16 = h4(aw[cc]), u16 = h4(au[cc]);
+            if (i < 3) {
+                Wr[i < 3 ? i : 0][cc] = w16;
+                Ur[i < 3 ? i : 0][cc] = u16;
+            }
+            *reinterpret_cast<f16x4 *>(&sm.W[(32 * p + 16 * cc + r16) * WS + 16 * i + 4 * q]) = neg(w16);
+            Uo[i][cc] = au[cc];
+        }
+    }
+}
 
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
@@ -462,29 +514,31 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         for (int i = (tid - 256) * 8; i < C * WS; i += 256 * 8)
             *reinterpret_cast<f32x4 *>(&sm.A[i]) = zero4();
         Producer pr;
-        pr.prefetch_k(u, 0, w, r16, qd);
-        pr.prefetch_vq(u, 0, w, l, r16, qd);
-        pr.convert(u.rows_in(0), w, l, r16);
-        pr.store_k(sm, 0, w, r16, qd);
-        pr.store_vq(sm, 0, w, l, r16, qd);
-        pr.prefetch_k(u, 1, w, r16, qd);
-        pr.prefetch_vq(u, 1, w, l, r16, qd);
+        pr.prefetch(u, 0, w, l, r16, qd);
+        pr.convert(sm, 0, u.rows_in(0), w, l, r16, qd);
+        pr.store_q(sm, 0, w, l, r16, qd);
+        pr.prefetch(u, 1, w, l, r16, qd);
         __syncthreads();
         // Period c (c = -1 .. nch-1) prepares chunk c+1 and stages chunk c+2;
         // the last period's work is on empty chunks and is never read.
         for (int c = -1; c < nch; ++c) {
             const int nb = (c + 1) & 1;
+            pr.store_v(sm, w, r16, qd);                // V of chunk c+1
             switch (w) {
-            case 0: pr.phase1<0>(sm, nb, r16, qd); break;
-            case 1: pr.phase1<1>(sm, nb, r16, qd); break;
-            case 2: pr.phase1<2>(sm, nb, r16, qd); break;
-            default: pr.phase1<3>(sm, nb, r16, qd); break;
+            case 0: pr.gram<0>(sm, nb, r16, qd); break;
+            case 1: pr.gram<1>(sm, nb, r16, qd); break;
+            case 2: pr.gram<2>(sm, nb, r16, qd); break;
+            default: pr.gram<3>(sm, nb, r16, qd); break;
             }
             __syncthreads();
-            pr.phase2(sm, nb, w, r16, qd, l);
-            pr.convert(u.rows_in(c + 2), w, l, r16);
-            pr.store_k(sm, nb ^ 1, w, r16, qd);      // nobody reads this K buffer in phase 2
-            pr.prefetch_k(u, c + 3, w, r16, qd);
+            switch (w) {
+            case 0: pr.solve<0>(sm, nb, r16, qd); break;
+            case 1: pr.solve<1>(sm, nb, r16, qd); break;
+            case 2: pr.solve<2>(sm, nb, r16, qd); break;
+            default: pr.solve<3>(sm, nb, r16, qd); break;
+            }
+            pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);   // K of chunk c+2 stored here
+            pr.prefetch(u, c + 3, w, l, r16, qd);
             __syncthreads();
             switch (w) {
             case 0: pr.store_a<0>(sm, r16, qd); break;
@@ -492,8 +546,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             case 2: pr.store_a<2>(sm, r16, qd); break;
             default: pr.store_a<3>(sm, r16, qd); break;
             }
-            pr.store_vq(sm, nb ^ 1, w, l, r16, qd);
-            pr.prefetch_vq(u, c + 3, w, l, r16, qd);
+            pr.store_q(sm, nb ^ 1, w, l, r16, qd);
             __syncthreads();
         }
         return;
@@ -527,9 +580,12 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         return;
     }
     __syncthreads();
-    // the period in which the producers prepare chunk 0
+    // the period in which the producers prepare chunk 0; its phase 3 is the
+    // W/U step of chunk 0
     __syncthreads();
     __syncthreads();
+    f32x4 Ur[4][2];
+    wu_step(sm, 0, w, r16, qd, Ur);
     __syncthreads();
 
     const uint32_t HD = static_cast<uint32_t>(H) * D;
@@ -540,26 +596,51 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         const int cnv = u.rows_in(c);
 
         // ======== phase 1: D = U - W S; S <- exp(G_C) S + K^T diag(exp(G_C - G)) D ========
+        // Operands are read one batch ahead of the products that use them; the
+        // scheduling barrier keeps each batch's reads above the previous batch's
+        // products so that their LDS latency overlaps matrix-core work.
         f16x8 Sh[4][2], Dh[2][2];
         {
+            const f16 *Wc = sm.W + trw;
+            auto ld_w = [&](int s, f16x8 *dst) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+                for (int m = 0; m < 4; ++m) {
+                    const f16 *wp = Wc + 32 * s * WS + 16 * m;
+                    dst[m] = cat(rd_tr(wp), rd_tr(wp + 16 * WS));
+                }
+            };
+            const f16 *Kc = sm.K[cur] + trk;
+            auto ld_k = [&](int i, f16x8 *dst) {
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) Sh[s][cc] = cat(h4(S[2 * s][cc]), h4(S[2 * s + 1][cc]));
+                for (int s2 = 0; s2 < 2; ++s2) {
+                    const f16 *kp = Kc + 32 * s2 * KS + 16 * i;
+                    dst[s2] = cat(rd_tr(kp), rd_tr(kp + 16 * KS));
+                }
+            };
+            f16x8 wa[2][4];
+            ld_w(0, wa[0]);
             f32x4 Dt[4][2];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) Dt[m][cc] = f4(sm.U[w][m][cc][l]);
+                for (int cc = 0; cc < 2; ++cc) Dt[m][cc] = Ur[m][cc];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const f16 *wp = sm.W + trw + 32 * s * WS + 16 * m;
-                    const f16x8 a = cat(rd_tr(wp), rd_tr(wp + 16 * WS));
+                for (int cc = 0; cc < 2; ++cc) Sh[s][cc] = cat(h4(S[2 * s][cc]), h4(S[2 * s + 1][cc]));
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) Dt[m][cc] = mfma(a, Sh[s][cc], Dt[m][cc]);
-                }
+            for (int s = 0; s < 4; ++s) {
+                if (s < 3) ld_w(s + 1, wa[(s + 1) & 1]);
+                fence();
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) Dt[m][cc] = mfma(wa[s & 1][m], Sh[s][cc], Dt[m][cc]);
+            }
+            f16x8 ka[2][4];
+            ld_k(0, ka[0]);
+            ld_k(1, ka[0] + 2);
+            fence();
             f16x8 Dp[2][2];
             const float *EC = sm.EC[cur];
 #pragma unroll
@@ -573,18 +654,24 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 }
             }
             const float eC = sm.EG[cur][C - 1];
-            const f16 *Kc = sm.K[cur] + trk;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < 8; ++i)
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) S[i][cc] *= eC;
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    const f16 *kp = Kc + 32 * s2 * KS + 16 * i;
-                    const f16x8 a = cat(rd_tr(kp), rd_tr(kp + 16 * KS));
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) S[i][cc] = mfma(a, Dp[s2][cc], S[i][cc]);
+            for (int ib = 0; ib < 4; ++ib) {
+                if (ib < 3) {
+                    ld_k(2 * ib + 2, ka[(ib + 1) & 1]);
+                    ld_k(2 * ib + 3, ka[(ib + 1) & 1] + 2);
                 }
+                fence();
+#pragma unroll
+                for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+                    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc)
+                            S[2 * ib + ii][cc] = mfma(ka[ib & 1][2 * ii + s2], Dp[s2][cc], S[2 * ib + ii][cc]);
             }
         }
         __syncthreads();
@@ -598,32 +685,53 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             f32x4 Ot[4][2];       // Ot[m][cc]: O[16m + r16][32w + 16cc + 4q + e]
 #pragma unroll
             for (int m = 0; m < 4; ++m) Ot[m][0] = Ot[m][1] = zero4();
-            const f16 *Qc = sm.Q[cur];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
+            const f16 *Qc = sm.Q[cur] + r16 * KS + 4 * qd;
+            auto ld_q = [&](int s, f16x8 *dst) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const f16 *qp = Qc + (16 * m + r16) * KS + 32 * s + 4 * qd;
-                    const f16x8 b = cat(rd4(qp), rd4(qp + 16));
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) Ot[m][cc] = mfma(Sh[s][cc], b, Ot[m][cc]);
+                    const f16 *qp = Qc + 16 * m * KS + 32 * s;
+                    dst[m] = cat(rd4(qp), rd4(qp + 16));
                 }
+            };
+            const f16 *Ac = sm.A + r16 * WS + 4 * qd;
+            f16x8 qb[2][4], ab[6];
+            ld_q(0, qb[0]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (s < 3) ld_q(s + 1, qb[(s + 1) & 1]);
+                if (s == 3) {
+                    int n = 0;
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+#pragma unroll
+                        for (int s2 = 0; s2 <= m / 2; ++s2) {
+                            const f16 *ap = Ac + 16 * m * WS + 32 * s2;
+                            ab[n++] = cat(rd4(ap), rd4(ap + 16));
+                        }
+                }
+                fence();
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) Ot[m][cc] = mfma(Sh[s][cc], qb[s & 1][m], Ot[m][cc]);
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const float eg = sm.EG[cur][16 * m + r16];
                 Ot[m][0] *= eg;
                 Ot[m][1] *= eg;
             }
+            {
+                int n = 0;
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+                for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int s2 = 0; s2 < 2; ++s2) {
-                    if (s2 > m / 2) continue;
-                    const f16 *ap = sm.A + (16 * m + r16) * WS + 32 * s2 + 4 * qd;
-                    const f16x8 b = cat(rd4(ap), rd4(ap + 16));
+                    for (int s2 = 0; s2 <= m / 2; ++s2) {
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) Ot[m][cc] = mfma(Dh[s2][cc], b, Ot[m][cc]);
-                }
+                        for (int cc = 0; cc < 2; ++cc) Ot[m][cc] = mfma(Dh[s2][cc], ab[n], Ot[m][cc]);
+                        ++n;
+                    }
+            }
             bf16 *obase = O + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
@@ -637,7 +745,8 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             }
         }
         __syncthreads();
-        // phase 3: the producers stage the next chunks
+        // ======== phase 3: W and U of the next chunk ========
+        if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, r16, qd, Ur);
         __syncthreads();
     }
 
