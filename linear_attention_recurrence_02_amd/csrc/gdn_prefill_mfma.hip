@@ -69,21 +69,26 @@ typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int C = 64;             // chunk length
 constexpr int D = kHeadDim;       // 128
-constexpr int KS = D + 8;         // fp16 row stride of the token-major K, V, Q, exp(G) Q tiles
-constexpr int WS = C + 8;         // fp16 row stride of W (dk-major) and A (token-major)
+constexpr int KS = D + 16;        // fp16 row stride of the token-major K and V tiles
+constexpr int QS = D + 12;        // fp16 row stride of the token-major Q tiles
+constexpr int WS = C + 16;        // fp16 row stride of W (dk-major)
+constexpr int AS = C + 4;         // fp16 row stride of A (token-major)
 constexpr int BS = 16 + 8;        // fp16 row stride of the 16 x 16 blocks T_ii, P_i, P'_i, M_ij
 constexpr int NS = 20;            // fp32 row stride of the diagonal blocks of N
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Rows are padded so that the rows a lane group touches in one instruction
-// start on different LDS banks and every address a lane forms is one per-lane
-// base plus a compile-time offset.
+// LDS layouts.  Each array's row stride (and, for K, V and W, an XOR of the
+// column with a few row bits) is chosen so that its main access patterns hit
+// 32 distinct banks per 128-byte wavefront slice: the 16-byte row reads and the
+// four-row transpose loads of K and V, the 8-byte row reads of Q and A, and the
+// transpose loads and 8-byte writes of W.  Every swizzle term is a per-lane
+// constant, so each address is a per-lane base plus a compile-time offset.
 struct __attribute__((aligned(16))) Smem {
-    f16 K[2][C * KS];             // keys, double-buffered
-    f16 V[C * KS];                // values
-    f16 Q[2][C * KS];             // queries, double-buffered
-    f16 W[D * WS];                // -W, dk-major: W[d * WS + t] = -W_td
-    f16 A[C * WS];                // decayed masked Q K^T, token-major
+    f16 K[2][C * KS];             // keys, double-buffered; column c of row t at c ^ ksw(t)
+    f16 V[C * KS];                // values, same layout as K
+    f16 Q[2][C * QS];             // queries, double-buffered
+    f16 W[D * WS];                // -W, dk-major: -W_td at d * WS + (t ^ wsw(d))
+    f16 A[C * AS];                // decayed masked Q K^T, token-major
     float NR[4][16 * NS];         // diagonal blocks of N, row-major
     f16 Tii[4][16 * BS];          // T_ii
     f16 P[4][16 * BS];            // T_ii diag(beta exp G)
@@ -94,6 +99,11 @@ struct __attribute__((aligned(16))) Smem {
     float EC[2][C];               // exp(G_last - G_t)
     float Bt[2][C];               // beta
 };
+
+// Column swizzles: K and V flip column bit 3 with row bit 2; W flips column
+// bits 2..3 with row bits 2..3.
+__device__ __forceinline__ int ksw(int row) { return ((row >> 2) & 1) << 3; }
+__device__ __forceinline__ int wsw(int row) { return ((row >> 2) & 3) << 2; }
 
 // index of the off-diagonal block (i, j), i > j, in Smem::M
 __device__ __forceinline__ constexpr int oblk(int i, int j) { return i * (i - 1) / 2 + j; }
@@ -173,9 +183,20 @@ __device__ __forceinline__ void to_fp16_rows(f32x4 *x, int r, int nv) {
         for (int s = 0; s < 4; ++s) x[s] = ok ? x[s] : zero4();
     }
 }
-__device__ __forceinline__ void store_rows(f16 *tile, const f32x4 *x, int r, int q) {
+__device__ __forceinline__ void store_rows_kv(f16 *tile, const f32x4 *x, int r, int q) {
+    const int c = (8 * q) ^ ksw(r);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4 *>(&tile[r * KS + 32 * s + 8 * q]) = x[s];
+    for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4 *>(&tile[r * KS + 32 * s + c]) = x[s];
+}
+// Q rows are only 8-byte aligned (QS is 2 mod 4 words): two 8-byte stores.
+__device__ __forceinline__ void store_rows_q(f16 *tile, const f32x4 *x, int r, int q) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        f32x2 *d = reinterpret_cast<f32x2 *>(&tile[r * QS + 32 * s + 8 * q]);
+        d[0] = f32x2{x[s][0], x[s][1]};
+        d[1] = f32x2{x[s][2], x[s][3]};
+    }
 }
 
 struct Unit {
@@ -216,7 +237,7 @@ struct Producer {
     // and Q, scan the log-decay (wave p = 0).
     __device__ void convert(Smem &sm, int nb, int nv, int p, int l, int r16, int q) {
         to_fp16_rows(pK, 16 * p + r16, nv);
-        store_rows(sm.K[nb], pK, 16 * p + r16, q);
+        store_rows_kv(sm.K[nb], pK, 16 * p + r16, q);
         to_fp16_rows(pV, 16 * p + r16, nv);
         to_fp16_rows(pQ, 16 * p + r16, nv);
 #pragma unroll
@@ -239,9 +260,9 @@ struct Producer {
             sec = __builtin_amdgcn_exp2f(last - sg2);
         }
     }
-    __device__ void store_v(Smem &sm, int p, int r16, int q) { store_rows(sm.V, hV, 16 * p + r16, q); }
+    __device__ void store_v(Smem &sm, int p, int r16, int q) { store_rows_kv(sm.V, hV, 16 * p + r16, q); }
     __device__ void store_q(Smem &sm, int nb, int p, int l, int r16, int q) {
-        store_rows(sm.Q[nb], hQ, 16 * p + r16, q);
+        store_rows_q(sm.Q[nb], hQ, 16 * p + r16, q);
         if (p == 0) {
             sm.G2[nb][l] = sg2;
             sm.EG[nb][l] = seg;
@@ -269,11 +290,12 @@ struct Producer {
 #pragma unroll
         for (int j = 0; j <= IB; ++j) qa[j] = zero4();
         f16x8 kr[2][JM + 1], qr[2];
+        const int kcol = (8 * q) ^ ksw(r16);
         auto ld = [&](int s, f16x8 *k8, f16x8 &q8) {
-            const int col = 32 * s + 8 * q;
 #pragma unroll
-            for (int jb = 0; jb <= JM; ++jb) k8[jb] = rd8(Kn + (16 * jb + r16) * KS + col);
-            q8 = rd8(Qn + (16 * IB + r16) * KS + col);
+            for (int jb = 0; jb <= JM; ++jb) k8[jb] = rd8(Kn + (16 * jb + r16) * KS + 32 * s + kcol);
+            const f16 *qp = Qn + (16 * IB + r16) * QS + 32 * s + 8 * q;
+            q8 = cat(rd4(qp), rd4(qp + 4));
         };
         ld(0, kr[0], qr[0]);
 #pragma unroll
@@ -426,7 +448,7 @@ struct Producer {
         constexpr int IB = 3 - P;
 #pragma unroll
         for (int jb = 0; jb <= IB; ++jb)
-            *reinterpret_cast<f16x4 *>(&sm.A[(16 * IB + r16) * WS + 16 * jb + 4 * q]) = Ah[jb];
+            *reinterpret_cast<f16x4 *>(&sm.A[(16 * IB + r16) * AS + 16 * jb + 4 * q]) = Ah[jb];
     }
 };
 
@@ -436,7 +458,7 @@ struct Producer {
 __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q, f32x4 (*Uo)[2]) {
     r16 = opaque(r16);
     q = opaque(q);
-    const int trk = (4 * q + (r16 >> 2)) * KS + 4 * (r16 & 3);
+    const int trk = (4 * q + (r16 >> 2)) * KS + ((4 * (r16 & 3)) ^ ksw(4 * q));
     const f16 *kb = sm.K[nb] + trk + 32 * p;
     const f16 *vb = sm.V + trk + 32 * p;
     const int co = r16 * BS + 4 * q;
@@ -483,7 +505,7 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q,
                 Wr[i < 3 ? i : 0][cc] = w16;
                 Ur[i < 3 ? i : 0][cc] = u16;
             }
-            *reinterpret_cast<f16x4 *>(&sm.W[(32 * p + 16 * cc + r16) * WS + 16 * i + 4 * q]) = neg(w16);
+            *reinterpret_cast<f16x4 *>(&sm.W[(32 * p + 16 * cc + r16) * WS + 16 * i + ((4 * q) ^ wsw(r16))]) = neg(w16);
             Uo[i][cc] = au[cc];
         }
     }
@@ -511,7 +533,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         // ======================= producer waves =======================
         if (nch == 0) return;
         // A entries above the diagonal blocks are never written.
-        for (int i = (tid - 256) * 8; i < C * WS; i += 256 * 8)
+        for (int i = (tid - 256) * 8; i < C * AS; i += 256 * 8)
             *reinterpret_cast<f32x4 *>(&sm.A[i]) = zero4();
         Producer pr;
         pr.prefetch(u, 0, w, l, r16, qd);
@@ -589,8 +611,8 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     __syncthreads();
 
     const uint32_t HD = static_cast<uint32_t>(H) * D;
-    const int trw = (4 * qd + (r16 >> 2)) * WS + 4 * (r16 & 3);
-    const int trk = (4 * qd + (r16 >> 2)) * KS + 4 * (r16 & 3);
+    const int trw = (4 * qd + (r16 >> 2)) * WS + ((4 * (r16 & 3)) ^ wsw(4 * qd));
+    const int trk = (4 * qd + (r16 >> 2)) * KS + ((4 * (r16 & 3)) ^ ksw(4 * qd));
     for (int c = 0; c < nch; ++c) {
         const int cur = c & 1;
         const int cnv = u.rows_in(c);
@@ -685,15 +707,15 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             f32x4 Ot[4][2];       // Ot[m][cc]: O[16m + r16][32w + 16cc + 4q + e]
 #pragma unroll
             for (int m = 0; m < 4; ++m) Ot[m][0] = Ot[m][1] = zero4();
-            const f16 *Qc = sm.Q[cur] + r16 * KS + 4 * qd;
+            const f16 *Qc = sm.Q[cur] + r16 * QS + 4 * qd;
             auto ld_q = [&](int s, f16x8 *dst) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const f16 *qp = Qc + 16 * m * KS + 32 * s;
+                    const f16 *qp = Qc + 16 * m * QS + 32 * s;
                     dst[m] = cat(rd4(qp), rd4(qp + 16));
                 }
             };
-            const f16 *Ac = sm.A + r16 * WS + 4 * qd;
+            const f16 *Ac = sm.A + r16 * AS + 4 * qd;
             f16x8 qb[2][4], ab[6];
             ld_q(0, qb[0]);
 #pragma unroll
@@ -705,7 +727,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     for (int m = 0; m < 4; ++m)
 #pragma unroll
                         for (int s2 = 0; s2 <= m / 2; ++s2) {
-                            const f16 *ap = Ac + 16 * m * WS + 32 * s2;
+                            const f16 *ap = Ac + 16 * m * AS + 32 * s2;
                             ab[n++] = cat(rd4(ap), rd4(ap + 16));
                         }
                 }
