@@ -23,31 +23,34 @@
 //
 // One 512-thread workgroup (8 waves) per (sequence, head), two roles:
 //   * consumer waves 0..3 walk the chunks in order.  Wave w owns dv columns
-//     [32w, 32w+32) of S, D and O; its share of S lives in 8 x 2 result tiles
-//     of v_mfma_f32_16x16x32_f16 (16 dk rows x 16 dv columns, 4 fp32 per lane:
-//     lane l holds rows 4(l/16)..+3 of column l%16) for the whole walk.  Per
-//     chunk: D = U - W S, S <- exp(G_C) S + K^T diag(exp(G_C - G)) D, then
-//     O = diag(exp G) Q S + A D with the S that entered the chunk.  S and D
-//     enter these products straight from their result tiles: a result tile is
-//     the B operand of a product over its rows when the partner A operand is
-//     read in the matching k order (lane group q takes k = 4q..4q+3 and
-//     16+4q..16+4q+3 of a 32-wide k step).  K^T and W are read with the gfx950
-//     LDS transpose load, which turns four 16-element rows into one column per
-//     lane.
+//     [32w, 32w+32) of S, D, U and O; its share of S lives in 8 x 2 result
+//     tiles of v_mfma_f32_16x16x32_f16 (16 dk rows x 16 dv columns, 4 fp32 per
+//     lane: lane l holds rows 4(l/16)..+3 of column l%16) for the whole walk.
+//     Per chunk: D = U - W S, S <- exp(G_C) S + K^T diag(exp(G_C - G)) D,
+//     O = diag(exp G) Q S + A D with the S that entered the chunk, and the W/U
+//     block substitution of the next chunk (its own 32 columns of W and U; U
+//     stays in registers).  S and D enter the products straight from their
+//     result tiles: a result tile is the B operand of a product over its rows
+//     when the partner A operand is read in the matching k order (lane group q
+//     takes k = 4q..4q+3 and 16+4q..16+4q+3 of a 32-wide k step), and, read
+//     as an A operand, it is its own transpose (O is computed as O^T).  K^T,
+//     V and W are read with the gfx950 LDS transpose load, which turns four
+//     16-element rows into one column per lane.
 //   * producer waves 4..7 prepare chunk c+1 while the consumers work on chunk
 //     c: the Gram tiles K K^T and K Q^T (exact products of fp16 copies of the
 //     bf16 inputs, fp32 accumulation) with the decay and beta applied on the
-//     accumulators; T_ii by back substitution in fp32 (one block per wave);
-//     M_ij and the W/U substitution on the matrix cores (each wave owns 32
-//     columns of W and of U); and the staging of chunk c+2 (rows prefetched
-//     into registers a period earlier, converted to fp16).
+//     accumulators; T_ii by back substitution in fp32 (one block per wave) and
+//     M_ij = T_ii N_ij; and the staging of chunk c+2 (rows prefetched into
+//     registers a period earlier, converted to fp16).
 //   Each chunk period has three barrier-separated phases:
-//     1: consumers D = U - W S, state update  | producers Gram tiles, N, T_ii,
-//                                            |   M_ij of chunk c+1
-//     2: consumers O = exp(G) Q S + A D      | producers W, U of chunk c+1
-//     3: -                                    | producers A, exp(G) Q of chunk
-//                                            |   c+1; stage chunk c+2
-//   Each array is written in a phase in which nobody reads it: K and the
+//     1: consumers D, state update (chunk c)  | producers Gram tiles (c+1),
+//                                            |   store V (c+1)
+//     2: consumers O (chunk c)               | producers T_ii, P_i, M_ij (c+1);
+//                                            |   convert c+2, store its K;
+//                                            |   prefetch c+3
+//     3: consumers W, U (chunk c+1)          | producers store A (c+1), Q and
+//                                            |   scalars (c+2)
+//   Each array is written in a phase in which nobody reads it: K, Q and the
 //   per-token scalars are double-buffered, everything else is single.
 //   The two roles run as two separate loops under a wave-uniform branch and
 //   execute the same number of barriers (1 + 3 (nch + 1)).
@@ -171,6 +174,25 @@ __device__ __forceinline__ void load_rows(f32x4 *dst, const bf16 *src, int64_t s
 #pragma unroll
     for (int s = 0; s < 4; ++s) dst[s] = *reinterpret_cast<const f32x4 *>(p + 32 * s);
 }
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts
+// within each row of 16 lanes, then the last lane of row 0 (of rows 0..1) is
+// added to rows 1 and 3 (rows 2 and 3).  Lanes a shift leaves without a source
+// add zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true);
+    return v + __builtin_bit_cast(float, t);
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+    x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
+    return x;
+}
+
 // Rows of one 16-token block held by a producer lane (row r, columns
 // 32s + 8q..+7 for s = 0..3), converted in place from bf16 to fp16; rows at or
 // past nv are zeroed (only a sequence's last chunk has such rows).
@@ -212,10 +234,11 @@ struct Unit {
 
 // Producer wave p = 4..7 - 4 (lane r16 + 16 q).  Rows 16p + r16 of chunk c+2
 // (and token l's g and beta) are loaded into pK, pV, pQ (pg, pb) a period
-// ahead; in phase 2 of period c they are converted to fp16, K is stored, and V
-// and Q wait in hV, hQ for their phases (V: phase 1 of the next period, after
-// the consumers' W/U step has read the previous V; Q and the per-token scalars:
-// phase 3, after the consumers' output step has read the previous ones).
+// ahead; in phase 2 of period c they are converted to fp16 and K is stored;
+// Q and the per-token scalars wait in hQ (sg2, ...) for phase 3, after the
+// consumers' output step has read the previous ones, and V waits in hV for
+// phase 1 of the next period, after the consumers' W/U step has read the
+// previous V.
 struct Producer {
     f32x4 pK[4], pV[4], pQ[4];
     f32x4 hV[4], hQ[4];
@@ -247,15 +270,9 @@ struct Producer {
         }
         if (p == 0) {
             const bool okl = l < nv;
-            float x = okl ? pg : 0.f;
             sbt = okl ? pb : 0.f;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off);
-                if (l >= off) x += y;
-            }
-            sg2 = x * kLog2e;
-            const float last = __shfl(sg2, 63);
+            sg2 = wave_prefix_sum(okl ? pg : 0.f) * kLog2e;
+            const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sg2), 63));
             seg = __builtin_amdgcn_exp2f(sg2);
             sec = __builtin_amdgcn_exp2f(last - sg2);
         }
@@ -559,7 +576,8 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             case 2: pr.solve<2>(sm, nb, r16, qd); break;
             default: pr.solve<3>(sm, nb, r16, qd); break;
             }
-            pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);   // K of chunk c+2 stored here
+            // K of chunk c+2 goes to the buffer nobody reads in phases 2 and 3
+            pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
             pr.prefetch(u, c + 3, w, l, r16, qd);
             __syncthreads();
             switch (w) {
