@@ -152,10 +152,15 @@ def bench_prefill(torch, gdn, w, iters, warmup):
     O = torch.empty_like(w.v)
     N = w.q.shape[0] if w.cu_seqlens is None else w.cu_seqlens.numel() - 1
     S_T = torch.empty((N, w.q.shape[2], DK, DV), dtype=torch.float32, device="cuda")
-    for _ in range(warmup):
+    # Warm up for at least `warmup` calls and about 0.25 s of GPU time, so that
+    # the clocks have settled before the timed calls.
+    t_end = time.perf_counter() + 0.25
+    n = 0
+    while n < warmup or time.perf_counter() < t_end:
         gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
                               O=O, S_T=S_T)
-    torch.cuda.synchronize()
+        torch.cuda.synchronize()
+        n += 1
     times = []
     for _ in range(iters):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
