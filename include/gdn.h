@@ -35,7 +35,9 @@
  *     enqueued; a rejected call enqueues nothing.  A failed launch returns
  *     GDN_ERR_HIP.
  *   - Preconditions not checked: g <= 0 and 0 <= beta <= 1 (the accuracy
- *     contract assumes them), finite inputs (NaN/Inf propagate).
+ *     contract assumes them), finite inputs (NaN/Inf propagate).  For bf16
+ *     io the prompt form rounds its matrix operands to fp16, so state, value
+ *     and delta magnitudes must stay well inside fp16's range (< 6.5e4).
  */
 #ifndef GDN_H
 #define GDN_H
