@@ -21,7 +21,7 @@ import numpy as np
 
 from .build import LIB_PATH, build as _build
 
-__all__ = ["prefill", "decode", "default_threads", "load"]
+__all__ = ["prefill", "prefill_states", "decode", "default_threads", "load"]
 
 _lib = None
 
@@ -40,6 +40,9 @@ def load():
     lib.gdn_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, ip, i64, i64, i64,
                                        i64, i64, dp, dp, ctypes.c_int]
     lib.gdn_oracle_prefill.restype = ctypes.c_int
+    lib.gdn_oracle_prefill_states.argtypes = [dp, dp, dp, dp, dp, dp, ip, i64, i64, i64,
+                                              i64, i64, dp, dp, dp, ctypes.c_int]
+    lib.gdn_oracle_prefill_states.restype = ctypes.c_int
     lib.gdn_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
                                       i64, dp, ctypes.c_int]
     lib.gdn_oracle_decode.restype = ctypes.c_int
@@ -70,14 +73,15 @@ def _ptr(a, ctype=ctypes.c_double):
     return a.ctypes.data_as(ctypes.POINTER(ctype))
 
 
-def prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads=None):
+def prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads=None, states=False):
     """Run the per-token recurrence over whole sequences.
 
     q, k: [B, T, H, dk]; v: [B, T, H, dv]; g, beta: [B, T, H].
     S0: [N, H, dk, dv] or None (zero state).
     cu_seqlens: None (N = B sequences of length T) or [N+1] int offsets into
     the packed token axis (then B must be 1 and T = cu_seqlens[-1]).
-    Returns (O [B, T, H, dv], S_T [N, H, dk, dv]) as fp64 numpy arrays.
+    Returns (O [B, T, H, dv], S_T [N, H, dk, dv]) as fp64 numpy arrays; with
+    states=True also S_tok [B, T, H, dk, dv], the state after every token.
     """
     q, k, v, g, beta, S0 = map(_f64, (q, k, v, g, beta, S0))
     B, T, H, dk = q.shape
@@ -99,13 +103,20 @@ def prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, nthreads=None):
         raise ValueError("oracle.prefill: S0 must be [N, H, dk, dv]")
     O = np.zeros((B, T, H, dv), dtype=np.float64)
     S_T = np.zeros((N, H, dk, dv), dtype=np.float64)
-    rc = load().gdn_oracle_prefill(
-        _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
-        _ptr(cu, ctypes.c_int64), N, T, H, dk, dv, _ptr(O), _ptr(S_T),
-        nthreads or default_threads())
+    if states:
+        S_tok = np.zeros((B, T, H, dk, dv), dtype=np.float64)
+        rc = load().gdn_oracle_prefill_states(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+            _ptr(cu, ctypes.c_int64), N, T, H, dk, dv, _ptr(O), _ptr(S_T), _ptr(S_tok),
+            nthreads or default_threads())
+    else:
+        rc = load().gdn_oracle_prefill(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(S0),
+            _ptr(cu, ctypes.c_int64), N, T, H, dk, dv, _ptr(O), _ptr(S_T),
+            nthreads or default_threads())
     if rc != 0:
         raise ValueError(f"oracle.prefill failed with code {rc}")
-    return O, S_T
+    return (O, S_T, S_tok) if states else (O, S_T)
 
 
 def decode(q, k, v, g, beta, S, nthreads=None):

@@ -71,6 +71,8 @@ typedef struct {
     int64_t s_qk, s_v, s_gb;   /* token strides for q/k, v/o, g/beta */
     const double *S_in;        /* NULL: zero initial state */
     double *S_out;             /* dk x dv; may equal S_in */
+    double *S_tok;             /* NULL, or the state after each token ... */
+    int64_t s_st;              /* ... with this stride (elements) between tokens */
 } unit_t;
 
 typedef struct {
@@ -86,10 +88,13 @@ static void run_unit(const unit_t *u, int64_t dk, int64_t dv, double *S, double 
         memcpy(S, u->S_in, (size_t)(dk * dv) * sizeof(double));
     else
         memset(S, 0, (size_t)(dk * dv) * sizeof(double));
-    for (int64_t t = 0; t < u->ntok; ++t)
+    for (int64_t t = 0; t < u->ntok; ++t) {
         gdn_token(S, dk, dv, u->q + t * u->s_qk, u->k + t * u->s_qk,
                   u->v + t * u->s_v, u->g[t * u->s_gb], u->beta[t * u->s_gb],
                   u->o + t * u->s_v, kv);
+        if (u->S_tok)
+            memcpy(u->S_tok + t * u->s_st, S, (size_t)(dk * dv) * sizeof(double));
+    }
     memcpy(u->S_out, S, (size_t)(dk * dv) * sizeof(double));
 }
 
@@ -150,11 +155,11 @@ static int run_pool(unit_t *units, int64_t nunits, int64_t dk, int64_t dv, int n
  * S_T may equal S0 (in-place update).  Returns 0, -1 for bad arguments, -2 for
  * an allocation failure.
  */
-int gdn_oracle_prefill(const double *q, const double *k, const double *v,
-                       const double *g, const double *beta, const double *S0,
-                       const int64_t *cu_seqlens, int64_t N, int64_t T,
-                       int64_t H, int64_t dk, int64_t dv, double *O,
-                       double *S_T, int nthreads)
+static int prefill_units(const double *q, const double *k, const double *v,
+                         const double *g, const double *beta, const double *S0,
+                         const int64_t *cu_seqlens, int64_t N, int64_t T,
+                         int64_t H, int64_t dk, int64_t dv, double *O,
+                         double *S_T, double *S_tok, int nthreads)
 {
     if (N < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || !S_T)
         return -1;
@@ -187,11 +192,41 @@ int gdn_oracle_prefill(const double *q, const double *k, const double *v,
             u->s_gb = H;
             u->S_in = S0 ? S0 + (n * H + h) * dk * dv : NULL;
             u->S_out = S_T + (n * H + h) * dk * dv;
+            u->S_tok = S_tok ? S_tok + (start * H + h) * dk * dv : NULL;
+            u->s_st = H * dk * dv;
         }
     }
     int rc = run_pool(units, nunits, dk, dv, nthreads);
     free(units);
     return rc;
+}
+
+int gdn_oracle_prefill(const double *q, const double *k, const double *v,
+                       const double *g, const double *beta, const double *S0,
+                       const int64_t *cu_seqlens, int64_t N, int64_t T,
+                       int64_t H, int64_t dk, int64_t dv, double *O,
+                       double *S_T, int nthreads)
+{
+    return prefill_units(q, k, v, g, beta, S0, cu_seqlens, N, T, H, dk, dv, O, S_T,
+                         NULL, nthreads);
+}
+
+/*
+ * The same run, also keeping the state after every token (what a caller needs
+ * to roll back a verify pass to any accepted prefix without a snapshot):
+ *   S_tok : [B, T, H, dk, dv] (packed: [1, T, H, dk, dv]); S_tok at token row r
+ *           of head h is the state after that token, within its sequence.
+ */
+int gdn_oracle_prefill_states(const double *q, const double *k, const double *v,
+                              const double *g, const double *beta, const double *S0,
+                              const int64_t *cu_seqlens, int64_t N, int64_t T,
+                              int64_t H, int64_t dk, int64_t dv, double *O,
+                              double *S_T, double *S_tok, int nthreads)
+{
+    if (!S_tok)
+        return -1;
+    return prefill_units(q, k, v, g, beta, S0, cu_seqlens, N, T, H, dk, dv, O, S_T,
+                         S_tok, nthreads);
 }
 
 /*

@@ -273,3 +273,46 @@ def test_chunk_form_unit_matches_transition_form_with_padding_only_tail():
     b = transition_form_unit(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0],
                              beta[0, :, 0], S0[0, 0])
     assert rel_err(a[0], b[0]) < 1e-12 and rel_err(a[1], b[1]) < 1e-12
+
+
+# --- per-token states (the rewindable verify form) --------------------------
+
+def test_token_states_equal_the_prompt_form_on_every_prefix():
+    # the state after token t equals the pages' chunk form run on the prefix
+    # through t (an independent NumPy implementation), in packed batches
+    rng = np.random.default_rng(31)
+    lens = [3, 16, 0, 9]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q, k, v, g, beta, _ = rand_case(rng, 1, int(cu[-1]), 2, 7, 5)
+    S0 = 0.1 * rng.standard_normal((len(lens), 2, 7, 5))
+    O, S_T, S_tok = oracle.prefill(q, k, v, g, beta, S0, cu_seqlens=cu, states=True)
+    assert S_tok.shape == (1, int(cu[-1]), 2, 7, 5)
+    for n, (s, e) in enumerate(zip(cu[:-1], cu[1:])):
+        for t in range(s, e):
+            for h in range(2):
+                _, Sp = chunk_form_unit(q[0, s:t + 1, h], k[0, s:t + 1, h], v[0, s:t + 1, h],
+                                        g[0, s:t + 1, h], beta[0, s:t + 1, h], S0[n, h], 5)
+                assert rel_err(S_tok[0, t, h], Sp) < 1e-12
+
+
+def test_token_states_follow_the_matrix_form():
+    # the pages' one-token matrix form, iterated, gives every emitted state
+    rng = np.random.default_rng(32)
+    q, k, v, g, beta, S0 = rand_case(rng, 2, 12, 2, 6, 9)
+    O, S_T, S_tok = oracle.prefill(q, k, v, g, beta, S0, states=True)
+    for b in range(2):
+        for h in range(2):
+            S = S0[b, h]
+            for t in range(12):
+                o, S = matrix_step(q[b, t, h], k[b, t, h], v[b, t, h], g[b, t, h], beta[b, t, h], S)
+                assert rel_err(S_tok[b, t, h], S) < 1e-12
+                assert rel_err(O[b, t, h], o) < 1e-12
+
+
+def test_token_states_keep_outputs_and_final_state():
+    rng = np.random.default_rng(33)
+    q, k, v, g, beta, S0 = rand_case(rng, 2, 10, 3, 8, 8)
+    O, S_T = oracle.prefill(q, k, v, g, beta, S0)
+    O2, S_T2, S_tok = oracle.prefill(q, k, v, g, beta, S0, states=True)
+    assert np.array_equal(O, O2) and np.array_equal(S_T, S_T2)
+    assert np.array_equal(S_tok[:, -1], S_T)
