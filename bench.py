@@ -189,6 +189,44 @@ def bench_prefill(torch, gdn, w, iters, warmup):
     }
 
 
+def bench_states(torch, gdn, w, iters):
+    """The rewindable verify form: gdn_prefill_states over a verify workload;
+    the figure is the state bytes it writes (plus the state and token bytes it
+    reads) per second."""
+    O = torch.empty_like(w.v)
+    B, T, H = w.q.shape[:3]
+    S_tok = torch.empty((B, T, H, DK, DV), dtype=torch.float32, device="cuda")
+    t_end = time.perf_counter() + 0.25
+    n = 0
+    while n < 2 or time.perf_counter() < t_end:
+        gdn.gdn_prefill_states(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, O=O,
+                               S_tok=S_tok)
+        torch.cuda.synchronize()
+        n += 1
+    times = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        gdn.gdn_prefill_states(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, O=O,
+                               S_tok=S_tok)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    t = statistics.median(times)
+    rows = B * T
+    nseq = len(w.meta["lengths"]) if w.cu_seqlens is not None else B
+    esz = w.q.element_size()
+    state_out = rows * H * STATE_BYTES
+    nbytes = state_out + (nseq * H * STATE_BYTES if w.S0 is not None else 0) \
+        + rows * H * (4 * DK * esz + 8)
+    return {
+        "workload": w.name + "_token_states", "tokens": rows, "heads": H, "seconds": t,
+        "tokens_per_s": rows / t, "state_write_gbs": state_out / t / 1e9,
+        "hbm_frac": nbytes / t / HBM_PEAK, "alg_bytes": nbytes,
+        "roofline": roofline("hbm", nbytes / t / 1e9, HBM_PEAK / 1e9, "GB/s"),
+    }
+
+
 def cpu_baseline_decode(w, target_s=12.0):
     """The oracle, as it stands, on the first n steps of the decode workload,
     n sized from a timed probe so that the sample takes about target_s."""
@@ -333,6 +371,13 @@ def main():
                     r["cpu_baseline"] = cpu_baseline_prefill(w)
             del w
             torch.cuda.empty_cache()
+        w = inputs.verify_blocks(device="cuda")
+        r = bench_states(torch, gdn, w, args.prefill_iters)
+        log(f"token states {r['workload']}: {r['state_write_gbs']:.1f} GB/s of states, "
+            f"{r['seconds']*1e3:.3f} ms, HBM {100*r['hbm_frac']:.1f}%")
+        pre[r["workload"]] = r
+        del w
+        torch.cuda.empty_cache()
         result["prefill"] = pre
 
     if dec is not None and not args.no_cpu_baseline:

@@ -110,6 +110,31 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
                       void *O, float *S_T, void *stream);
 
 /*
+ * gdn_prefill_states -- the prompt form that also keeps the state after every
+ * token.  The Qwen3.5-9B-npu model page (section "New in v2", the prompt
+ * lookup decoding item) checks a block of drafted tokens in one pass and,
+ * since a DeltaNet state cannot be rewound, snapshots the state first and
+ * re-feeds the accepted tokens.  With the state after each token kept,
+ * the caller takes S_tok at the last accepted token instead: no snapshot and no
+ * second pass.  Each token applies the page's one-token matrix form (as
+ * gdn_decode_step) to a state kept on chip; the result equals gdn_chunk_prefill's
+ * up to rounding.
+ *
+ *   q, k, v, g, beta, S0, cu_seqlens, B_or_N, T, H, dk, dv, O: as for
+ *               gdn_chunk_prefill (there is no chunk argument).
+ *   S_tok       [B, T, H, 128, 128] fp32 (packed: [1, T, H, 128, 128]): for each
+ *               token row and head, the state after that token within its
+ *               sequence (so a sequence's last row holds its final state).
+ *               64 KiB per token and head is written.
+ *   O and S_tok must not overlap each other, the inputs or S0 (GDN_ERR_ALIAS).
+ */
+int gdn_prefill_states(const void *q, const void *k, const void *v, int io_dtype,
+                       const float *g, const float *beta, const float *S0,
+                       const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                       int64_t H, int64_t dk, int64_t dv, void *O, float *S_tok,
+                       void *stream);
+
+/*
  * gdn_decode_step -- one token per (sequence, head) with the page's one-token
  * matrix form: with d = exp(g), a = S^T k and b = S^T q read in one pass over
  * S, delta = beta (v - d a), o = d b + (q.k) delta and S' = d S + k delta^T,

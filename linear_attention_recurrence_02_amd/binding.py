@@ -20,7 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_decode_step")
+EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_prefill_states",
+            "gdn_decode_step")
 
 _lib = None
 
@@ -51,6 +52,9 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_prefill.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                       i64, i64, i64, i64, vp, vp, vp]
     lib.gdn_chunk_prefill.restype = ctypes.c_int
+    lib.gdn_prefill_states.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
+                                       i64, i64, i64, vp, vp, vp]
+    lib.gdn_prefill_states.restype = ctypes.c_int
     lib.gdn_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i64,
                                     i64, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
@@ -133,6 +137,42 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
         _stream(stream))
     _check(st)
     return O, S_T
+
+
+def gdn_prefill_states(q, k, v, g, beta, S0=None, cu_seqlens=None, *, O=None, S_tok=None,
+                       stream=None):
+    """The prompt form that also keeps the state after every token.
+
+    Inputs as for gdn_chunk_prefill.  Returns (O, S_tok) with S_tok
+    [B, T, H, 128, 128] fp32: the state after each token row within its
+    sequence.  O/S_tok may be given to write in place.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed batches (cu_seqlens) need B == 1")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype \
+            or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape [B, T, H, d] and dtype")
+    if g.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("g and beta must be [B, T, H]")
+    if O is None:
+        O = torch.empty_like(v)
+    if S_tok is None:
+        S_tok = torch.empty((B, T, H, dk, dv), dtype=torch.float32, device=q.device)
+    if O.dtype != q.dtype or O.shape != v.shape:
+        raise ValueError("O must match v's shape and dtype")
+    if S_tok.shape != (B, T, H, dk, dv) or (S0 is not None and S0.shape != (N, H, dk, dv)):
+        raise ValueError("S_tok must be [B, T, H, dk, dv] and S0 [N, H, dk, dv]")
+    st = load_library().gdn_prefill_states(
+        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+        _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+        N, T, H, dk, dv, _ptr(O, name="O"), _ptr(S_tok, torch.float32, "S_tok"),
+        _stream(stream))
+    _check(st)
+    return O, S_tok
 
 
 def gdn_decode_step(q, k, v, g, beta, S, *, o=None, stream=None):

@@ -92,6 +92,49 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+int gdn_prefill_states(const void *q, const void *k, const void *v, int io_dtype,
+                       const float *g, const float *beta, const float *S0,
+                       const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                       int64_t H, int64_t dk, int64_t dv, void *O, float *S_tok,
+                       void *stream) {
+    if (!dims_ok(B_or_N) || !dims_ok(T) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
+    const int64_t N = B_or_N;
+    const int64_t rows = cu_seqlens ? T : N * T;
+    if (rows > 0 && (!q || !k || !v || !g || !beta || !O || !S_tok)) return GDN_ERR_INVALID_ARG;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (dk != gdn::kHeadDim || dv != gdn::kHeadDim) return GDN_ERR_UNSUPPORTED;
+    for (const void *p : {q, k, v, static_cast<const void *>(O), static_cast<const void *>(S_tok)})
+        if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    if (S0 && !aligned(S0, 16)) return GDN_ERR_INVALID_ARG;
+    if (!aligned(g, 4) || !aligned(beta, 4) || (cu_seqlens && !aligned(cu_seqlens, 4)))
+        return GDN_ERR_INVALID_ARG;
+
+    if (N * H >= kMaxDim / 2) return GDN_ERR_INVALID_ARG;   // two workgroups per unit
+    const int64_t state_elems = gdn::kHeadDim * gdn::kHeadDim;
+    if (rows > (int64_t(1) << 44) / (H * state_elems)) return GDN_ERR_INVALID_ARG;
+    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t tok_bytes = rows * H * gdn::kHeadDim * esz;
+    const int64_t gb_bytes = rows * H * 4;
+    const int64_t st_bytes = N * H * state_elems * 4;
+    const int64_t stok_bytes = rows * H * state_elems * 4;
+
+    const Range rq = span_of(q, tok_bytes), rk = span_of(k, tok_bytes),
+                rv = span_of(v, tok_bytes), rg = span_of(g, gb_bytes),
+                rb = span_of(beta, gb_bytes), rO = span_of(O, tok_bytes),
+                rSt = span_of(S_tok, stok_bytes),
+                rS0 = S0 ? span_of(S0, st_bytes) : Range{0, 0};
+    for (Range r : {rq, rk, rv, rg, rb, rS0, rSt})
+        if (overlap(rO, r)) return GDN_ERR_ALIAS;
+    for (Range r : {rq, rk, rv, rg, rb, rS0})
+        if (overlap(rSt, r)) return GDN_ERR_ALIAS;
+
+    gdn::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, N, T, H, 0,
+                       io_dtype == GDN_BF16, O, nullptr};
+    if (N == 0) return GDN_OK;
+    hipError_t e = gdn::launch_prefill_states(a, S_tok, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
                     const float *g, const float *beta, float *S, int64_t B,
                     int64_t H, int64_t dk, int64_t dv, void *o, void *stream) {

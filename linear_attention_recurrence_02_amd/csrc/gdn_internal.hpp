@@ -39,6 +39,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
 bool prefill_mfma_supports(const PrefillArgs &a);
+// The prompt form keeping the state after every token in S_tok (chunk unused).
+hipError_t launch_prefill_states(const PrefillArgs &a, float *S_tok, hipStream_t stream);
 
 // ---- small device helpers -------------------------------------------------
 

@@ -1,0 +1,158 @@
+// The prompt form with the state after every token kept (the rewindable verify
+// form): for each (sequence, head), starting from S0, the per-token gated delta
+// rule (Qwen3.5-9B-npu model page, "How it works" -> "Gated DeltaNet on the
+// NPU", the 1-token matrix form applied token by token):
+//     d = exp(g_t), a = S^T k_t, b = S^T q_t
+//     delta = beta_t (v_t - d a)
+//     o_t = d b + (q_t.k_t) delta
+//     S   = d S + k_t delta^T            -> written to S_tok[t]
+// A verify pass over a block of drafted tokens (the same page, section "New in
+// v2", prompt lookup decoding: the state is snapshotted because it cannot be
+// rewound) can then be rolled back to any accepted prefix by taking S_tok at
+// its last accepted token: no snapshot and no second pass.
+//
+// The work is bound by the state writes (64 KiB per token and head).  As in the
+// decode step, each head state is split into two 64-column halves, one
+// 256-thread workgroup per half; the half stays in registers across the
+// sequence (thread (wave w, lane l): columns 64 half + 4 (l%16)..+3, rows
+// rp + 16m with rp = 4w + l/16), and after each token every thread writes its
+// 8 x 16 bytes of the new state.  q and k of the token go through LDS (double-
+// buffered, so one barrier per token separates their write from the previous
+// token's reads); the column sums a and b are reduced across lanes and then
+// across the four waves through LDS.
+
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+template <typename IO>
+__global__ __launch_bounds__(256) void states_kernel(const IO *__restrict__ q,
+                                                     const IO *__restrict__ k,
+                                                     const IO *__restrict__ v,
+                                                     const float *__restrict__ g,
+                                                     const float *__restrict__ beta,
+                                                     const float *__restrict__ S0,
+                                                     const int32_t *__restrict__ cu_seqlens,
+                                                     int64_t T, int64_t H,
+                                                     IO *__restrict__ O,
+                                                     float *__restrict__ S_tok) {
+    constexpr int D = kHeadDim;
+    const int64_t unit = blockIdx.x >> 1;       // (sequence, head)
+    const int half = blockIdx.x & 1;            // value columns [64 half, 64 half + 64)
+    const int64_t h = unit % H;
+    int64_t start, len;
+    sequence_span(cu_seqlens, unit / H, T, start, len);
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, w = tid >> 6;
+    const int cg = lane & 15;
+    const int rp = 4 * w + (lane >> 4);
+    const int c0 = 64 * half + 4 * cg;          // first of this thread's 4 columns
+
+    __shared__ float sq[2][D], sk[2][D];
+    __shared__ float4 red_a[4][16], red_b[4][16];
+
+    float4 s[8];
+    if (S0) {
+        const float *S0u = S0 + unit * (D * D) + c0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) s[m] = *reinterpret_cast<const float4 *>(S0u + (rp + 16 * m) * D);
+    } else {
+#pragma unroll
+        for (int m = 0; m < 8; ++m) s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    for (int64_t t = 0; t < len; ++t) {
+        const int buf = static_cast<int>(t & 1);
+        const int64_t row = start + t;
+        const int64_t tok = (row * H + h) * D;
+        if (tid < D) {
+            sq[buf][tid] = to_f32(q[tok + tid]);
+            sk[buf][tid] = to_f32(k[tok + tid]);
+        }
+        float4 vv;
+        vv.x = to_f32(v[tok + c0]);
+        vv.y = to_f32(v[tok + c0 + 1]);
+        vv.z = to_f32(v[tok + c0 + 2]);
+        vv.w = to_f32(v[tok + c0 + 3]);
+        const float d = expf(g[row * H + h]);
+        const float bt = beta[row * H + h];
+        __syncthreads();
+
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float kr = sk[buf][rp + 16 * m], qr = sq[buf][rp + 16 * m];
+            a.x += s[m].x * kr; a.y += s[m].y * kr; a.z += s[m].z * kr; a.w += s[m].w * kr;
+            b.x += s[m].x * qr; b.y += s[m].y * qr; b.z += s[m].z * qr; b.w += s[m].w * qr;
+        }
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            a.x += __shfl_xor(a.x, off); a.y += __shfl_xor(a.y, off);
+            a.z += __shfl_xor(a.z, off); a.w += __shfl_xor(a.w, off);
+            b.x += __shfl_xor(b.x, off); b.y += __shfl_xor(b.y, off);
+            b.z += __shfl_xor(b.z, off); b.w += __shfl_xor(b.w, off);
+        }
+        if (lane < 16) {
+            red_a[w][cg] = a;
+            red_b[w][cg] = b;
+        }
+        float qk = sq[buf][lane] * sk[buf][lane] + sq[buf][lane + 64] * sk[buf][lane + 64];
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off);
+        __syncthreads();
+
+        float4 A = red_a[0][cg], Bq = red_b[0][cg];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+            const float4 x = red_a[ww][cg], y = red_b[ww][cg];
+            A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
+            Bq.x += y.x; Bq.y += y.y; Bq.z += y.z; Bq.w += y.w;
+        }
+        float4 dl;
+        dl.x = bt * (vv.x - d * A.x);
+        dl.y = bt * (vv.y - d * A.y);
+        dl.z = bt * (vv.z - d * A.z);
+        dl.w = bt * (vv.w - d * A.w);
+
+        float *St = S_tok + (row * H + h) * (D * D) + c0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const float kr = sk[buf][rp + 16 * m];
+            s[m].x = d * s[m].x + kr * dl.x;
+            s[m].y = d * s[m].y + kr * dl.y;
+            s[m].z = d * s[m].z + kr * dl.z;
+            s[m].w = d * s[m].w + kr * dl.w;
+            *reinterpret_cast<float4 *>(St + (rp + 16 * m) * D) = s[m];
+        }
+        if (rp == 0) {
+            IO *ou = O + tok + c0;
+            ou[0] = from_f32<IO>(d * Bq.x + qk * dl.x);
+            ou[1] = from_f32<IO>(d * Bq.y + qk * dl.y);
+            ou[2] = from_f32<IO>(d * Bq.z + qk * dl.z);
+            ou[3] = from_f32<IO>(d * Bq.w + qk * dl.w);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_states(const PrefillArgs &a, float *S_tok, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(2 * a.N * a.H)), block(256);
+    if (a.bf16) {
+        using T = __hip_bfloat16;
+        states_kernel<T><<<grid, block, 0, stream>>>(
+            static_cast<const T *>(a.q), static_cast<const T *>(a.k),
+            static_cast<const T *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
+            static_cast<T *>(a.O), S_tok);
+    } else {
+        states_kernel<float><<<grid, block, 0, stream>>>(
+            static_cast<const float *>(a.q), static_cast<const float *>(a.k),
+            static_cast<const float *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
+            static_cast<float *>(a.O), S_tok);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -89,6 +89,28 @@ def test_prefill_aliasing_rules(lib):
     assert prefill(lib, N=0, S_T=A + 256 * MB) == binding.GDN_OK        # S_T == S0
 
 
+def states(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB,
+           beta=A + 200 * MB, S0=A + 256 * MB, cu=None, N=2, T=64, H=2, dk=128,
+           dv=128, O=A + 512 * MB, S_tok=A + 1024 * MB):
+    return lib.gdn_prefill_states(q, k, v, dtype, g, beta, S0, cu, N, T, H, dk, dv, O,
+                                  S_tok, None)
+
+
+def test_prefill_states_validation(lib):
+    assert states(lib, S_tok=None) == binding.GDN_ERR_INVALID_ARG
+    assert states(lib, v=None) == binding.GDN_ERR_INVALID_ARG
+    assert states(lib, H=0) == binding.GDN_ERR_INVALID_ARG
+    assert states(lib, dk=64) == binding.GDN_ERR_UNSUPPORTED
+    assert states(lib, dtype=5) == binding.GDN_ERR_UNSUPPORTED
+    assert states(lib, S_tok=A + 1024 * MB + 8) == binding.GDN_ERR_INVALID_ARG
+    # S_tok holds 2 x 64 token rows x 2 heads x 64 KiB = 16 MiB
+    assert states(lib, S_tok=A + 256 * MB) == binding.GDN_ERR_ALIAS      # over S0
+    assert states(lib, S_tok=A + 120 * MB) == binding.GDN_ERR_ALIAS      # over k, v
+    assert states(lib, O=A + 1030 * MB) == binding.GDN_ERR_ALIAS         # O over S_tok
+    assert states(lib, N=0) == binding.GDN_OK
+    assert states(lib, N=0, S_tok=None, q=None, k=None, v=None, O=None) == binding.GDN_OK
+
+
 def test_decode_rejects_bad_calls(lib):
     assert decode(lib, S=None) == binding.GDN_ERR_INVALID_ARG
     assert decode(lib, B=-1) == binding.GDN_ERR_INVALID_ARG
