@@ -21,7 +21,7 @@ import numpy as np
 
 from .build import LIB_PATH, build as _build
 
-__all__ = ["prefill", "prefill_states", "decode", "default_threads", "load"]
+__all__ = ["prefill", "decode", "gated_rmsnorm", "default_threads", "load"]
 
 _lib = None
 
@@ -46,6 +46,8 @@ def load():
     lib.gdn_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, i64, i64, i64, i64,
                                       i64, dp, ctypes.c_int]
     lib.gdn_oracle_decode.restype = ctypes.c_int
+    lib.gdn_oracle_gated_rmsnorm.argtypes = [dp, dp, dp, i64, i64, ctypes.c_double, dp]
+    lib.gdn_oracle_gated_rmsnorm.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -143,3 +145,20 @@ def decode(q, k, v, g, beta, S, nthreads=None):
     if rc != 0:
         raise ValueError(f"oracle.decode failed with code {rc}")
     return (o[0] if single else o), S
+
+
+def gated_rmsnorm(o, z, w, eps):
+    """Gated RMS norm over the last axis: y = w * o / sqrt(mean(o^2) + eps) * silu(z).
+
+    o and z: any shape [..., dv] (the same); w: [dv].  Returns fp64 numpy y.
+    """
+    o, z, w = map(_f64, (o, z, w))
+    if z.shape != o.shape or w.shape != (o.shape[-1],):
+        raise ValueError("oracle.gated_rmsnorm: inconsistent shapes")
+    y = np.zeros_like(o)
+    dv = o.shape[-1]
+    rows = o.size // dv if dv else 0
+    rc = load().gdn_oracle_gated_rmsnorm(_ptr(o), _ptr(z), _ptr(w), rows, dv, float(eps), _ptr(y))
+    if rc != 0:
+        raise ValueError(f"oracle.gated_rmsnorm failed with code {rc}")
+    return y

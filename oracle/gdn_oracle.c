@@ -265,3 +265,36 @@ int gdn_oracle_decode(const double *q, const double *k, const double *v,
     free(units);
     return rc;
 }
+
+/*
+ * Gated RMS norm of output rows -- the norm that follows the recurrence inside
+ * a Gated DeltaNet block (Qwen3.5-4B -- Hexagon NPU (QHexRT) -- v81 page, the
+ * opening description of the text decoder: a short causal-conv FIFO, an SSM
+ * state and a gated RMSNorm; the Qwen3.5-9B-npu model page, "How it works" ->
+ * "fp16 precision of the DeltaNet output", relies on that norm being
+ * scale-invariant with eps scaled by the square of the factor).  Per row of dv
+ * values:
+ *
+ *     r   = 1 / sqrt(mean_j(o_j^2) + eps)
+ *     y_j = w_j * (o_j * r) * silu(z_j),     silu(x) = x / (1 + exp(-x))
+ *
+ *   o, z, y : [rows, dv]     w : [dv] (one weight vector shared by every row)
+ */
+int gdn_oracle_gated_rmsnorm(const double *o, const double *z, const double *w,
+                             int64_t rows, int64_t dv, double eps, double *y)
+{
+    if (rows < 0 || dv <= 0 || !(eps >= 0.0))
+        return -1;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double *orow = o + r * dv, *zrow = z + r * dv;
+        double ss = 0.0;
+        for (int64_t j = 0; j < dv; ++j)
+            ss += orow[j] * orow[j];
+        const double inv = 1.0 / sqrt(ss / (double)dv + eps);
+        for (int64_t j = 0; j < dv; ++j) {
+            const double silu = zrow[j] / (1.0 + exp(-zrow[j]));
+            y[r * dv + j] = w[j] * (orow[j] * inv) * silu;
+        }
+    }
+    return 0;
+}

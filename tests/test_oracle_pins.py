@@ -316,3 +316,72 @@ def test_token_states_keep_outputs_and_final_state():
     O2, S_T2, S_tok = oracle.prefill(q, k, v, g, beta, S0, states=True)
     assert np.array_equal(O, O2) and np.array_equal(S_T, S_T2)
     assert np.array_equal(S_tok[:, -1], S_T)
+
+
+# --- the gated RMS norm on the output (the norm that follows the recurrence) ---
+
+def test_gated_rmsnorm_closed_form_two_columns():
+    # Hand-computed: rows of two values, so mean(o^2) = (o0^2 + o1^2) / 2; gates
+    # at +-ln 3, where sigmoid is 3/4 and 1/4; distinct weights per column.
+    l3 = np.log(3.0)
+    o = np.array([[3.0, 4.0], [-1.0, 0.0]])
+    z = np.array([[l3, -l3], [l3, l3]])
+    w = np.array([2.0, 0.5])
+    y = oracle.gated_rmsnorm(o, z, w, 0.0)
+    r = 1.0 / np.sqrt(12.5)
+    expect = np.array([[2.0 * 3.0 * r * 0.75 * l3, 0.5 * 4.0 * r * (-0.25 * l3)],
+                       [2.0 * -1.0 * np.sqrt(2.0) * 0.75 * l3, 0.0]])
+    assert rel_err(y, expect) < 1e-14
+    # eps sits inside the root, added to the mean square: 12.5 + 12.5 = 25
+    y = oracle.gated_rmsnorm(o[:1], z[:1], w, 12.5)
+    assert rel_err(y, np.array([[2.0 * 3.0 / 5.0 * 0.75 * l3, 0.5 * 4.0 / 5.0 * (-0.25 * l3)]])) < 1e-14
+
+
+def test_gated_rmsnorm_rows_have_unit_rms_once_the_gate_is_divided_out():
+    from scipy.special import expit
+    rng = np.random.default_rng(31)
+    o = rng.standard_normal((9, 128)) * rng.uniform(1e-3, 10.0, (9, 1))
+    z = rng.standard_normal((9, 128))
+    y = oracle.gated_rmsnorm(o, z, np.ones(128), 0.0)
+    unit = y / (z * expit(z))
+    assert np.allclose(np.sqrt(np.mean(unit ** 2, axis=-1)), 1.0, rtol=1e-13, atol=0)
+    assert np.allclose(unit * np.sqrt(np.mean(o ** 2, axis=-1, keepdims=True)), o,
+                       rtol=1e-13, atol=1e-300)
+
+
+def test_gated_rmsnorm_gate_limits():
+    rng = np.random.default_rng(32)
+    o = rng.standard_normal((3, 16))
+    w = rng.uniform(0.5, 1.5, 16)
+    # a strongly negative gate shuts the output, zero gate gives exactly zero
+    assert np.abs(oracle.gated_rmsnorm(o, np.full_like(o, -60.0), w, 1e-6)).max() < 1e-20
+    assert np.all(oracle.gated_rmsnorm(o, np.zeros_like(o), w, 1e-6) == 0.0)
+    # a strongly positive gate passes x * 1: y = w o / rms(o) * z
+    z = np.full_like(o, 40.0)
+    y = oracle.gated_rmsnorm(o, z, w, 0.0)
+    rms = np.sqrt(np.mean(o ** 2, axis=-1, keepdims=True))
+    assert rel_err(y, w * o / rms * 40.0) < 1e-15
+
+
+def test_gated_norm_of_the_output_is_invariant_to_the_pages_q_rescale():
+    # The Qwen3.5-9B-npu page rescales q by 1024 inside the recurrence and the
+    # norm's eps by 1024^2 and calls it the same math: O is linear in q, so
+    # mean(O^2) scales by 1024^2 and the norm's output does not change.
+    rng = np.random.default_rng(33)
+    q, k, v, g, beta, S0 = rand_case(rng, 1, 40, 2, 128, 128)
+    z = rng.standard_normal((1, 40, 2, 128))
+    w = rng.uniform(0.5, 1.5, 128)
+    eps = 1e-3
+    O, _ = oracle.prefill(q, k, v, g, beta, S0)
+    O2, _ = oracle.prefill(1024.0 * q, k, v, g, beta, S0)
+    y = oracle.gated_rmsnorm(O, z, w, eps)
+    assert rel_err(oracle.gated_rmsnorm(O2, z, w, eps * 1024.0 ** 2), y) < 1e-12
+    # ... and eps matters here, so the check above is not vacuous
+    assert rel_err(oracle.gated_rmsnorm(O2, z, w, eps), y) > 1e-4
+
+
+def test_gated_rmsnorm_rejects_bad_arguments():
+    with pytest.raises(ValueError):
+        oracle.gated_rmsnorm(np.ones((2, 4)), np.ones((2, 3)), np.ones(4), 1e-6)
+    with pytest.raises(ValueError):
+        oracle.gated_rmsnorm(np.ones((2, 4)), np.ones((2, 4)), np.ones(4), -1.0)
