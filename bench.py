@@ -148,25 +148,33 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold):
     return dict(units=units, wall_s=wall, gpu_ms=gpu_ms, eager_s=eager, workload=w)
 
 
-def bench_prefill(torch, gdn, w, iters, warmup):
+def bench_prefill(torch, gdn, w, iters, warmup, gate=None):
+    """The prompt form over workload w; with gate = (z, norm_w, eps) the form
+    with the gated RMS norm on the output (gdn_chunk_prefill_gated)."""
     O = torch.empty_like(w.v)
     N = w.q.shape[0] if w.cu_seqlens is None else w.cu_seqlens.numel() - 1
     S_T = torch.empty((N, w.q.shape[2], DK, DV), dtype=torch.float32, device="cuda")
+
+    def call():
+        if gate is None:
+            gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
+                                  O=O, S_T=S_T)
+        else:
+            gdn.gdn_chunk_prefill_gated(w.q, w.k, w.v, w.g, w.beta, *gate, w.S0,
+                                        w.cu_seqlens, w.chunk, Y=O, S_T=S_T)
     # Warm up for at least `warmup` calls and about 0.25 s of GPU time, so that
     # the clocks have settled before the timed calls.
     t_end = time.perf_counter() + 0.25
     n = 0
     while n < warmup or time.perf_counter() < t_end:
-        gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
-                              O=O, S_T=S_T)
+        call()
         torch.cuda.synchronize()
         n += 1
     times = []
     for _ in range(iters):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
-                              O=O, S_T=S_T)
+        call()
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) / 1e3)
@@ -180,8 +188,10 @@ def bench_prefill(torch, gdn, w, iters, warmup):
     esz = w.q.element_size()
     flops = prefill_flops(lengths, H, w.chunk)
     nbytes = prefill_bytes(tokens, H, len(lengths), w.S0 is not None, esz)
+    if gate is not None:
+        nbytes += tokens * H * DV * esz          # the gate rows z
     return {
-        "workload": w.name, "tokens": tokens, "heads": H, "chunk": w.chunk,
+        "workload": w.name + ("_gated_norm" if gate is not None else ""), "tokens": tokens, "heads": H, "chunk": w.chunk,
         "seconds": t, "tokens_per_s": tokens / t,
         "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
         "alg_flops": flops, "alg_bytes": nbytes,
@@ -369,6 +379,12 @@ def main():
                     "prefill_large", source_digest("gdn_prefill_mfma.hip"))
                 if not args.no_cpu_baseline:
                     r["cpu_baseline"] = cpu_baseline_prefill(w)
+                # the same workload with the gated RMS norm fused on the output
+                rg = bench_prefill(torch, gdn, w, args.prefill_iters, 2,
+                                   gate=inputs.norm_gate(w))
+                log(f"prefill {rg['workload']}: {rg['tokens_per_s']:.3e} tok/s, "
+                    f"{rg['seconds']*1e3:.3f} ms, HBM {100*rg['hbm_frac']:.1f}%")
+                pre[rg["workload"]] = rg
             del w
             torch.cuda.empty_cache()
         w = inputs.verify_blocks(device="cuda")

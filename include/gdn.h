@@ -110,6 +110,39 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
                       void *O, float *S_T, void *stream);
 
 /*
+ * gdn_chunk_prefill_gated -- gdn_chunk_prefill with the gated RMS norm that
+ * follows the recurrence in a Gated DeltaNet block (Qwen3.5-4B -- Hexagon NPU
+ * (QHexRT) -- v81 page, the opening description of the text decoder: a short
+ * causal-conv FIFO, an SSM state and a gated RMSNorm) applied to each output
+ * row before it is rounded and stored:
+ *
+ *     y = norm_w * o / sqrt(mean(o^2) + eps) * silu(z),  silu(x) = x / (1 + exp(-x))
+ *
+ * with the mean over the 128 values of one token row of one head.  The norm is
+ * scale-invariant up to eps (the Qwen3.5-9B-npu model page, "How it works" ->
+ * "fp16 precision of the DeltaNet output", scales q by 1024 and eps by 1024^2
+ * for exactly that reason), so it takes the fp32 O before any rounding.
+ *
+ *   q, k, v, g, beta, S0, cu_seqlens, B_or_N, T, H, dk, dv, chunk, S_T: as for
+ *               gdn_chunk_prefill.
+ *   z           [B, T, H, 128] io_dtype, 16-byte aligned; NULL only when the call
+ *               has no token rows.
+ *   norm_w      [128] fp32, one weight vector shared by all heads, 4-byte aligned.
+ *   eps         finite and >= 0 (else GDN_ERR_INVALID_ARG); with eps = 0 an
+ *               all-zero output row gives NaN.
+ *   Y           same shape and dtype as v: the normed rows (O itself is not
+ *               written anywhere).
+ *   Y must not overlap any input, z, norm_w or S_T; S_T must not overlap z or
+ *   norm_w (GDN_ERR_ALIAS), besides the rules of gdn_chunk_prefill.
+ */
+int gdn_chunk_prefill_gated(const void *q, const void *k, const void *v, int io_dtype,
+                            const float *g, const float *beta, const float *S0,
+                            const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                            int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                            const void *z, const float *norm_w, float eps, void *Y,
+                            float *S_T, void *stream);
+
+/*
  * gdn_prefill_states -- the prompt form that also keeps the state after every
  * token.  The Qwen3.5-9B-npu model page (section "New in v2", the prompt
  * lookup decoding item) checks a block of drafted tokens in one pass and,

@@ -20,8 +20,8 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_prefill_states",
-            "gdn_decode_step")
+EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_gated",
+            "gdn_prefill_states", "gdn_decode_step")
 
 _lib = None
 
@@ -52,6 +52,10 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_prefill.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                       i64, i64, i64, i64, vp, vp, vp]
     lib.gdn_chunk_prefill.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_gated.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64,
+                                            i64, i64, i64, i64, i64, vp, vp, ctypes.c_float,
+                                            vp, vp, vp]
+    lib.gdn_chunk_prefill_gated.restype = ctypes.c_int
     lib.gdn_prefill_states.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                        i64, i64, i64, vp, vp, vp]
     lib.gdn_prefill_states.restype = ctypes.c_int
@@ -137,6 +141,46 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
         _stream(stream))
     _check(st)
     return O, S_T
+
+
+def gdn_chunk_prefill_gated(q, k, v, g, beta, z, norm_w, eps, S0=None, cu_seqlens=None,
+                            chunk=64, *, Y=None, S_T=None, stream=None):
+    """The prompt form with the gated RMS norm applied to each output row.
+
+    Inputs as for gdn_chunk_prefill, plus z: [B, T, H, 128] with q's dtype (the
+    gate), norm_w: [128] fp32 and eps >= 0.  Returns (Y, S_T) with
+    Y = norm_w * O / sqrt(mean(O^2) + eps) * silu(z) per token row and head.
+    """
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed batches (cu_seqlens) need B == 1")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype \
+            or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape [B, T, H, d] and dtype")
+    if g.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("g and beta must be [B, T, H]")
+    if z.shape != v.shape or z.dtype != q.dtype:
+        raise ValueError("z must match v's shape and q's dtype")
+    if norm_w.shape != (dv,):
+        raise ValueError("norm_w must be [dv]")
+    if Y is None:
+        Y = torch.empty_like(v)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if Y.dtype != q.dtype or Y.shape != v.shape:
+        raise ValueError("Y must match v's shape and dtype")
+    if S_T.shape != (N, H, dk, dv) or (S0 is not None and S0.shape != (N, H, dk, dv)):
+        raise ValueError("S0 / S_T must be [N, H, dk, dv]")
+    st = load_library().gdn_chunk_prefill_gated(
+        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+        _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+        N, T, H, dk, dv, int(chunk), _ptr(z, name="z"), _ptr(norm_w, torch.float32, "norm_w"),
+        float(eps), _ptr(Y, name="Y"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
+    _check(st)
+    return Y, S_T
 
 
 def gdn_prefill_states(q, k, v, g, beta, S0=None, cu_seqlens=None, *, O=None, S_tok=None,

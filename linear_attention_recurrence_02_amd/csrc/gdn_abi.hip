@@ -4,6 +4,7 @@
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
+#include <cfloat>
 #include <cstdint>
 
 namespace {
@@ -45,11 +46,16 @@ const char *gdn_status_string(int status) {
     }
 }
 
-int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
-                      const float *g, const float *beta, const float *S0,
-                      const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
-                      int64_t H, int64_t dk, int64_t dv, int64_t chunk, void *O,
-                      float *S_T, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the prompt-form calls: fills `a` (and the byte spans
+// of the token buffers for further alias checks) or returns a status.
+int check_prefill(const void *q, const void *k, const void *v, int io_dtype, const float *g,
+                  const float *beta, const float *S0, const int32_t *cu_seqlens,
+                  int64_t B_or_N, int64_t T, int64_t H, int64_t dk, int64_t dv,
+                  int64_t chunk, void *O, float *S_T, gdn::PrefillArgs &a, int64_t &tok_bytes) {
     if (!dims_ok(B_or_N) || !dims_ok(T) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
     const int64_t N = B_or_N;
     const int64_t rows = cu_seqlens ? T : N * T;        // token rows of H heads
@@ -68,7 +74,7 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
     if (N * H >= kMaxDim) return GDN_ERR_INVALID_ARG;     // one workgroup per unit
     if (rows > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return GDN_ERR_INVALID_ARG;
     const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
-    const int64_t tok_bytes = rows * H * gdn::kHeadDim * esz;
+    tok_bytes = rows * H * gdn::kHeadDim * esz;
     const int64_t gb_bytes = rows * H * 4;
     const int64_t st_bytes = N * H * gdn::kHeadDim * gdn::kHeadDim * 4;
 
@@ -83,13 +89,61 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
         if (overlap(rST, r)) return GDN_ERR_ALIAS;
     if (S0 && overlap(rST, rS0) && rST.lo != rS0.lo) return GDN_ERR_ALIAS;
 
-    gdn::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, N, T, H,
-                       static_cast<int>(chunk), io_dtype == GDN_BF16, O, S_T};
-    if (N == 0) return GDN_OK;   // nothing to do
+    a = gdn::PrefillArgs{q, k, v, g, beta, S0, cu_seqlens, N, T, H,
+                         static_cast<int>(chunk), io_dtype == GDN_BF16, O, S_T};
+    return GDN_OK;
+}
+
+int launch_prefill(const gdn::PrefillArgs &a, void *stream) {
+    if (a.N == 0) return GDN_OK;   // nothing to do
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = gdn::prefill_mfma_supports(a) ? gdn::launch_prefill_mfma(a, s)
                                                  : gdn::launch_prefill_valu(a, s);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
+                      const float *g, const float *beta, const float *S0,
+                      const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                      int64_t H, int64_t dk, int64_t dv, int64_t chunk, void *O,
+                      float *S_T, void *stream) {
+    gdn::PrefillArgs a{};
+    int64_t tok_bytes = 0;
+    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
+                                 dv, chunk, O, S_T, a, tok_bytes);
+    return st != GDN_OK ? st : launch_prefill(a, stream);
+}
+
+int gdn_chunk_prefill_gated(const void *q, const void *k, const void *v, int io_dtype,
+                            const float *g, const float *beta, const float *S0,
+                            const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                            int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                            const void *z, const float *norm_w, float eps, void *Y,
+                            float *S_T, void *stream) {
+    gdn::PrefillArgs a{};
+    int64_t tok_bytes = 0;
+    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
+                                 dv, chunk, Y, S_T, a, tok_bytes);
+    if (st != GDN_OK) return st;
+    if (!norm_w || !aligned(norm_w, 4)) return GDN_ERR_INVALID_ARG;
+    if (tok_bytes > 0 && !z) return GDN_ERR_INVALID_ARG;
+    if (!aligned(z, 16)) return GDN_ERR_INVALID_ARG;
+    if (!(eps >= 0.f && eps <= FLT_MAX)) return GDN_ERR_INVALID_ARG;   // finite, >= 0
+    const Range rz = span_of(z, tok_bytes), rw = span_of(norm_w, gdn::kHeadDim * 4),
+                rY = span_of(Y, tok_bytes),
+                rST = span_of(S_T, a.N * H * gdn::kHeadDim * gdn::kHeadDim * 4);
+    for (Range r : {rz, rw})
+        if (overlap(rY, r) || overlap(rST, r)) return GDN_ERR_ALIAS;
+    // z is NULL only in a call without token rows, where the plain form does
+    // the same work (S_T = S0)
+    a.z = z;
+    a.norm_w = norm_w;
+    a.eps = eps;
+    return launch_prefill(a, stream);
 }
 
 int gdn_prefill_states(const void *q, const void *k, const void *v, int io_dtype,

@@ -24,6 +24,11 @@ struct PrefillArgs {
     bool bf16;                  // io dtype of q/k/v/O
     void *O;
     float *S_T;
+    // Gated RMS norm on the output rows (null z: plain O).  O then receives
+    // y = norm_w * O / sqrt(mean(O^2) + eps) * silu(z), z with the io dtype.
+    const void *z = nullptr;
+    const float *norm_w = nullptr;
+    float eps = 0.f;
 };
 
 struct DecodeArgs {

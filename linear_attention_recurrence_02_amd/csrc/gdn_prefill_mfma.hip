@@ -101,15 +101,37 @@ struct __attribute__((aligned(16))) Smem {
     float EG[2][C];               // exp(G_t)
     float EC[2][C];               // exp(G_last - G_t)
     float Bt[2][C];               // beta
+    float NP[C][4];               // gated norm: per-wave partial sums of O^2 by token row
+    float NW[D];                  // gated norm: weights
+    uint32_t NPC;                 // gated norm: partial-sum sets posted by consumer waves
 };
 
 // Column swizzles: K and V flip column bit 3 with row bit 2; W flips column
 // bits 2..3 with row bits 2..3.
 __device__ __forceinline__ int ksw(int row) { return ((row >> 2) & 1) << 3; }
 __device__ __forceinline__ int wsw(int row) { return ((row >> 2) & 3) << 2; }
+__device__ __forceinline__ int zsw(int row) { return (row >> 1) & 3; }
 
 // index of the off-diagonal block (i, j), i > j, in Smem::M
 __device__ __forceinline__ constexpr int oblk(int i, int j) { return i * (i - 1) / 2 + j; }
+
+// Workgroup barrier for the consumer loop.  __syncthreads() is also a release
+// fence, and a release waits for every direct-to-LDS load still in flight; the
+// gated output keeps such loads (each wave's own gate rows, read only by that
+// wave) in flight across barriers, so its loop uses a barrier that waits only
+// for this wave's LDS operations and keeps the compiler from moving memory
+// accesses across it.
+template <bool kLdsOnly>
+__device__ __forceinline__ void phase_barrier() {
+    if constexpr (kLdsOnly) {
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+    } else {
+        __syncthreads();
+    }
+}
 
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -528,12 +550,19 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q,
     }
 }
 
+template <bool kGated>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t T,
-    int64_t H, bf16 *__restrict__ O, float *__restrict__ S_T) {
+    int64_t H, bf16 *__restrict__ O, float *__restrict__ S_T, const bf16 *__restrict__ z,
+    const float *__restrict__ norm_w, float eps) {
     __shared__ Smem sm;
+    // Gated norm: consumer wave w's gate columns 32w..32w+31, token-major; the
+    // 16-byte slot j of row t at j ^ zsw(t).  A variable of its own, so that
+    // the compiler can tell the direct-to-LDS loads into it from the reads of
+    // the other arrays and does not wait for them before those reads.
+    __shared__ bf16 Zs[4][kGated ? C * 32 : 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, l = tid & 63, r16 = l & 15, qd = l >> 4;
@@ -619,6 +648,8 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     STu[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16] = S[i][c][e];
         return;
     }
+    if (kGated && tid < D) sm.NW[tid] = norm_w[tid];
+    if (kGated && tid == 0) sm.NPC = 0;
     __syncthreads();
     // the period in which the producers prepare chunk 0; its phase 3 is the
     // W/U step of chunk 0
@@ -629,6 +660,24 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     __syncthreads();
 
     const uint32_t HD = static_cast<uint32_t>(H) * D;
+    // Gated norm: the gate rows of chunk cz straight into LDS (no registers):
+    // wave w fetches its 32 columns of the 64 rows, 16 rows per instruction,
+    // lane i's 16 bytes landing at slot i of the instruction's 1 KiB.  Rows
+    // past the sequence repeat the chunk's row 0 and are never used.
+    auto fetch_gate = [&](int cz) {
+        const bf16 *zc = z + (u.row0(cz) * H + u.h) * D + 32 * w;
+        const int nz = u.rows_in(cz);
+        const int lr = opaque(l);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int t = 16 * i + (lr >> 2);
+            const uint32_t off = static_cast<uint32_t>(t < nz ? t : 0) * HD + 8 * ((lr & 3) ^ zsw(t));
+            __builtin_amdgcn_global_load_lds(zc + off,
+                                             (__attribute__((address_space(3))) void *)&Zs[w][16 * 32 * i],
+                                             16, 0, 0);
+        }
+    };
+    if constexpr (kGated) fetch_gate(0);
     const int trw = (4 * qd + (r16 >> 2)) * WS + ((4 * (r16 & 3)) ^ wsw(4 * qd));
     const int trk = (4 * qd + (r16 >> 2)) * KS + ((4 * (r16 & 3)) ^ ksw(4 * qd));
     for (int c = 0; c < nch; ++c) {
@@ -636,9 +685,6 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         const int cnv = u.rows_in(c);
 
         // ======== phase 1: D = U - W S; S <- exp(G_C) S + K^T diag(exp(G_C - G)) D ========
-        // Operands are read one batch ahead of the products that use them; the
-        // scheduling barrier keeps each batch's reads above the previous batch's
-        // products so that their LDS latency overlaps matrix-core work.
         f16x8 Sh[4][2], Dh[2][2];
         {
             const f16 *Wc = sm.W + trw;
@@ -714,15 +760,20 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                             S[2 * ib + ii][cc] = mfma(ka[ib & 1][2 * ii + s2], Dp[s2][cc], S[2 * ib + ii][cc]);
             }
         }
-        __syncthreads();
+        phase_barrier<kGated>();
 
         // ======== phase 2: O = diag(exp G) Q S + A D (S as it entered the chunk) ========
         // Computed transposed, O^T = S^T Q^T diag(exp G) + D^T A^T: the fp16
         // tiles of S and D serve as A operands as they are, a lane's column is
         // one token (one decay factor), and each lane ends up with four
         // consecutive columns of one token row (one 8-byte store).
+        // With the gated norm, the gate rows z are loaded before the products,
+        // O is multiplied by w silu(z) after them, and each wave leaves its
+        // partial sums of O^2 per token row in LDS; the rows are scaled by
+        // 1/sqrt(mean(O^2) + eps) and stored after the barrier.
+        bf16 *obase = O + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
+        f32x4 Ot[4][2];           // Ot[m][cc]: O[16m + r16][32w + 16cc + 4q + e]
         {
-            f32x4 Ot[4][2];       // Ot[m][cc]: O[16m + r16][32w + 16cc + 4q + e]
 #pragma unroll
             for (int m = 0; m < 4; ++m) Ot[m][0] = Ot[m][1] = zero4();
             const f16 *Qc = sm.Q[cur] + r16 * QS + 4 * qd;
@@ -772,22 +823,96 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                         ++n;
                     }
             }
-            bf16 *obase = O + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
+            if constexpr (kGated) {
+                const f32x4 nw0 = *reinterpret_cast<const f32x4 *>(&sm.NW[32 * w + 4 * qd]);
+                const f32x4 nw1 = *reinterpret_cast<const f32x4 *>(&sm.NW[32 * w + 16 + 4 * qd]);
+                // this wave's gate rows, fetched into LDS a period ago
+                __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0)
+                bf16x4 zr[4][2];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const int t = 16 * m + r16;
-                if (t < cnv) {
-                    const uint32_t off = static_cast<uint32_t>(t) * HD;
+                for (int m = 0; m < 4; ++m) {
+                    const int t = 16 * m + r16;
 #pragma unroll
                     for (int cc = 0; cc < 2; ++cc)
-                        *reinterpret_cast<bf16x4 *>(obase + off + 16 * cc) = __builtin_convertvector(Ot[m][cc], bf16x4);
+                        zr[m][cc] = *reinterpret_cast<const bf16x4 *>(
+                            &Zs[w][t * 32 + 8 * ((2 * cc + (qd >> 1)) ^ zsw(t)) + 4 * (qd & 1)]);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    float ss = 0.f;
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) ss += Ot[m][cc][e] * Ot[m][cc][e];
+                    // lanes r16 + 16 q of the four lane groups hold one row
+                    ss += __shfl_xor(ss, 16);
+                    ss += __shfl_xor(ss, 32);
+                    if (qd == 0) sm.NP[16 * m + r16][w] = ss;
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        const f32x4 zf = __builtin_convertvector(zr[m][cc], f32x4);
+                        const f32x4 nw = cc ? nw1 : nw0;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-zf[e]));
+                            Ot[m][cc][e] *= nw[e] * (zf[e] * sg);
+                        }
+                    }
+                }
+                // The four consumer waves meet on an LDS counter (the producers
+                // are still solving): each posts its partial sums, then waits
+                // until all four sets of this chunk are there.  Rows are then
+                // normed and stored here, in the part of the period where the
+                // CU has no other memory traffic.  Every consumer wave posts
+                // once per chunk and no wave can run a chunk ahead (the phase
+                // barriers), so the count reaches 4 (c + 1); the spin is
+                // bounded all the same.
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): partials landed
+                if (l == 0) __hip_atomic_fetch_add(&sm.NPC, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const uint32_t target = 4u * static_cast<uint32_t>(c + 1);
+                for (int spin = 0; spin < (1 << 22); ++spin) {
+                    const uint32_t seen = __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(&sm.NPC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+                    if (seen >= target) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                asm volatile("" ::: "memory");
+                const int rr = opaque(r16);
+                const float *np = &sm.NP[rr][0];
+                bf16 *orow = obase + static_cast<uint32_t>(rr) * HD;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const f32x4 ps = *reinterpret_cast<const f32x4 *>(np + 64 * m);
+                    const float ms = (ps[0] + ps[1] + ps[2] + ps[3]) * (1.f / D);
+                    const float rs = __builtin_amdgcn_rsqf(ms + eps);
+                    if (rr < cnv - 16 * m) {
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc)
+                            *reinterpret_cast<bf16x4 *>(orow + 16 * m * HD + 16 * cc) =
+                                __builtin_convertvector(Ot[m][cc] * rs, bf16x4);
+                    }
+                }
+                // this wave's reads of its gate slice are done: refill it with
+                // the next chunk's rows, a period ahead of their use
+                if (c + 1 < nch) fetch_gate(c + 1);
+            } else {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int t = 16 * m + r16;
+                    if (t < cnv) {
+                        const uint32_t off = static_cast<uint32_t>(t) * HD;
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc)
+                            *reinterpret_cast<bf16x4 *>(obase + off + 16 * cc) = __builtin_convertvector(Ot[m][cc], bf16x4);
+                    }
                 }
             }
         }
-        __syncthreads();
+        phase_barrier<kGated>();
         // ======== phase 3: W and U of the next chunk ========
         if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, r16, qd, Ur);
-        __syncthreads();
+        phase_barrier<kGated>();
     }
 
 #pragma unroll
@@ -805,10 +930,11 @@ bool prefill_mfma_supports(const PrefillArgs &a) { return a.bf16 && a.chunk == C
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(512);
-    prefill_mfma_kernel<<<grid, block, 0, stream>>>(
+    auto kern = a.z ? prefill_mfma_kernel<true> : prefill_mfma_kernel<false>;
+    kern<<<grid, block, 0, stream>>>(
         static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
         static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
-        static_cast<bf16 *>(a.O), a.S_T);
+        static_cast<bf16 *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps);
     return hipGetLastError();
 }
 

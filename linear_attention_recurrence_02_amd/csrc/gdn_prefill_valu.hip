@@ -20,6 +20,12 @@
 // The chunk's K and Q (fp32, rows padded to 129 words so that the Gram phase's
 // row-strided reads hit distinct LDS banks), D, N and the masked decayed
 // QK^T live in LDS.
+//
+// With the gated RMS norm on the output (the norm a Gated DeltaNet block
+// applies after the recurrence), each output row is reduced across the
+// workgroup as it is produced (one barrier per row, partial sums
+// double-buffered by row parity) and stored as
+// w_j o_j / sqrt(mean(o^2) + eps) silu(z_j).
 
 #include "gdn_internal.hpp"
 
@@ -29,17 +35,19 @@ namespace {
 constexpr int kThreads = 128;
 constexpr int kRow = kHeadDim + 1;   // padded LDS row stride for K and Q
 
-template <typename IO, int C>
+template <typename IO, int C, bool kGated>
 __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t T,
-    int64_t H, IO *__restrict__ O, float *__restrict__ S_T) {
+    int64_t H, IO *__restrict__ O, float *__restrict__ S_T, const IO *__restrict__ z,
+    const float *__restrict__ norm_w, float eps) {
     __shared__ float sK[C * kRow], sQ[C * kRow];
     __shared__ float sD[C * kHeadDim];
     __shared__ float sN[C * C], sA[C * C];
     __shared__ double sG[C];
     __shared__ float sg[C], sB[C], sEG[C], sEC[C];
+    __shared__ float sRed[2][kThreads / 64];
 
     const int64_t unit = blockIdx.x;
     const int64_t n = unit / H, h = unit % H;
@@ -47,6 +55,7 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     int64_t start, len;
     sequence_span(cu_seqlens, n, T, start, len);
 
+    const float nw = kGated ? norm_w[j] : 0.f;
     float S[kHeadDim];
     const float *S0u = S0 ? S0 + unit * (kHeadDim * kHeadDim) : nullptr;
 #pragma unroll
@@ -121,7 +130,22 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
             sD[t * kHeadDim + j] = r;
             float o = sEG[t] * qs;
             for (int s = 0; s <= t; ++s) o += sA[t * C + s] * sD[s * kHeadDim + j];
-            if (t < nv) O[((row0 + t) * H + h) * kHeadDim + j] = from_f32<IO>(o);
+            const int64_t oi = ((row0 + t) * H + h) * kHeadDim + j;
+            if constexpr (kGated) {
+                float ss = o * o;
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+                if ((j & 63) == 0) sRed[t & 1][j >> 6] = ss;
+                __syncthreads();
+                const float ms = (sRed[t & 1][0] + sRed[t & 1][1]) * (1.f / kHeadDim);
+                if (t < nv) {
+                    const float zf = to_f32(z[oi]);
+                    const float silu = zf / (1.f + expf(-zf));
+                    O[oi] = from_f32<IO>(nw * (o / sqrtf(ms + eps)) * silu);
+                }
+            } else {
+                if (t < nv) O[oi] = from_f32<IO>(o);
+            }
         }
 
         // Carry the state to the end of the chunk.
@@ -145,10 +169,11 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
 template <typename IO, int C>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(kThreads);
-    prefill_valu_kernel<IO, C><<<grid, block, 0, stream>>>(
+    auto kern = a.z ? prefill_valu_kernel<IO, C, true> : prefill_valu_kernel<IO, C, false>;
+    kern<<<grid, block, 0, stream>>>(
         static_cast<const IO *>(a.q), static_cast<const IO *>(a.k),
         static_cast<const IO *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
-        static_cast<IO *>(a.O), a.S_T);
+        static_cast<IO *>(a.O), a.S_T, static_cast<const IO *>(a.z), a.norm_w, a.eps);
     return hipGetLastError();
 }
 

@@ -163,3 +163,15 @@ def varlen_prefill(seed=0, device="cpu"):
 def verify_blocks(seed=0, device="cpu"):
     """256 sequences x 16-token verify blocks, H=16, from snapshotted states."""
     return verify_workload(256, 16, 16, seed=seed, device=device)
+
+
+def norm_gate(w: Workload, seed: int = 0, eps: float = 1e-6):
+    """Inputs of the gated RMS norm on the output of workload ``w``: the gate z
+    ~ N(0, 1) with v's shape and io dtype, and weights ~ U(0.5, 1.5) fp32 [dv],
+    both from a generator on v's device seeded with ``seed + 7919`` (so that they
+    do not repeat the workload's own draws); eps as given (1e-6 by default, the
+    usual RMS-norm epsilon).  Returns (z, norm_w, eps)."""
+    gen = _generator(seed + 7919, w.v.device)
+    z = torch.randn(*w.v.shape, generator=gen, device=w.v.device).to(w.v.dtype)
+    norm_w = 0.5 + torch.rand(w.v.shape[-1], generator=gen, device=w.v.device)
+    return z, norm_w, eps

@@ -111,6 +111,36 @@ def test_prefill_states_validation(lib):
     assert states(lib, N=0, S_tok=None, q=None, k=None, v=None, O=None) == binding.GDN_OK
 
 
+def gated(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB,
+          beta=A + 200 * MB, S0=A + 256 * MB, cu=None, N=2, T=64, H=2, dk=128,
+          dv=128, chunk=64, z=A + 1024 * MB, w=A + 1100 * MB, eps=1e-6, Y=A + 512 * MB,
+          S_T=A + 768 * MB):
+    return lib.gdn_chunk_prefill_gated(q, k, v, dtype, g, beta, S0, cu, N, T, H, dk, dv,
+                                       chunk, z, w, eps, Y, S_T, None)
+
+
+def test_prefill_gated_validation(lib):
+    # the prompt form's own rules still hold
+    assert gated(lib, q=None) == binding.GDN_ERR_INVALID_ARG
+    assert gated(lib, chunk=48) == binding.GDN_ERR_UNSUPPORTED
+    assert gated(lib, Y=A) == binding.GDN_ERR_ALIAS                     # Y over q
+    # the gate, the weights and eps
+    assert gated(lib, z=None) == binding.GDN_ERR_INVALID_ARG
+    assert gated(lib, w=None) == binding.GDN_ERR_INVALID_ARG
+    assert gated(lib, z=A + 1024 * MB + 8) == binding.GDN_ERR_INVALID_ARG
+    assert gated(lib, w=A + 1100 * MB + 2) == binding.GDN_ERR_INVALID_ARG
+    assert gated(lib, eps=-1e-6) == binding.GDN_ERR_INVALID_ARG
+    assert gated(lib, eps=float("nan")) == binding.GDN_ERR_INVALID_ARG
+    assert gated(lib, eps=float("inf")) == binding.GDN_ERR_INVALID_ARG
+    # Y holds 2 x 64 rows x 2 heads x 256 B = 64 KiB
+    assert gated(lib, z=A + 512 * MB + 1024) == binding.GDN_ERR_ALIAS    # z under Y
+    assert gated(lib, w=A + 512 * MB + 64) == binding.GDN_ERR_ALIAS     # w under Y
+    assert gated(lib, w=A + 768 * MB + 64) == binding.GDN_ERR_ALIAS     # w under S_T
+    assert gated(lib, N=0) == binding.GDN_OK
+    assert gated(lib, T=0, z=None, q=None, k=None, v=None, g=None, beta=None,
+                 Y=None, N=0) == binding.GDN_OK
+
+
 def test_decode_rejects_bad_calls(lib):
     assert decode(lib, S=None) == binding.GDN_ERR_INVALID_ARG
     assert decode(lib, B=-1) == binding.GDN_ERR_INVALID_ARG

@@ -1,0 +1,123 @@
+"""GPU parity of gdn_chunk_prefill_gated (the prompt form with the gated RMS
+norm on each output row) against the fp64 oracle: the oracle's O through the
+oracle's gated norm, on the same seeded inputs, through the C ABI.
+
+The norm is taken per (token, head) row, so Y is compared row by row: an
+element may differ from the reference by tol * max|r| over its row plus half a
+unit in the last place of the output dtype (bf16 outputs).  The norm divides
+by the row's RMS, so a row's error is O's error relative to that row; see the
+tolerance constants below.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_02_amd import inputs
+from linear_attention_recurrence_02_amd.binding import gdn_chunk_prefill, gdn_chunk_prefill_gated
+from metrics import TOL_BF16, TOL_F32, bf16_half_ulp, f64, spans_of, worst_slice_error
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def row_error(Y, Yr, bf16):
+    """Worst over rows of max|y - r| / max|r| (bf16: with half an ulp of the
+    output allowed elementwise), over every (token, head) row of [.., 128]."""
+    y, r = f64(Y).reshape(-1, 128), f64(Yr).reshape(-1, 128)
+    den = np.abs(r).max(axis=1, keepdims=True)
+    den = np.where(den > 0, den, 1.0)
+    diff = np.abs(y - r)
+    if bf16:
+        diff = np.maximum(diff - bf16_half_ulp(np.maximum(np.abs(y), np.abs(r))), 0.0)
+    e = (diff / den).max(axis=1)
+    return float(e.max()) if e.size else 0.0
+
+
+def run(w, z, nw, eps, q=None):
+    Y, S_T = gdn_chunk_prefill_gated(w.q if q is None else q, w.k, w.v, w.g, w.beta, z, nw, eps,
+                                     w.S0, w.cu_seqlens, w.chunk)
+    torch.cuda.synchronize()
+    return Y, S_T
+
+
+def check(w, Y, S_T, z, nw, eps, label, spans=None):
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, cu_seqlens=w.cu_seqlens)
+    Yr = oracle.gated_rmsnorm(Or, z, nw, eps)
+    bf16 = w.q.dtype == torch.bfloat16
+    ey = row_error(Y, Yr, bf16)
+    es = worst_slice_error(S_T, Sr)
+    say(f"[{label}] worst row error Y={ey:.3e}  S_T={es:.3e}")
+    tol = TOL_BF16 if bf16 else TOL_F32
+    assert ey <= tol and es <= tol, (ey, es)
+
+
+def test_gated_bf16_chunk64_ragged_tail():
+    # matrix-core kernel: 4 full chunks and a 44-token tail, nonzero S0
+    w = inputs.prefill_workload(2, 300, 3, chunk=64, seed=21, device=DEV)
+    z, nw, eps = inputs.norm_gate(w, seed=21)
+    Y, S_T = run(w, z, nw, eps)
+    check(w, Y, S_T, z, nw, eps, "bf16 c64")
+    # the state is the plain prompt form's, bit for bit
+    _, S_plain = gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, None, 64)
+    torch.cuda.synchronize()
+    assert torch.equal(S_T, S_plain)
+
+
+def test_gated_bf16_packed_with_empty_and_short_sequences():
+    w = inputs.varlen_workload([0, 5, 64, 130, 1], H=2, seed=22, device=DEV)
+    z, nw, eps = inputs.norm_gate(w, seed=22)
+    Y, S_T = run(w, z, nw, eps)
+    check(w, Y, S_T, z, nw, eps, "bf16 packed")
+
+
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_gated_bf16_vector_kernel(chunk):
+    w = inputs.prefill_workload(1, 100, 2, chunk=chunk, seed=23, device=DEV)
+    z, nw, eps = inputs.norm_gate(w, seed=23)
+    Y, S_T = run(w, z, nw, eps)
+    check(w, Y, S_T, z, nw, eps, f"bf16 c{chunk}")
+
+
+def test_gated_fp32_tiny_workload():
+    w = inputs.tiny_prefill(device=DEV)
+    z, nw, eps = inputs.norm_gate(w, seed=0)
+    Y, S_T = run(w, z, nw, eps)
+    check(w, Y, S_T, z, nw, eps, "fp32 tiny")
+
+
+def test_gated_eps_dominates():
+    # eps far above mean(O^2): the norm no longer rescales, y ~ w o silu(z) / sqrt(eps)
+    w = inputs.prefill_workload(1, 130, 2, chunk=64, seed=24, device=DEV)
+    z, nw, _ = inputs.norm_gate(w, seed=24)
+    Y, S_T = run(w, z, nw, 100.0)
+    check(w, Y, S_T, z, nw, 100.0, "eps=100")
+
+
+def test_gated_is_invariant_to_the_q_rescale():
+    # q x 1024 with eps x 1024^2 (exact in bf16) gives the normed output of q, eps
+    w = inputs.prefill_workload(1, 200, 2, chunk=64, seed=25, device=DEV)
+    z, nw, eps = inputs.norm_gate(w, seed=25, eps=1e-3)
+    Y, S_T = run(w, z, nw, eps * 1024.0 ** 2, q=w.q * 1024)
+    check(w, Y, S_T, z, nw, eps, "q x 1024")
+
+
+def test_gated_large_workload_sampled_units():
+    # the large prompt workload (8 x 16384 tokens x 32 heads) in one call;
+    # sampled (sequence, head) units in full against the oracle
+    w = inputs.large_prefill(device=DEV)
+    z, nw, eps = inputs.norm_gate(w, seed=0)
+    Y, S_T = run(w, z, nw, eps)
+    assert torch.isfinite(Y.float()).all()
+    for n, h in ((0, 0), (7, 19)):
+        sl = lambda x: x[n:n + 1, :, h:h + 1]
+        Or, Sr = oracle.prefill(sl(w.q), sl(w.k), sl(w.v), sl(w.g), sl(w.beta), None)
+        Yr = oracle.gated_rmsnorm(Or, sl(z), nw, eps)
+        ey = row_error(sl(Y), Yr, True)
+        es = worst_slice_error(S_T[n:n + 1, h:h + 1], Sr)
+        say(f"[large seq {n} head {h}] worst row error Y={ey:.3e}  S_T={es:.3e}")
+        assert ey <= TOL_BF16 and es <= TOL_BF16, (ey, es)
