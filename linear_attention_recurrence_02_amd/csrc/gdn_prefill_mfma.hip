@@ -444,29 +444,23 @@ struct Producer {
 #pragma unroll
             for (int j = 0; j < uu; ++j) y[j] -= rc[r][j >> 2][j & 3] * y[uu];
         }
-        if (q == 0) {
-            f16x8 t0, t1, p0, p1, v0, v1;
+        // Every lane group holds the whole row; group q rounds and stores
+        // columns 4q..4q+3 of it, picked by blending with 0/1 weights (the
+        // compiler turns selects on a lane value into an indexed scratch
+        // array).
+        {
+            const float m0 = q == 0 ? 1.f : 0.f, m1 = q == 1 ? 1.f : 0.f;
+            const float m2 = q == 2 ? 1.f : 0.f, m3 = q == 3 ? 1.f : 0.f;
+            f32x4 y4;
 #pragma unroll
-            for (int v4 = 0; v4 < 4; ++v4) {
-                const f32x4 bt = *reinterpret_cast<const f32x4 *>(&Bt[16 * P + 4 * v4]);
-                const f32x4 eg = *reinterpret_cast<const f32x4 *>(&EG[16 * P + 4 * v4]);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * v4 + e;
-                    const f16 tv = static_cast<f16>(y[j]);
-                    const f16 pv = static_cast<f16>(y[j] * (bt[e] * eg[e]));
-                    const f16 vv = static_cast<f16>(y[j] * bt[e]);
-                    if (j < 8) { t0[j] = tv; p0[j] = pv; v0[j] = vv; }
-                    else { t1[j - 8] = tv; p1[j - 8] = pv; v1[j - 8] = vv; }
-                }
-            }
-            f16 *tr = &sm.Tii[P][r16 * BS], *pr = &sm.P[P][r16 * BS], *vr = &sm.Pv[P][r16 * BS];
-            *reinterpret_cast<f16x8 *>(tr) = t0;
-            *reinterpret_cast<f16x8 *>(tr + 8) = t1;
-            *reinterpret_cast<f16x8 *>(pr) = p0;
-            *reinterpret_cast<f16x8 *>(pr + 8) = p1;
-            *reinterpret_cast<f16x8 *>(vr) = v0;
-            *reinterpret_cast<f16x8 *>(vr + 8) = v1;
+            for (int e = 0; e < 4; ++e)
+                y4[e] = y[e] * m0 + y[4 + e] * m1 + y[8 + e] * m2 + y[12 + e] * m3;
+            const f32x4 bt = *reinterpret_cast<const f32x4 *>(&Bt[16 * P + 4 * q]);
+            const f32x4 eg = *reinterpret_cast<const f32x4 *>(&EG[16 * P + 4 * q]);
+            const int o = r16 * BS + 4 * q;
+            *reinterpret_cast<f16x4 *>(&sm.Tii[P][o]) = h4(y4);
+            *reinterpret_cast<f16x4 *>(&sm.P[P][o]) = h4(y4 * (bt * eg));
+            *reinterpret_cast<f16x4 *>(&sm.Pv[P][o]) = h4(y4 * bt);
         }
         // M_Pj^T = N_Pj^T T_PP^T: A = N_Pj (lane: row j = r16, k = t = 4q..),
         // B[t'][t] = T_PP[t][t'] (lane: column t = r16, k = t' = 4q..).  The
