@@ -61,6 +61,14 @@ typedef enum {
     GDN_BF16 = 1
 } gdn_dtype;
 
+/* How the prompt form's matrix-core kernel forms the 16 x 16 diagonal blocks of
+ * (I + N)^-1 (see gdn_chunk_prefill_ex). */
+typedef enum {
+    GDN_INVERSE_DEFAULT = 0,        /* the library's choice */
+    GDN_INVERSE_SUBSTITUTION = 1,   /* back substitution, fp32, on the vector ALUs */
+    GDN_INVERSE_DOUBLING = 2        /* exact block doubling on the matrix cores */
+} gdn_inverse;
+
 /* Library ABI version (increments on any signature change). */
 int gdn_version(void);
 
@@ -108,6 +116,27 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
                       const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
                       int64_t H, int64_t dk, int64_t dv, int64_t chunk,
                       void *O, float *S_T, void *stream);
+
+/*
+ * gdn_chunk_prefill_ex -- gdn_chunk_prefill with a choice of how (I + N)^-1 is
+ * formed.  The Qwen3.5-9B-npu model page ("How it works" -> "Gated DeltaNet on
+ * the NPU") computes the triangular inverse by exact block doubling,
+ * (D + C)^-1 = D^-1 - D^-1 C D^-1, from 1 x 1 blocks up; gdn_chunk_prefill by
+ * default builds each 16 x 16 diagonal block that way on the matrix cores
+ * (GDN_INVERSE_DOUBLING) and applies the block structure above it by block
+ * forward substitution.  GDN_INVERSE_SUBSTITUTION forms the diagonal blocks by
+ * fp32 back substitution instead.  Both reach the same result up to rounding.
+ * The choice applies to bf16 inputs at chunk 64 (the matrix-core kernel); the
+ * other configurations substitute column by column and ignore it.
+ *
+ *   inverse     a gdn_inverse value (else GDN_ERR_UNSUPPORTED).
+ *   Every other argument: as for gdn_chunk_prefill.
+ */
+int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dtype,
+                         const float *g, const float *beta, const float *S0,
+                         const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
+                         int64_t dk, int64_t dv, int64_t chunk, int inverse, void *O,
+                         float *S_T, void *stream);
 
 /*
  * gdn_chunk_prefill_gated -- gdn_chunk_prefill with the gated RMS norm that

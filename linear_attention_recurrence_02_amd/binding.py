@@ -20,8 +20,9 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
-EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_gated",
-            "gdn_prefill_states", "gdn_decode_step")
+EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_ex",
+            "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_decode_step")
+GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
 
 _lib = None
 
@@ -52,6 +53,9 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_prefill.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                       i64, i64, i64, i64, vp, vp, vp]
     lib.gdn_chunk_prefill.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_ex.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
+                                         i64, i64, i64, i64, ctypes.c_int, vp, vp, vp]
+    lib.gdn_chunk_prefill_ex.restype = ctypes.c_int
     lib.gdn_chunk_prefill_gated.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64,
                                             i64, i64, i64, i64, i64, vp, vp, ctypes.c_float,
                                             vp, vp, vp]
@@ -107,12 +111,14 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
-                      O=None, S_T=None, stream=None):
+                      O=None, S_T=None, stream=None, inverse=None):
     """Chunkwise-parallel prompt form over whole sequences.
 
     q, k, v: [B, T, H, 128] (bf16 or fp32; packed batches B = 1);
     g, beta: [B, T, H] fp32; S0: [N, H, 128, 128] fp32 or None;
     cu_seqlens: int32 [N+1] device offsets or None.
+    inverse: None (gdn_chunk_prefill) or a GDN_INVERSE_* value
+    (gdn_chunk_prefill_ex).
     Returns (O, S_T); O/S_T may be given to write in place (S_T may be S0).
     """
     B, T, H, dk = q.shape
@@ -133,12 +139,15 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
         raise ValueError("O must match v's shape and dtype")
     if S_T.shape != (N, H, dk, dv) or (S0 is not None and S0.shape != (N, H, dk, dv)):
         raise ValueError("S0 / S_T must be [N, H, dk, dv]")
-    st = load_library().gdn_chunk_prefill(
-        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
-        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
-        _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
-        N, T, H, dk, dv, int(chunk), _ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"),
-        _stream(stream))
+    args = (_ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+            _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+            _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+            N, T, H, dk, dv, int(chunk))
+    out = (_ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
+    if inverse is None:
+        st = load_library().gdn_chunk_prefill(*args, *out)
+    else:
+        st = load_library().gdn_chunk_prefill_ex(*args, int(inverse), *out)
     _check(st)
     return O, S_T
 

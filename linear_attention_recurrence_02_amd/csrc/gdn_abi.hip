@@ -118,6 +118,25 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
     return st != GDN_OK ? st : launch_prefill(a, stream);
 }
 
+int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dtype,
+                         const float *g, const float *beta, const float *S0,
+                         const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
+                         int64_t dk, int64_t dv, int64_t chunk, int inverse, void *O,
+                         float *S_T, void *stream) {
+    if (inverse != GDN_INVERSE_DEFAULT && inverse != GDN_INVERSE_SUBSTITUTION &&
+        inverse != GDN_INVERSE_DOUBLING)
+        return GDN_ERR_UNSUPPORTED;
+    gdn::PrefillArgs a{};
+    int64_t tok_bytes = 0;
+    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
+                                 dv, chunk, O, S_T, a, tok_bytes);
+    if (st != GDN_OK) return st;
+    if (inverse != GDN_INVERSE_DEFAULT)
+        a.inverse = inverse == GDN_INVERSE_DOUBLING ? gdn::kInverseDoubling
+                                                    : gdn::kInverseSubstitution;
+    return launch_prefill(a, stream);
+}
+
 int gdn_chunk_prefill_gated(const void *q, const void *k, const void *v, int io_dtype,
                             const float *g, const float *beta, const float *S0,
                             const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,

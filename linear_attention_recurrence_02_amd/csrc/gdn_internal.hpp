@@ -10,6 +10,9 @@ namespace gdn {
 
 constexpr int kHeadDim = 128;   // dk == dv == 128: the page's per-head state size
 
+constexpr int kInverseSubstitution = 1;   // back substitution on the vector ALUs
+constexpr int kInverseDoubling = 2;       // block doubling on the matrix cores
+
 // A validated prompt-form call.  Token rows are counted in units of H heads:
 // the element (row r, head h, dim i) of q/k/v/O sits at ((r * H) + h) * 128 + i.
 struct PrefillArgs {
@@ -29,6 +32,9 @@ struct PrefillArgs {
     const void *z = nullptr;
     const float *norm_w = nullptr;
     float eps = 0.f;
+    // How the matrix-core kernel forms the diagonal 16 x 16 blocks of
+    // (I + N)^-1 (the vector kernel always substitutes column by column).
+    int inverse = kInverseDoubling;
 };
 
 struct DecodeArgs {

@@ -390,14 +390,60 @@ struct Producer {
         }
     }
 
-    // Phase 2 for the chunk in buffer set nb: T_PP = (I + N_PP)^-1 by back
-    // substitution (row r16 per lane; the four lane groups repeat it), T_PP,
-    // P_P and P'_P to LDS, and M_Pj = T_PP N_Pj for j < P.
+    // T_PP = (I + N_PP)^-1 by the exact block doubling of the Qwen3.5-9B-npu
+    // model page ("How it works" -> "Gated DeltaNet on the NPU":
+    // (D + C)^-1 = D^-1 - D^-1 C D^-1, every intermediate a true
+    // sub-inverse).  Starting from D = I, the inverse on the diagonal blocks
+    // of size b is extended to size 2b by T <- T - T C_b T, where C_b holds the
+    // entries of N coupling the two halves of each 2b block; sizes 2, 4, 8, 16.
+    // Each step is three 16x16x16 products on the matrix cores: R = C_b T,
+    // T R and its transpose R^T T^T.  T and U = T^T are both kept as result
+    // tiles (lane (c = r16, q) holds T[4q+e][c] and T[c][4q+e]): a result tile
+    // is a B operand as it is, and read as an A operand it is its own
+    // transpose.  Operands are rounded to fp16, sums are fp32.  Returns the U
+    // tile: columns 4q..4q+3 of row r16 of T_PP.
     template <int P>
+    __device__ f32x4 invert_doubling(const Smem &sm, int r16, int q) {
+        const float *Nr = sm.NR[P];
+        const f32x4 nrow = *reinterpret_cast<const f32x4 *>(&Nr[r16 * NS + 4 * q]);   // N[r16][4q..]
+        // level 1: T = I - C_1, C_1 = the entries N[i][i-1] of odd rows i
+        const float nsub = (r16 & 1) ? 0.f : Nr[(r16 + 1) * NS + r16];               // N[r16+1][r16]
+        f32x4 Tt, Ut;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 4 * q + e;
+            Tt[e] = (i == r16 ? 1.f : 0.f) - ((r16 & 1) == 0 && i == r16 + 1 ? nsub : 0.f);
+            Ut[e] = (i == r16 ? 1.f : 0.f) - ((r16 & 1) == 1 && i == r16 - 1 ? nrow[e] : 0.f);
+        }
+#pragma unroll
+        for (int b = 2; b <= 8; b *= 2) {
+            f32x4 cb;   // C_b[r16][4q+e]: rows in the lower half of a 2b block, columns in its upper half
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int j = 4 * q + e;
+                cb[e] = ((r16 / b) & 1) && j / b == r16 / b - 1 ? nrow[e] : 0.f;
+            }
+            const f32x4 R = mfma(cat(h4(cb), zh4()), cat(h4(Tt), zh4()), zero4());   // C_b T
+            const f16x8 rh = cat(h4(R), zh4()), uh = cat(h4(Ut), zh4());
+            Tt -= mfma(uh, rh, zero4());                                            // T C_b T
+            Ut -= mfma(rh, uh, zero4());                                            // (T C_b T)^T
+        }
+        return Ut;
+    }
+
+    // Phase 2 for the chunk in buffer set nb: T_PP = (I + N_PP)^-1 by back
+    // substitution (row r16 per lane; the four lane groups repeat it) or by
+    // block doubling (invert_doubling), T_PP, P_P and P'_P to LDS, and
+    // M_Pj = T_PP N_Pj for j < P.
+    template <int P, bool kDoubling>
     __device__ void solve(Smem &sm, int nb, int r16, int q) {
         r16 = opaque(r16);
         q = opaque(q);
         const float *Bt = sm.Bt[nb], *EG = sm.EG[nb];
+        f32x4 y4;       // T_PP[r16][4q..4q+3]
+        if constexpr (kDoubling) {
+            y4 = invert_doubling<P>(sm, r16, q);
+        } else {
         // Row r16 of T_PP = (I + N_PP)^-1 by back substitution: y (I + N) = e_t,
         // once y_u is final, y_j -= y_u N_uj for every j < u.  The rows of N
         // are read in three batches (rows 15..12, 11..8, 7..1), each issued
@@ -444,17 +490,19 @@ struct Producer {
 #pragma unroll
             for (int j = 0; j < uu; ++j) y[j] -= rc[r][j >> 2][j & 3] * y[uu];
         }
-        // Every lane group holds the whole row; group q rounds and stores
-        // columns 4q..4q+3 of it, picked by blending with 0/1 weights (the
-        // compiler turns selects on a lane value into an indexed scratch
-        // array).
+        // Every lane group holds the whole row; group q keeps columns
+        // 4q..4q+3 of it, picked by blending with 0/1 weights (the compiler
+        // turns selects on a lane value into an indexed scratch array).
         {
             const float m0 = q == 0 ? 1.f : 0.f, m1 = q == 1 ? 1.f : 0.f;
             const float m2 = q == 2 ? 1.f : 0.f, m3 = q == 3 ? 1.f : 0.f;
-            f32x4 y4;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 y4[e] = y[e] * m0 + y[4 + e] * m1 + y[8 + e] * m2 + y[12 + e] * m3;
+        }
+        }
+        // group q rounds and stores its 4 columns of the row
+        {
             const f32x4 bt = *reinterpret_cast<const f32x4 *>(&Bt[16 * P + 4 * q]);
             const f32x4 eg = *reinterpret_cast<const f32x4 *>(&EG[16 * P + 4 * q]);
             const int o = r16 * BS + 4 * q;
@@ -466,7 +514,7 @@ struct Producer {
         // B[t'][t] = T_PP[t][t'] (lane: column t = r16, k = t' = 4q..).  The
         // result lane holds M[t = r16][j = 4q + e]; stored negated.
         if (P > 0) {
-            const f16x8 bt = cat(rd4(&sm.Tii[P][r16 * BS + 4 * q]), zh4());
+            const f16x8 bt = cat(h4(y4), zh4());
 #pragma unroll
             for (int jb = 0; jb < P; ++jb) {
                 const f32x4 mt = mfma(cat(Nop[jb], zh4()), bt, zero4());
@@ -544,7 +592,7 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q,
     }
 }
 
-template <bool kGated>
+template <bool kGated, bool kDoubling>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
@@ -594,10 +642,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             }
             __syncthreads();
             switch (w) {
-            case 0: pr.solve<0>(sm, nb, r16, qd); break;
-            case 1: pr.solve<1>(sm, nb, r16, qd); break;
-            case 2: pr.solve<2>(sm, nb, r16, qd); break;
-            default: pr.solve<3>(sm, nb, r16, qd); break;
+            case 0: pr.solve<0, kDoubling>(sm, nb, r16, qd); break;
+            case 1: pr.solve<1, kDoubling>(sm, nb, r16, qd); break;
+            case 2: pr.solve<2, kDoubling>(sm, nb, r16, qd); break;
+            default: pr.solve<3, kDoubling>(sm, nb, r16, qd); break;
             }
             // K of chunk c+2 goes to the buffer nobody reads in phases 2 and 3
             pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
@@ -924,7 +972,9 @@ bool prefill_mfma_supports(const PrefillArgs &a) { return a.bf16 && a.chunk == C
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(512);
-    auto kern = a.z ? prefill_mfma_kernel<true> : prefill_mfma_kernel<false>;
+    const bool dbl = a.inverse == kInverseDoubling;
+    auto kern = a.z ? (dbl ? prefill_mfma_kernel<true, true> : prefill_mfma_kernel<true, false>)
+                    : (dbl ? prefill_mfma_kernel<false, true> : prefill_mfma_kernel<false, false>);
     kern<<<grid, block, 0, stream>>>(
         static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
         static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
