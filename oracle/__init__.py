@@ -21,7 +21,7 @@ import numpy as np
 
 from .build import LIB_PATH, build as _build
 
-__all__ = ["prefill", "decode", "gated_rmsnorm", "default_threads", "load"]
+__all__ = ["prefill", "decode", "gated_rmsnorm", "preop", "default_threads", "load"]
 
 _lib = None
 
@@ -48,6 +48,9 @@ def load():
     lib.gdn_oracle_decode.restype = ctypes.c_int
     lib.gdn_oracle_gated_rmsnorm.argtypes = [dp, dp, dp, i64, i64, ctypes.c_double, dp]
     lib.gdn_oracle_gated_rmsnorm.restype = ctypes.c_int
+    lib.gdn_oracle_preop.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, i64, i64, i64, i64, i64,
+                                     i64, ctypes.c_double, dp, dp, dp, dp, dp, dp]
+    lib.gdn_oracle_preop.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -162,3 +165,43 @@ def gated_rmsnorm(o, z, w, eps):
     if rc != 0:
         raise ValueError(f"oracle.gated_rmsnorm failed with code {rc}")
     return y
+
+
+def preop(xq, xk, xv, a, b, conv_w, state, cu_seqlens=None, eps=1e-6):
+    """The block's pre-operations: causal depthwise conv over the carried FIFO,
+    silu, L2 norm of q and k, g = -softplus(a), beta = sigmoid(b).
+
+    xq, xk: [B, T, H, dk]; xv: [B, T, H, dv]; a, b: [B, T, H];
+    conv_w: [3, H, dmax, K]; state: [N, 3, H, K-1, dmax] (dmax = max(dk, dv));
+    cu_seqlens as for prefill.  Returns fp64 (q, k, v, g, beta, state_out).
+    """
+    xq, xk, xv, a, b, conv_w, state = map(_f64, (xq, xk, xv, a, b, conv_w, state))
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    K = conv_w.shape[-1]
+    dmax = max(dk, dv)
+    cu = None
+    if cu_seqlens is not None:
+        if B != 1:
+            raise ValueError("oracle.preop: packed batches need B == 1")
+        cu = np.ascontiguousarray(np.asarray(
+            cu_seqlens.cpu().numpy() if hasattr(cu_seqlens, "cpu") else cu_seqlens,
+            dtype=np.int64))
+        N = cu.shape[0] - 1
+    else:
+        N = B
+    if xk.shape != xq.shape or xv.shape[:3] != (B, T, H) or a.shape != (B, T, H) \
+            or b.shape != (B, T, H) or conv_w.shape != (3, H, dmax, K) \
+            or state.shape != (N, 3, H, K - 1, dmax):
+        raise ValueError("oracle.preop: inconsistent shapes")
+    q, k = np.zeros_like(xq), np.zeros_like(xk)
+    v = np.zeros_like(xv)
+    g, beta = np.zeros_like(a), np.zeros_like(b)
+    state_out = np.zeros_like(state)
+    rc = load().gdn_oracle_preop(_ptr(xq), _ptr(xk), _ptr(xv), _ptr(a), _ptr(b), _ptr(conv_w),
+                                 _ptr(state), _ptr(cu, ctypes.c_int64), N, T, H, dk, dv, K,
+                                 float(eps), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                 _ptr(state_out))
+    if rc != 0:
+        raise ValueError(f"oracle.preop failed with code {rc}")
+    return q, k, v, g, beta, state_out

@@ -298,3 +298,99 @@ int gdn_oracle_gated_rmsnorm(const double *o, const double *z, const double *w,
     }
     return 0;
 }
+
+/*
+ * Pre-operations of a Gated DeltaNet block, from the per-token projections to
+ * the recurrence's inputs (Qwen3.5-4B -- Hexagon NPU (QHexRT) -- v81 page, the
+ * opening description of the text decoder: a short causal-conv FIFO before the
+ * SSM state; the QCS6490 page's port notes Softplus in the gate; the gate and
+ * write strength enter the recurrence as g <= 0 and beta in (0, 1)).  For every
+ * sequence n, head h and each of the three streams x in {q, k, v}, channel c:
+ *
+ *     conv_t[c] = sum_{j=0}^{K-1} w[c][j] * x_{t-K+1+j}[c]
+ *                 (rows before the sequence's first token are the carried FIFO
+ *                  state: the K-1 rows that preceded it, oldest first)
+ *     y_t[c]    = silu(conv_t[c]),                 silu(u) = u / (1 + exp(-u))
+ *     q_t       = y_t / sqrt(sum_c y_t[c]^2 + eps)  (and likewise k_t; v_t = y_t)
+ *     g_t       = -softplus(a_t),                  softplus(u) = log(1 + exp(u))
+ *     beta_t    = sigmoid(b_t)                     = 1 / (1 + exp(-b_t))
+ *
+ * and the FIFO state after the call holds the last K-1 raw rows of the
+ * concatenation [state_in; x rows of the sequence].
+ *
+ *   xq, xk : [rows, H, dk]   xv : [rows, H, dv]      (raw projections)
+ *   a, b   : [rows, H]
+ *   conv_w : [3, H, dmax, K]  (stream s = 0, 1, 2 for q, k, v; dmax = max(dk, dv);
+ *                              only the first dk or dv channels are used)
+ *   state  : [N, 3, H, K-1, dmax] in, state_out the same shape out (may alias)
+ *   cu     : N+1 row offsets (rows = cu[N]); NULL for N sequences of T rows
+ *   outputs q, k : [rows, H, dk]  v : [rows, H, dv]  g, beta : [rows, H]
+ */
+int gdn_oracle_preop(const double *xq, const double *xk, const double *xv,
+                     const double *a, const double *b, const double *conv_w,
+                     const double *state_in, const int64_t *cu, int64_t N, int64_t T,
+                     int64_t H, int64_t dk, int64_t dv, int64_t K, double eps,
+                     double *q, double *k, double *v, double *g, double *beta,
+                     double *state_out)
+{
+    if (N < 0 || T < 0 || H <= 0 || dk <= 0 || dv <= 0 || K < 1 || !(eps >= 0.0))
+        return -1;
+    const int64_t dmax = dk > dv ? dk : dv, W = K - 1;
+    const double *xs[3] = {xq, xk, xv};
+    double *ys[3] = {q, k, v};
+    const int64_t ds[3] = {dk, dk, dv};
+    double *sout = (double *)malloc((size_t)(N * 3 * H * (W > 0 ? W : 1) * dmax) * sizeof(double));
+    double *win = (double *)malloc((size_t)(K * dmax) * sizeof(double));
+    double *row = (double *)malloc((size_t)dmax * sizeof(double));
+    if (!sout || !win || !row) {
+        free(sout); free(win); free(row);
+        return -2;
+    }
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t start = cu ? cu[n] : n * T, len = cu ? cu[n + 1] - cu[n] : T;
+        for (int64_t h = 0; h < H; ++h) {
+            for (int64_t t = 0; t < len; ++t) {      /* the gates */
+                const int64_t i = (start + t) * H + h;
+                g[i] = -log1p(exp(a[i]));
+                beta[i] = 1.0 / (1.0 + exp(-b[i]));
+            }
+            for (int s = 0; s < 3; ++s) {
+                const int64_t d = ds[s];
+                const double *st = state_in + ((n * 3 + s) * H + h) * W * dmax;
+                const double *wc = conv_w + (s * H + h) * dmax * K;
+                for (int64_t t = 0; t < len; ++t) {
+                    /* window rows t-K+1 .. t: from the state before the start */
+                    for (int64_t j = 0; j < K; ++j) {
+                        const int64_t r = t - (K - 1) + j;      /* row within the sequence */
+                        for (int64_t c = 0; c < d; ++c)
+                            win[j * dmax + c] = r >= 0 ? xs[s][((start + r) * H + h) * d + c]
+                                                       : st[(W + r) * dmax + c];
+                    }
+                    double ss = 0.0;
+                    for (int64_t c = 0; c < d; ++c) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < K; ++j)
+                            acc += wc[c * K + j] * win[j * dmax + c];
+                        row[c] = acc / (1.0 + exp(-acc));
+                        ss += row[c] * row[c];
+                    }
+                    const double scale = s < 2 ? 1.0 / sqrt(ss + eps) : 1.0;
+                    for (int64_t c = 0; c < d; ++c)
+                        ys[s][((start + t) * H + h) * d + c] = row[c] * scale;
+                }
+                /* the FIFO after the call: the last W rows of [state; x rows] */
+                double *so = sout + ((n * 3 + s) * H + h) * W * dmax;
+                for (int64_t j = 0; j < W; ++j) {
+                    const int64_t r = len - W + j;              /* row within the sequence */
+                    for (int64_t c = 0; c < dmax; ++c)
+                        so[j * dmax + c] = c >= d ? 0.0
+                                         : r >= 0 ? xs[s][((start + r) * H + h) * d + c]
+                                                  : st[(W + r) * dmax + c];
+                }
+            }
+        }
+    }
+    memcpy(state_out, sout, (size_t)(N * 3 * H * W * dmax) * sizeof(double));
+    free(sout); free(win); free(row);
+    return 0;
+}

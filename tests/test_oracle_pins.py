@@ -385,3 +385,105 @@ def test_gated_rmsnorm_rejects_bad_arguments():
         oracle.gated_rmsnorm(np.ones((2, 4)), np.ones((2, 3)), np.ones(4), 1e-6)
     with pytest.raises(ValueError):
         oracle.gated_rmsnorm(np.ones((2, 4)), np.ones((2, 4)), np.ones(4), -1.0)
+
+
+# --- the block's pre-operations (conv FIFO, silu, L2 norm, gates) --------------
+
+def preop_case(rng, B, T, H, d, K=4, N=None):
+    x = [rng.standard_normal((B, T, H, d)) for _ in range(3)]
+    a = rng.standard_normal((B, T, H))
+    b = rng.standard_normal((B, T, H))
+    w = rng.standard_normal((3, H, d, K)) * 0.5
+    st = rng.standard_normal((N or B, 3, H, K - 1, d))
+    return x, a, b, w, st
+
+
+def test_preop_conv_is_numpy_correlate_over_state_and_rows():
+    from scipy.special import expit
+    rng = np.random.default_rng(51)
+    x, a, b, w, st = preop_case(rng, 1, 9, 2, 6)
+    _, _, v, _, _, _ = oracle.preop(*x, a, b, w, st, eps=0.0)
+    for h in range(2):
+        for c in range(6):
+            full = np.concatenate([st[0, 2, h, :, c], x[2][0, :, h, c]])
+            conv = np.correlate(full, w[2, h, c], mode="valid")       # 9 outputs
+            assert np.allclose(v[0, :, h, c], conv * expit(conv), rtol=1e-13, atol=1e-15)
+
+
+def test_preop_one_hot_taps():
+    from scipy.special import expit
+    rng = np.random.default_rng(52)
+    x, a, b, w, st = preop_case(rng, 1, 7, 1, 5)
+    # the newest tap alone: q is silu(x) normalised
+    w1 = np.zeros_like(w); w1[..., 3] = 1.0
+    q, _, v, _, _, _ = oracle.preop(*x, a, b, w1, st, eps=0.0)
+    y = x[0] * expit(x[0])
+    assert rel_err(q, y / np.linalg.norm(y, axis=-1, keepdims=True)) < 1e-14
+    assert rel_err(v, x[2] * expit(x[2])) < 1e-14
+    # the oldest tap alone: v_t = silu(x_{t-3}), the first three from the FIFO
+    w0 = np.zeros_like(w); w0[..., 0] = 1.0
+    _, _, v, _, _, _ = oracle.preop(*x, a, b, w0, st, eps=0.0)
+    src = np.concatenate([st[0, 2, 0], x[2][0, :, 0]], axis=0)[:7]
+    assert rel_err(v[0, :, 0], src * expit(src)) < 1e-14
+
+
+def test_preop_q_and_k_have_unit_norm():
+    rng = np.random.default_rng(53)
+    x, a, b, w, st = preop_case(rng, 2, 11, 3, 16)
+    q, k, _, _, _, _ = oracle.preop(*x, a, b, w, st, eps=0.0)
+    assert np.allclose(np.linalg.norm(q, axis=-1), 1.0, rtol=1e-13, atol=0)
+    assert np.allclose(np.linalg.norm(k, axis=-1), 1.0, rtol=1e-13, atol=0)
+
+
+def test_preop_gates_closed_forms():
+    rng = np.random.default_rng(54)
+    x, a, b, w, st = preop_case(rng, 1, 4, 1, 4)
+    a[0, :, 0] = [0.0, np.log(np.e - 1.0), -30.0, 30.0]
+    b[0, :, 0] = [0.0, np.log(3.0), -np.log(3.0), 40.0]
+    _, _, _, g, beta, _ = oracle.preop(*x, a, b, w, st)
+    assert rel_err(g[0, :, 0], [-np.log(2.0), -1.0, -np.exp(-30.0), -30.0]) < 1e-12
+    assert rel_err(beta[0, :, 0], [0.5, 0.75, 0.25, 1.0]) < 1e-15
+
+
+def test_preop_fifo_after_short_and_long_calls():
+    rng = np.random.default_rng(55)
+    x, a, b, w, st = preop_case(rng, 1, 6, 2, 4)
+    # one token: the FIFO keeps its two newest rows and appends the token
+    sl = lambda t, n: t[:, :n]
+    out = oracle.preop(*(sl(xx, 1) for xx in x), sl(a, 1), sl(b, 1), w, st)
+    s_out = out[5]
+    for s in range(3):
+        assert np.array_equal(s_out[0, s, :, :2], st[0, s, :, 1:])
+        assert np.array_equal(s_out[0, s, :, 2], x[s][0, 0])
+    # six tokens: the FIFO is the last three rows
+    s_out = oracle.preop(*x, a, b, w, st)[5]
+    for s in range(3):
+        assert np.array_equal(s_out[0, s], np.moveaxis(x[s][0, 3:], 0, 1))
+
+
+@pytest.mark.parametrize("cut", [1, 2, 3, 7])
+def test_preop_split_and_resume_equals_one_call(cut):
+    rng = np.random.default_rng(56 + cut)
+    x, a, b, w, st = preop_case(rng, 1, 12, 2, 8)
+    whole = oracle.preop(*x, a, b, w, st)
+    p1 = oracle.preop(*(xx[:, :cut] for xx in x), a[:, :cut], b[:, :cut], w, st)
+    p2 = oracle.preop(*(xx[:, cut:] for xx in x), a[:, cut:], b[:, cut:], w, p1[5])
+    for i in range(5):
+        assert np.array_equal(np.concatenate([p1[i], p2[i]], axis=1), whole[i])
+    assert np.array_equal(p2[5], whole[5])
+
+
+def test_preop_packed_batch_equals_separate_calls():
+    rng = np.random.default_rng(57)
+    lens = [5, 0, 2, 9]
+    T = sum(lens)
+    x, a, b, w, _ = preop_case(rng, 1, T, 2, 8)
+    st = rng.standard_normal((len(lens), 3, 2, 3, 8))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    packed = oracle.preop(*x, a, b, w, st, cu_seqlens=cu)
+    for n in range(len(lens)):
+        s, e = cu[n], cu[n + 1]
+        one = oracle.preop(*(xx[:, s:e] for xx in x), a[:, s:e], b[:, s:e], w, st[n:n + 1])
+        for i in range(5):
+            assert np.array_equal(packed[i][:, s:e], one[i])
+        assert np.array_equal(packed[5][n], one[5][0])
