@@ -237,6 +237,44 @@ def bench_states(torch, gdn, w, iters):
     }
 
 
+def bench_preop(torch, gdn, p, iters):
+    """The block's pre-operations (gdn_preop) over one call's projections; the
+    figure is the HBM bytes it must move per second."""
+    B, T, H = p.xq.shape[:3]
+    st = p.state.clone()
+    out = (torch.empty_like(p.xq), torch.empty_like(p.xk), torch.empty_like(p.xv),
+           torch.empty_like(p.a), torch.empty_like(p.b))
+
+    def call():
+        gdn.gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st, p.cu_seqlens, out=out)
+
+    t_end = time.perf_counter() + 0.25
+    n = 0
+    while n < 2 or time.perf_counter() < t_end:
+        call()
+        torch.cuda.synchronize()
+        n += 1
+    times = []
+    for _ in range(iters):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / 1e3)
+    t = statistics.median(times)
+    rows = B * T
+    esz = p.xq.element_size()
+    # projections in and q/k/v out, gate inputs in and g/beta out, plus each
+    # sequence's FIFO read and written (conv weights are negligible)
+    nbytes = rows * H * (6 * DK * esz + 16) + 2 * p.state.numel() * esz
+    return {
+        "workload": f"preop_{B}x{T}x{H}", "tokens": rows, "heads": H, "seconds": t,
+        "tokens_per_s": rows / t, "hbm_frac": nbytes / t / HBM_PEAK, "alg_bytes": nbytes,
+        "roofline": roofline("hbm", nbytes / t / 1e9, HBM_PEAK / 1e9, "GB/s"),
+    }
+
+
 def cpu_baseline_decode(w, target_s=12.0):
     """The oracle, as it stands, on the first n steps of the decode workload,
     n sized from a timed probe so that the sample takes about target_s."""
@@ -387,6 +425,13 @@ def main():
                 pre[rg["workload"]] = rg
             del w
             torch.cuda.empty_cache()
+        p = inputs.preop_inputs(8, 16384, 32, device="cuda")
+        r = bench_preop(torch, gdn, p, args.prefill_iters)
+        log(f"pre-operations {r['workload']}: {r['seconds']*1e3:.3f} ms, "
+            f"{r['roofline']['achieved']:.0f} GB/s, HBM {100*r['hbm_frac']:.1f}%")
+        pre[r["workload"]] = r
+        del p
+        torch.cuda.empty_cache()
         w = inputs.verify_blocks(device="cuda")
         r = bench_states(torch, gdn, w, args.prefill_iters)
         log(f"token states {r['workload']}: {r['state_write_gbs']:.1f} GB/s of states, "

@@ -197,6 +197,41 @@ int gdn_prefill_states(const void *q, const void *k, const void *v, int io_dtype
                        void *stream);
 
 /*
+ * gdn_preop -- the block's pre-operations, from the per-token projections to the
+ * recurrence's inputs, in one pass.  The Qwen3.5-4B -- Hexagon NPU (QHexRT) --
+ * v81 page describes the block as a short causal-conv FIFO, an SSM state and a
+ * gated RMSNorm; the QCS6490 page's port notes name Softplus in the gate.  For
+ * each stream x of q, k, v and channel c, with rows before a sequence's first
+ * token taken from its FIFO state:
+ *
+ *     conv_t[c] = sum_{j=0..3} conv_w[c][j] x_{t-3+j}[c],   y_t = silu(conv_t)
+ *     q_t, k_t  = y_t / sqrt(sum_c y_t[c]^2 + eps),          v_t = y_t
+ *     g_t = -softplus(a_t),   beta_t = sigmoid(b_t)
+ *
+ * and the FIFO afterwards holds each sequence's last three raw rows (the
+ * newest rows of [state_in; the sequence's rows]).  The outputs are exactly
+ * gdn_chunk_prefill's (or, with one token per sequence, gdn_decode_step's)
+ * inputs.
+ *
+ *   xq, xk, xv  [B, T, H, 128] io_dtype (packed: [1, T, H, 128]), 16-byte aligned
+ *   a, b        [B, T, H] fp32
+ *   conv_w      [3, H, 128, 4] fp32 (streams q, k, v; taps oldest first), 16-byte aligned
+ *   state_in    [N, 3, H, 3, 128] io_dtype, rows oldest first; state_out the same
+ *               shape, either exactly state_in (updated in place) or disjoint
+ *   cu_seqlens, B_or_N, T, H: as for gdn_chunk_prefill; dk = dv = 128 and
+ *               kernel_size = 4 (else GDN_ERR_UNSUPPORTED)
+ *   eps         finite and >= 0
+ *   q, k, v     like xq; g, beta like a
+ *   No output may overlap an input or another output, save state_out == state_in
+ *   (GDN_ERR_ALIAS).
+ */
+int gdn_preop(const void *xq, const void *xk, const void *xv, int io_dtype, const float *a,
+              const float *b, const float *conv_w, const void *state_in, void *state_out,
+              const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H, int64_t dk,
+              int64_t dv, int64_t kernel_size, float eps, void *q, void *k, void *v, float *g,
+              float *beta, void *stream);
+
+/*
  * gdn_decode_step -- one token per (sequence, head) with the page's one-token
  * matrix form: with d = exp(g), a = S^T k and b = S^T q read in one pass over
  * S, delta = beta (v - d a), o = d b + (q.k) delta and S' = d S + k delta^T,

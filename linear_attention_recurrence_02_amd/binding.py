@@ -21,7 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_ex",
-            "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_decode_step")
+            "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step")
 GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
 
 _lib = None
@@ -53,6 +53,9 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_prefill.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                       i64, i64, i64, i64, vp, vp, vp]
     lib.gdn_chunk_prefill.restype = ctypes.c_int
+    lib.gdn_preop.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp, vp, i64, i64, i64,
+                              i64, i64, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp]
+    lib.gdn_preop.restype = ctypes.c_int
     lib.gdn_chunk_prefill_ex.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                          i64, i64, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.gdn_chunk_prefill_ex.restype = ctypes.c_int
@@ -190,6 +193,46 @@ def gdn_chunk_prefill_gated(q, k, v, g, beta, z, norm_w, eps, S0=None, cu_seqlen
         float(eps), _ptr(Y, name="Y"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
     _check(st)
     return Y, S_T
+
+
+def gdn_preop(xq, xk, xv, a, b, conv_w, state, cu_seqlens=None, eps=1e-6, *, state_out=None,
+              out=None, stream=None):
+    """The block's pre-operations (conv FIFO, silu, L2 norm of q and k, gates).
+
+    xq, xk, xv: [B, T, H, 128] (bf16 or fp32); a, b: [B, T, H] fp32;
+    conv_w: [3, H, 128, 4] fp32; state: [N, 3, H, 3, 128] with xq's dtype.
+    state_out: None updates ``state`` in place; else a tensor of its shape.
+    out: optional (q, k, v, g, beta) to write into.
+    Returns (q, k, v, g, beta).
+    """
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed batches (cu_seqlens) need B == 1")
+    if xk.shape != xq.shape or xv.shape[:3] != xq.shape[:3] or xk.dtype != xq.dtype \
+            or xv.dtype != xq.dtype:
+        raise ValueError("xq, xk, xv must share shape [B, T, H, d] and dtype")
+    if a.shape != (B, T, H) or b.shape != (B, T, H):
+        raise ValueError("a and b must be [B, T, H]")
+    if state.shape != (N, 3, H, 3, max(dk, dv)) or state.dtype != xq.dtype:
+        raise ValueError("state must be [N, 3, H, 3, d] with the projections' dtype")
+    if state_out is None:
+        state_out = state
+    if out is None:
+        out = (torch.empty_like(xq), torch.empty_like(xk), torch.empty_like(xv),
+               torch.empty_like(a), torch.empty_like(b))
+    q, k, v, g, beta = out
+    st = load_library().gdn_preop(
+        _ptr(xq, name="xq"), _ptr(xk, name="xk"), _ptr(xv, name="xv"), _io_dtype(xq),
+        _ptr(a, torch.float32, "a"), _ptr(b, torch.float32, "b"),
+        _ptr(conv_w, torch.float32, "conv_w"), _ptr(state, name="state"),
+        _ptr(state_out, name="state_out"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+        N, T, H, dk, dv, conv_w.shape[-1], float(eps), _ptr(q, name="q"), _ptr(k, name="k"),
+        _ptr(v, name="v"), _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+        _stream(stream))
+    _check(st)
+    return q, k, v, g, beta
 
 
 def gdn_prefill_states(q, k, v, g, beta, S0=None, cu_seqlens=None, *, O=None, S_tok=None,

@@ -208,6 +208,57 @@ int gdn_prefill_states(const void *q, const void *k, const void *v, int io_dtype
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+int gdn_preop(const void *xq, const void *xk, const void *xv, int io_dtype, const float *a,
+              const float *b, const float *conv_w, const void *state_in, void *state_out,
+              const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H, int64_t dk,
+              int64_t dv, int64_t kernel_size, float eps, void *q, void *k, void *v, float *g,
+              float *beta, void *stream) {
+    if (!dims_ok(B_or_N) || !dims_ok(T) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
+    const int64_t N = B_or_N;
+    const int64_t rows = cu_seqlens ? T : N * T;
+    if (rows > 0 && (!xq || !xk || !xv || !a || !b || !q || !k || !v || !g || !beta))
+        return GDN_ERR_INVALID_ARG;
+    if (N > 0 && (!conv_w || !state_in || !state_out)) return GDN_ERR_INVALID_ARG;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (dk != gdn::kHeadDim || dv != gdn::kHeadDim || kernel_size != 4) return GDN_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f && eps <= FLT_MAX)) return GDN_ERR_INVALID_ARG;
+    for (const void *p : {xq, xk, xv, static_cast<const void *>(q), static_cast<const void *>(k),
+                          static_cast<const void *>(v), static_cast<const void *>(conv_w), state_in,
+                          static_cast<const void *>(state_out)})
+        if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    for (const void *p : {static_cast<const void *>(a), static_cast<const void *>(b),
+                          static_cast<const void *>(g), static_cast<const void *>(beta),
+                          static_cast<const void *>(cu_seqlens)})
+        if (!aligned(p, 4)) return GDN_ERR_INVALID_ARG;
+    if (N >= kMaxDim) return GDN_ERR_INVALID_ARG;
+    if (rows > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return GDN_ERR_INVALID_ARG;
+    if ((rows + 127) / 128 >= 65536) return GDN_ERR_INVALID_ARG;     // grid.y of the launch
+    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t tok = rows * H * gdn::kHeadDim * esz, gb = rows * H * 4;
+    const int64_t st = N * 3 * H * 3 * gdn::kHeadDim * esz, wb = 3 * H * gdn::kHeadDim * 4 * 4;
+    const Range rxq = span_of(xq, tok), rxk = span_of(xk, tok), rxv = span_of(xv, tok),
+                ra = span_of(a, gb), rb = span_of(b, gb), rw = span_of(conv_w, wb),
+                rsi = span_of(state_in, st), rso = span_of(state_out, st),
+                rq = span_of(q, tok), rk = span_of(k, tok), rv = span_of(v, tok),
+                rg = span_of(g, gb), rbe = span_of(beta, gb);
+    for (Range o : {rq, rk, rv, rg, rbe, rso}) {
+        for (Range i : {rxq, rxk, rxv, ra, rb, rw})
+            if (overlap(o, i)) return GDN_ERR_ALIAS;
+    }
+    const Range outs[] = {rq, rk, rv, rg, rbe, rso};
+    for (int i = 0; i < 6; ++i)
+        for (int j = i + 1; j < 6; ++j)
+            if (overlap(outs[i], outs[j])) return GDN_ERR_ALIAS;
+    for (Range o : {rq, rk, rv, rg, rbe})
+        if (overlap(o, rsi)) return GDN_ERR_ALIAS;
+    if (overlap(rso, rsi) && rso.lo != rsi.lo) return GDN_ERR_ALIAS;   // in place or apart
+    if (N == 0) return GDN_OK;
+    gdn::PreopArgs p{xq, xk, xv, a, b, conv_w, state_in, state_out, cu_seqlens, N, T, rows, H,
+                     eps, io_dtype == GDN_BF16, q, k, v, g, beta};
+    const hipError_t e = gdn::launch_preop(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
                     const float *g, const float *beta, float *S, int64_t B,
                     int64_t H, int64_t dk, int64_t dv, void *o, void *stream) {

@@ -46,7 +46,23 @@ struct DecodeArgs {
     void *o;
 };
 
+// A validated pre-operation call (conv FIFO, silu, L2 norm, gates).
+struct PreopArgs {
+    const void *xq, *xk, *xv;   // raw projections [rows, H, 128]
+    const float *a, *b;         // gate inputs [rows, H]
+    const float *conv_w;        // [3, H, 128, 4]
+    const void *state_in;       // [N, 3, H, 3, 128], io dtype
+    void *state_out;            // same shape; may be state_in
+    const int32_t *cu_seqlens;  // may be null
+    int64_t N, T, rows, H;
+    float eps;
+    bool bf16;
+    void *q, *k, *v;
+    float *g, *beta;
+};
+
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_preop(const PreopArgs &p, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
 bool prefill_mfma_supports(const PrefillArgs &a);

@@ -175,3 +175,42 @@ def norm_gate(w: Workload, seed: int = 0, eps: float = 1e-6):
     z = torch.randn(*w.v.shape, generator=gen, device=w.v.device).to(w.v.dtype)
     norm_w = 0.5 + torch.rand(w.v.shape[-1], generator=gen, device=w.v.device)
     return z, norm_w, eps
+
+
+@dataclass
+class PreopInputs:
+    """Inputs of the block's pre-operations for one call."""
+    xq: torch.Tensor
+    xk: torch.Tensor
+    xv: torch.Tensor
+    a: torch.Tensor
+    b: torch.Tensor
+    conv_w: torch.Tensor
+    state: torch.Tensor
+    cu_seqlens: Optional[torch.Tensor] = None
+
+
+def preop_inputs(B: int, T: int, H: int, *, lengths=None, io_dtype=torch.bfloat16,
+                 seed: int = 0, device="cpu") -> PreopInputs:
+    """Raw projections and gate inputs for B sequences of T tokens (or a packed
+    batch of ``lengths``), drawn from a generator on ``device`` seeded with
+    ``seed`` in the order xq, xk, xv, a, b, conv_w, state: projections, gate
+    inputs and FIFO state ~ N(0, 1) (projections and state in the io dtype),
+    conv weights ~ N(0, 0.5^2) fp32.  No trained weights are involved; the
+    draws stand in for a model's projections and its conv parameters."""
+    gen = _generator(seed, device)
+    rn = lambda *shape: torch.randn(*shape, generator=gen, device=gen.device)
+    cu = None
+    if lengths is not None:
+        lengths = torch.as_tensor(lengths, dtype=torch.int64)
+        c = torch.zeros(lengths.numel() + 1, dtype=torch.int64)
+        c[1:] = torch.cumsum(lengths, 0)
+        cu = c.to(torch.int32).to(device)
+        B, T, N = 1, int(c[-1]), lengths.numel()
+    else:
+        N = B
+    xq, xk, xv = (rn(B, T, H, DK).to(io_dtype) for _ in range(3))
+    a, b = rn(B, T, H), rn(B, T, H)
+    conv_w = 0.5 * rn(3, H, DK, 4)
+    state = rn(N, 3, H, 3, DK).to(io_dtype)
+    return PreopInputs(xq, xk, xv, a, b, conv_w, state, cu)

@@ -160,6 +160,35 @@ def test_prefill_gated_validation(lib):
                  Y=None, N=0) == binding.GDN_OK
 
 
+def preop(lib, xq=A, xk=A + 8 * MB, xv=A + 16 * MB, dtype=1, a=A + 24 * MB, b=A + 25 * MB,
+          w=A + 26 * MB, si=A + 27 * MB, so=A + 27 * MB, cu=None, N=2, T=64, H=2, dk=128,
+          dv=128, K=4, eps=1e-6, q=A + 32 * MB, k=A + 40 * MB, v=A + 48 * MB, g=A + 56 * MB,
+          beta=A + 57 * MB):
+    return lib.gdn_preop(xq, xk, xv, dtype, a, b, w, si, so, cu, N, T, H, dk, dv, K, eps, q, k,
+                         v, g, beta, None)
+
+
+def test_preop_validation(lib):
+    assert preop(lib, xq=None) == binding.GDN_ERR_INVALID_ARG
+    assert preop(lib, w=None) == binding.GDN_ERR_INVALID_ARG
+    assert preop(lib, si=None) == binding.GDN_ERR_INVALID_ARG
+    assert preop(lib, K=3) == binding.GDN_ERR_UNSUPPORTED
+    assert preop(lib, dk=64) == binding.GDN_ERR_UNSUPPORTED
+    assert preop(lib, dtype=9) == binding.GDN_ERR_UNSUPPORTED
+    assert preop(lib, eps=-1.0) == binding.GDN_ERR_INVALID_ARG
+    assert preop(lib, xk=A + 8 * MB + 8) == binding.GDN_ERR_INVALID_ARG
+    assert preop(lib, w=A + 26 * MB + 4) == binding.GDN_ERR_INVALID_ARG
+    # 2 x 64 rows x 2 heads x 256 B = 64 KiB per token tensor
+    assert preop(lib, q=A + 1024) == binding.GDN_ERR_ALIAS              # q over xq
+    assert preop(lib, k=A + 32 * MB + 4096) == binding.GDN_ERR_ALIAS    # k over q
+    assert preop(lib, g=A + 24 * MB) == binding.GDN_ERR_ALIAS           # g over a
+    assert preop(lib, so=A + 27 * MB + 256) == binding.GDN_ERR_ALIAS    # partial state overlap
+    assert preop(lib, q=A + 27 * MB) == binding.GDN_ERR_ALIAS           # q over state_in
+    assert preop(lib, N=0) == binding.GDN_OK
+    assert preop(lib, N=0, xq=None, xk=None, xv=None, a=None, b=None, w=None, si=None,
+                 so=None, q=None, k=None, v=None, g=None, beta=None) == binding.GDN_OK
+
+
 def test_decode_rejects_bad_calls(lib):
     assert decode(lib, S=None) == binding.GDN_ERR_INVALID_ARG
     assert decode(lib, B=-1) == binding.GDN_ERR_INVALID_ARG

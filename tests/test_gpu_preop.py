@@ -1,0 +1,127 @@
+"""GPU parity of gdn_preop (the block's pre-operations: conv FIFO, silu, L2
+norm of q and k, gates) against the fp64 oracle, through the C ABI.
+
+Token outputs are compared row by row: an element may differ from the
+reference by 1e-5 * max|r| over its (token, head) row, plus half a unit in the
+last place of a bf16 output.  g and beta (fp32) to 1e-5 relative; the FIFO
+state holds copies of raw input rows and must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_02_amd import inputs
+from linear_attention_recurrence_02_amd.binding import gdn_chunk_prefill, gdn_preop
+from metrics import TOL_BF16, bf16_half_ulp, bf16_output_ok, f64, spans_of, worst_slice_error
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 1e-5
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def row_ok(x, r, bf16):
+    x, r = f64(x).reshape(-1, 128), f64(r).reshape(-1, 128)
+    if x.size == 0:
+        return 0.0
+    bound = TOL * np.abs(r).max(axis=1, keepdims=True)
+    if bf16:
+        bound = bound + bf16_half_ulp(np.maximum(np.abs(x), np.abs(r)))
+    return float((np.abs(x - r) / np.where(bound > 0, bound, 1e-300)).max())
+
+
+def check(p, out, state_out, label, eps=1e-6):
+    ref = oracle.preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, p.state, p.cu_seqlens, eps)
+    bf16 = p.xq.dtype == torch.bfloat16
+    ratios = [row_ok(out[i], ref[i], bf16) for i in range(3)]
+    say(f"[{label}] q/k/v bound ratios {ratios[0]:.3f} {ratios[1]:.3f} {ratios[2]:.3f}")
+    assert max(ratios) <= 1.0
+    for i in (3, 4):
+        assert np.allclose(f64(out[i]), ref[i], rtol=TOL, atol=1e-7)
+    assert np.array_equal(f64(state_out), ref[5]), "the FIFO state is a copy of raw rows"
+
+
+def test_preop_bf16_batch():
+    p = inputs.preop_inputs(2, 100, 3, seed=61, device=DEV)
+    st = p.state.clone()
+    out = gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st)
+    torch.cuda.synchronize()
+    check(p, out, st, "bf16 2x100")
+
+
+def test_preop_packed_with_empty_and_short_sequences_out_of_place():
+    p = inputs.preop_inputs(0, 0, 2, lengths=[0, 1, 2, 5, 130, 3], seed=62, device=DEV)
+    so = torch.empty_like(p.state)
+    snap = p.state.clone()
+    out = gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, p.state, p.cu_seqlens, state_out=so)
+    torch.cuda.synchronize()
+    assert torch.equal(p.state, snap)
+    check(p, out, so, "bf16 packed")
+
+
+def test_preop_fp32():
+    p = inputs.preop_inputs(1, 77, 2, io_dtype=torch.float32, seed=63, device=DEV)
+    st = p.state.clone()
+    out = gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st, eps=0.0)
+    torch.cuda.synchronize()
+    check(p, out, st, "fp32", eps=0.0)
+
+
+@pytest.mark.parametrize("cut", [1, 2, 3, 64, 129])
+def test_preop_split_and_resume_is_bitwise_one_call(cut):
+    p = inputs.preop_inputs(1, 300, 2, seed=64, device=DEV)
+    s1 = p.state.clone()
+    whole = gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, s1)
+    s2 = p.state.clone()
+    sl = lambda x, a, b: x[:, a:b].contiguous()
+    first = gdn_preop(sl(p.xq, 0, cut), sl(p.xk, 0, cut), sl(p.xv, 0, cut), sl(p.a, 0, cut),
+                      sl(p.b, 0, cut), p.conv_w, s2)
+    second = gdn_preop(sl(p.xq, cut, 300), sl(p.xk, cut, 300), sl(p.xv, cut, 300),
+                       sl(p.a, cut, 300), sl(p.b, cut, 300), p.conv_w, s2)
+    torch.cuda.synchronize()
+    for i in range(5):
+        assert torch.equal(torch.cat([first[i], second[i]], dim=1), whole[i]), i
+    assert torch.equal(s1, s2)
+
+
+def test_preop_large_workload_sampled_heads():
+    # the large prompt workload's shape: 8 x 16384 tokens x 32 heads
+    p = inputs.preop_inputs(8, 16384, 32, seed=65, device=DEV)
+    st = p.state.clone()
+    out = gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st)
+    torch.cuda.synchronize()
+    for n, h in ((0, 0), (7, 21)):
+        sub = inputs.PreopInputs(*(x[n:n + 1, :, h:h + 1] for x in (p.xq, p.xk, p.xv, p.a, p.b)),
+                                 p.conv_w[:, h:h + 1], p.state[n:n + 1, :, h:h + 1])
+        check(sub, [o[n:n + 1, :, h:h + 1] for o in out], st[n:n + 1, :, h:h + 1],
+              f"large seq {n} head {h}")
+
+
+def test_preop_then_prompt_form_end_to_end():
+    # the block from projections to outputs: pre-operations then the prompt form
+    p = inputs.preop_inputs(1, 200, 2, seed=66, device=DEV)
+    st = p.state.clone()
+    q, k, v, g, beta = gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st)
+    S0 = 0.1 * torch.randn(1, 2, 128, 128, device=DEV,
+                           generator=torch.Generator(device=DEV).manual_seed(66))
+    O, S_T = gdn_chunk_prefill(q, k, v, g, beta, S0, None, 64)
+    torch.cuda.synchronize()
+    spans = spans_of(1, 200)
+    # (1) the composition: the prompt form on the pre-operations' own outputs
+    Or, Sr = oracle.prefill(q, k, v, g, beta, S0)
+    ok, ratio = bf16_output_ok(O, Or, TOL_BF16, spans, 2)
+    es = worst_slice_error(S_T, Sr)
+    say(f"[composition] O bound ratio {ratio:.3f}, S_T {es:.3e}")
+    assert ok and es <= TOL_BF16
+    # (2) against the fp64 chain from the raw projections: the only extra error
+    # is the rounding of q, k and v to bf16 between the two steps (2^-9
+    # relative each, entering O and S bilinearly), so 4 * 2^-9 bounds it
+    rq, rk, rv, rg, rb, _ = oracle.preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, p.state)
+    Oc, Sc = oracle.prefill(rq, rk, rv, rg, rb, S0)
+    eo, es = worst_slice_error(O, Oc, spans, 2), worst_slice_error(S_T, Sc)
+    say(f"[fp64 chain] O {eo:.3e}, S_T {es:.3e} (bound {4 * 2.0 ** -9:.3e})")
+    assert eo <= 4 * 2.0 ** -9 and es <= 4 * 2.0 ** -9
