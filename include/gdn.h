@@ -142,8 +142,8 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
  * gdn_chunk_prefill_gated -- gdn_chunk_prefill with the gated RMS norm that
  * follows the recurrence in a Gated DeltaNet block (Qwen3.5-4B -- Hexagon NPU
  * (QHexRT) -- v81 page, the opening description of the text decoder: a short
- * causal-conv FIFO, an SSM state and a gated RMSNorm) applied to each output
- * row before it is rounded and stored:
+ * convolution window carried between calls, the recurrent state and a gated
+ * RMS norm) applied to each output row before it is rounded and stored:
  *
  *     y = norm_w * o / sqrt(mean(o^2) + eps) * silu(z),  silu(x) = x / (1 + exp(-x))
  *
@@ -199,8 +199,9 @@ int gdn_prefill_states(const void *q, const void *k, const void *v, int io_dtype
 /*
  * gdn_preop -- the block's pre-operations, from the per-token projections to the
  * recurrence's inputs, in one pass.  The Qwen3.5-4B -- Hexagon NPU (QHexRT) --
- * v81 page describes the block as a short causal-conv FIFO, an SSM state and a
- * gated RMSNorm; the QCS6490 page's port notes name Softplus in the gate.  For
+ * v81 page lists a causal convolution over a short window carried between calls,
+ * the recurrent state and a gated RMS norm; the QCS6490 page's port notes name
+ * Softplus among the gate's operations.  For
  * each stream x of q, k, v and channel c, with rows before a sequence's first
  * token taken from its FIFO state:
  *

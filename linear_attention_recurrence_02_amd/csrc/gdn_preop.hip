@@ -1,7 +1,8 @@
 // The block's pre-operations, from the per-token projections to the
 // recurrence's inputs (Qwen3.5-4B -- Hexagon NPU (QHexRT) -- v81 page, the
-// opening description of the text decoder: a short causal-conv FIFO before the
-// SSM state; Softplus in the gate per the QCS6490 page's port notes), in one
+// opening description of the text decoder: a causal convolution over a short
+// window carried between calls comes before the recurrent state; the QCS6490
+// page's port notes name Softplus among the gate's operations), in one
 // pass over the tokens.  For each of the streams q, k, v and every channel c:
 //     conv_t[c] = sum_j w[c][j] x_{t-3+j}[c]  (rows before a sequence's first
 //                 token come from its FIFO state), y_t = silu(conv_t),

@@ -269,8 +269,8 @@ int gdn_oracle_decode(const double *q, const double *k, const double *v,
 /*
  * Gated RMS norm of output rows -- the norm that follows the recurrence inside
  * a Gated DeltaNet block (Qwen3.5-4B -- Hexagon NPU (QHexRT) -- v81 page, the
- * opening description of the text decoder: a short causal-conv FIFO, an SSM
- * state and a gated RMSNorm; the Qwen3.5-9B-npu model page, "How it works" ->
+ * opening description of the text decoder, which lists a short convolution
+ * window carried between calls, the recurrent state and a gated RMS norm; the Qwen3.5-9B-npu model page, "How it works" ->
  * "fp16 precision of the DeltaNet output", relies on that norm being
  * scale-invariant with eps scaled by the square of the factor).  Per row of dv
  * values:
@@ -302,8 +302,9 @@ int gdn_oracle_gated_rmsnorm(const double *o, const double *z, const double *w,
 /*
  * Pre-operations of a Gated DeltaNet block, from the per-token projections to
  * the recurrence's inputs (Qwen3.5-4B -- Hexagon NPU (QHexRT) -- v81 page, the
- * opening description of the text decoder: a short causal-conv FIFO before the
- * SSM state; the QCS6490 page's port notes Softplus in the gate; the gate and
+ * opening description of the text decoder: a causal convolution over a short
+ * window carried between calls comes before the recurrent state; the QCS6490
+ * page's port notes name Softplus among the gate's operations; the gate and
  * write strength enter the recurrence as g <= 0 and beta in (0, 1)).  For every
  * sequence n, head h and each of the three streams x in {q, k, v}, channel c:
  *

@@ -365,7 +365,7 @@ def test_gated_rmsnorm_gate_limits():
 
 def test_gated_norm_of_the_output_is_invariant_to_the_pages_q_rescale():
     # The Qwen3.5-9B-npu page rescales q by 1024 inside the recurrence and the
-    # norm's eps by 1024^2 and calls it the same math: O is linear in q, so
+    # norm's eps by 1024^2 and states that nothing changes: O is linear in q, so
     # mean(O^2) scales by 1024^2 and the norm's output does not change.
     rng = np.random.default_rng(33)
     q, k, v, g, beta, S0 = rand_case(rng, 1, 40, 2, 128, 128)
