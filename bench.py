@@ -420,6 +420,8 @@ def main():
                 # the same workload with the gated RMS norm fused on the output
                 rg = bench_prefill(torch, gdn, w, args.prefill_iters, 2,
                                    gate=inputs.norm_gate(w))
+                rg["roofline"]["traffic"] = read_traffic(
+                    "prefill_large_gated", source_digest("gdn_prefill_mfma.hip"))
                 log(f"prefill {rg['workload']}: {rg['tokens_per_s']:.3e} tok/s, "
                     f"{rg['seconds']*1e3:.3f} ms, HBM {100*rg['hbm_frac']:.1f}%")
                 pre[rg["workload"]] = rg
@@ -427,6 +429,7 @@ def main():
             torch.cuda.empty_cache()
         p = inputs.preop_inputs(8, 16384, 32, device="cuda")
         r = bench_preop(torch, gdn, p, args.prefill_iters)
+        r["roofline"]["traffic"] = read_traffic("preop_large", source_digest("gdn_preop.hip"))
         log(f"pre-operations {r['workload']}: {r['seconds']*1e3:.3f} ms, "
             f"{r['roofline']['achieved']:.0f} GB/s, HBM {100*r['hbm_frac']:.1f}%")
         pre[r["workload"]] = r
@@ -434,6 +437,8 @@ def main():
         torch.cuda.empty_cache()
         w = inputs.verify_blocks(device="cuda")
         r = bench_states(torch, gdn, w, args.prefill_iters)
+        r["roofline"]["traffic"] = read_traffic("token_states_verify",
+                                                source_digest("gdn_states.hip"))
         log(f"token states {r['workload']}: {r['state_write_gbs']:.1f} GB/s of states, "
             f"{r['seconds']*1e3:.3f} ms, HBM {100*r['hbm_frac']:.1f}%")
         pre[r["workload"]] = r
