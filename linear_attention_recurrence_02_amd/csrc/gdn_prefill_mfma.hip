@@ -641,6 +641,12 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             default: pr.gram<3>(sm, nb, r16, qd); break;
             }
             __syncthreads();
+            // Phase 2 is the producers' critical phase, while the consumers'
+            // output step there has slack: the producers take precedence on
+            // their SIMDs (matrix core and vector ALU) until it ends.  Not
+            // with the gated norm, whose consumers norm and store the rows in
+            // this phase.
+            if constexpr (!kGated) __builtin_amdgcn_s_setprio(2);
             switch (w) {
             case 0: pr.solve<0, kDoubling>(sm, nb, r16, qd); break;
             case 1: pr.solve<1, kDoubling>(sm, nb, r16, qd); break;
@@ -650,6 +656,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             // K of chunk c+2 goes to the buffer nobody reads in phases 2 and 3
             pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
             pr.prefetch(u, c + 3, w, l, r16, qd);
+            if constexpr (!kGated) __builtin_amdgcn_s_setprio(0);
             __syncthreads();
             switch (w) {
             case 0: pr.store_a<0>(sm, r16, qd); break;
