@@ -80,6 +80,46 @@ template <> __device__ __forceinline__ __hip_bfloat16 from_f32<__hip_bfloat16>(f
     return __float2bfloat16(x);   // round to nearest even
 }
 
+// Packed batches of at most this many sequences are walked longest first.
+constexpr int64_t kMaxRankedSequences = 1024;
+
+// The sequence a workgroup of a packed batch takes so that the longest
+// sequences start first: the one of rank p when sequences are ordered by
+// length, longest first, ties by index (a permutation of 0..N-1).  Every
+// thread of the workgroup calls it with the same lens buffer (LDS, room for
+// kMaxRankedSequences + 3 ints): the lengths, from the clamped offsets as
+// everywhere else, are staged there once, then each thread ranks a share of
+// the sequences by counting, and the one whose rank is p is left in *slot.
+// The caller synchronises the workgroup before reading *slot.
+__device__ __forceinline__ void rank_longest_first(const int32_t *cu, int64_t N, int64_t T,
+                                                   int64_t p, int tid, int nthreads,
+                                                   int32_t *lens, int64_t *slot) {
+    const int n4 = static_cast<int>((N + 3) / 4) * 4;
+    for (int n = tid; n < n4; n += nthreads) {
+        int32_t l = -1;                              // padding ranks below every sequence
+        if (n < N) {
+            int64_t a = cu[n], b = cu[n + 1];
+            a = a < 0 ? 0 : (a > T ? T : a);
+            b = b < a ? a : (b > T ? T : b);
+            l = static_cast<int32_t>(b - a);
+        }
+        lens[n] = l;
+    }
+    __syncthreads();
+    for (int n = tid; n < N; n += nthreads) {
+        const int32_t ln = lens[n];
+        int rank = 0;
+        for (int m = 0; m < n4; m += 4) {
+            const int4 l4 = *reinterpret_cast<const int4 *>(&lens[m]);
+            rank += (l4.x > ln) || (l4.x == ln && m < n);
+            rank += (l4.y > ln) || (l4.y == ln && m + 1 < n);
+            rank += (l4.z > ln) || (l4.z == ln && m + 2 < n);
+            rank += (l4.w > ln) || (l4.w == ln && m + 3 < n);
+        }
+        if (rank == p) *slot = n;
+    }
+}
+
 // Sequence span of unit n: first token row and length.  Offsets from the
 // device are clamped into [0, T] so that a malformed array cannot make a
 // kernel read or write outside the caller's buffers.

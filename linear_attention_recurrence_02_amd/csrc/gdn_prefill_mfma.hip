@@ -596,9 +596,9 @@ template <bool kGated, bool kDoubling>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
-    const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t T,
+    const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t N, int64_t T,
     int64_t H, bf16 *__restrict__ O, float *__restrict__ S_T, const bf16 *__restrict__ z,
-    const float *__restrict__ norm_w, float eps) {
+    const float *__restrict__ norm_w, float eps, int rank_units) {
     __shared__ Smem sm;
     // Gated norm: consumer wave w's gate columns 32w..32w+31, token-major; the
     // 16-byte slot j of row t at j ^ zsw(t).  A variable of its own, so that
@@ -609,12 +609,26 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const int tid = threadIdx.x;
     const int wave = tid >> 6, l = tid & 63, r16 = l & 15, qd = l >> 4;
     const int w = wave & 3;                 // consumer column group / producer row block
-    const int64_t unit = blockIdx.x;
+    // A packed batch of sequences of mixed lengths is walked longest first
+    // (when the launch decided so), so that the long ones do not start last
+    // and set the end of the launch.
+    int64_t seq = blockIdx.x / H;
+    if (rank_units) {
+        // the lengths are staged in the first key buffer, which the producers
+        // first write after the barrier below
+        static_assert(sizeof(sm.K[0]) >= 4 * (kMaxRankedSequences + 3), "lens buffer");
+        __shared__ int64_t pick;
+        rank_longest_first(cu_seqlens, N, T, seq, tid, 512, reinterpret_cast<int32_t *>(sm.K[0]),
+                           &pick);
+        __syncthreads();
+        seq = pick;
+    }
+    const int64_t unit = seq * H + blockIdx.x % H;
     Unit u;
     u.q = q; u.k = k; u.v = v; u.g = g; u.beta = beta;
     u.H = H;
     u.h = unit % H;
-    sequence_span(cu_seqlens, unit / H, T, u.start, u.len);
+    sequence_span(cu_seqlens, seq, T, u.start, u.len);
     const int nch = static_cast<int>((u.len + C - 1) / C);
 
     if (wave >= 4) {
@@ -977,15 +991,35 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 
 bool prefill_mfma_supports(const PrefillArgs &a) { return a.bf16 && a.chunk == C; }
 
+// Whether the workgroups of a launch should take their sequences longest first:
+// it pays when a packed batch gives each CU only a few workgroups, so that a
+// long sequence started late sets the end of the launch; with many short
+// workgroups per CU the dispatch balances them already and the ranking (paid
+// by every workgroup) only costs.
+bool rank_longest_first_pays(const PrefillArgs &a) {
+    if (!a.cu_seqlens || a.N > kMaxRankedSequences) return false;
+    static int cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return false;
+        cus[dev] = n;
+    }
+    return a.N * a.H <= 4 * static_cast<int64_t>(cus[dev]);
+}
+
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(512);
+    const int rank = rank_longest_first_pays(a) ? 1 : 0;
     const bool dbl = a.inverse == kInverseDoubling;
     auto kern = a.z ? (dbl ? prefill_mfma_kernel<true, true> : prefill_mfma_kernel<true, false>)
                     : (dbl ? prefill_mfma_kernel<false, true> : prefill_mfma_kernel<false, false>);
     kern<<<grid, block, 0, stream>>>(
         static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
-        static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
-        static_cast<bf16 *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps);
+        static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.N, a.T, a.H,
+        static_cast<bf16 *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps, rank);
     return hipGetLastError();
 }
 
