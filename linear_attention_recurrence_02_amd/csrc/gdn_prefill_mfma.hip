@@ -592,13 +592,13 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q,
     }
 }
 
-template <bool kGated, bool kDoubling>
+template <bool kGated, bool kDoubling, bool kRank>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t N, int64_t T,
     int64_t H, bf16 *__restrict__ O, float *__restrict__ S_T, const bf16 *__restrict__ z,
-    const float *__restrict__ norm_w, float eps, int rank_units) {
+    const float *__restrict__ norm_w, float eps) {
     __shared__ Smem sm;
     // Gated norm: consumer wave w's gate columns 32w..32w+31, token-major; the
     // 16-byte slot j of row t at j ^ zsw(t).  A variable of its own, so that
@@ -610,10 +610,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const int wave = tid >> 6, l = tid & 63, r16 = l & 15, qd = l >> 4;
     const int w = wave & 3;                 // consumer column group / producer row block
     // A packed batch of sequences of mixed lengths is walked longest first
-    // (when the launch decided so), so that the long ones do not start last
-    // and set the end of the launch.
+    // (in the instantiation the launch picks for it), so that the long ones do
+    // not start last and set the end of the launch.
     int64_t seq = blockIdx.x / H;
-    if (rank_units) {
+    if constexpr (kRank) {
         // the lengths are staged in the first key buffer, which the producers
         // first write after the barrier below
         static_assert(sizeof(sm.K[0]) >= 4 * (kMaxRankedSequences + 3), "lens buffer");
@@ -1012,14 +1012,16 @@ bool rank_longest_first_pays(const PrefillArgs &a) {
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(512);
-    const int rank = rank_longest_first_pays(a) ? 1 : 0;
+    const bool rank = rank_longest_first_pays(a);
+    // (the longest-first order is compiled into the default form only)
     const bool dbl = a.inverse == kInverseDoubling;
-    auto kern = a.z ? (dbl ? prefill_mfma_kernel<true, true> : prefill_mfma_kernel<true, false>)
-                    : (dbl ? prefill_mfma_kernel<false, true> : prefill_mfma_kernel<false, false>);
+    auto kern = a.z ? (dbl ? prefill_mfma_kernel<true, true, false> : prefill_mfma_kernel<true, false, false>)
+                    : (dbl ? (rank ? prefill_mfma_kernel<false, true, true> : prefill_mfma_kernel<false, true, false>)
+                           : prefill_mfma_kernel<false, false, false>);
     kern<<<grid, block, 0, stream>>>(
         static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
         static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.N, a.T, a.H,
-        static_cast<bf16 *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps, rank);
+        static_cast<bf16 *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps);
     return hipGetLastError();
 }
 

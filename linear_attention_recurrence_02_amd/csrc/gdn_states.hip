@@ -16,10 +16,12 @@
 // 256-thread workgroup per half; the half stays in registers across the
 // sequence (thread (wave w, lane l): columns 64 half + 4 (l%16)..+3, rows
 // rp + 16m with rp = 4w + l/16), and after each token every thread writes its
-// 8 x 16 bytes of the new state.  q and k of the token go through LDS (double-
-// buffered, so one barrier per token separates their write from the previous
-// token's reads); the column sums a and b are reduced across lanes and then
-// across the four waves through LDS.
+// 8 x 16 bytes of the new state.  The column sums a and b are reduced across
+// lanes and then across the four waves through LDS, which takes the token's
+// one barrier; q and k of the next token are written to LDS before that
+// barrier, into one of three buffers (the one two tokens back, which every
+// thread has finished reading once it reaches this token's barrier), so the
+// same barrier publishes them.
 
 #include "gdn_internal.hpp"
 
@@ -50,8 +52,8 @@ __global__ __launch_bounds__(256) void states_kernel(const IO *__restrict__ q,
     const int rp = 4 * w + (lane >> 4);
     const int c0 = 64 * half + 4 * cg;          // first of this thread's 4 columns
 
-    __shared__ float sq[2][D], sk[2][D];
-    __shared__ float4 red_a[4][16], red_b[4][16];
+    __shared__ float sq[3][D], sk[3][D];
+    __shared__ float4 red_a[2][4][16], red_b[2][4][16];
 
     float4 s[8];
     if (S0) {
@@ -63,14 +65,16 @@ __global__ __launch_bounds__(256) void states_kernel(const IO *__restrict__ q,
         for (int m = 0; m < 8; ++m) s[m] = make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
+    if (len > 0 && tid < D) {
+        const int64_t tok = (start * H + h) * D;
+        sq[0][tid] = to_f32(q[tok + tid]);
+        sk[0][tid] = to_f32(k[tok + tid]);
+    }
+    __syncthreads();
     for (int64_t t = 0; t < len; ++t) {
-        const int buf = static_cast<int>(t & 1);
+        const int buf = static_cast<int>(t % 3), rb = static_cast<int>(t & 1);
         const int64_t row = start + t;
         const int64_t tok = (row * H + h) * D;
-        if (tid < D) {
-            sq[buf][tid] = to_f32(q[tok + tid]);
-            sk[buf][tid] = to_f32(k[tok + tid]);
-        }
         float4 vv;
         vv.x = to_f32(v[tok + c0]);
         vv.y = to_f32(v[tok + c0 + 1]);
@@ -78,7 +82,6 @@ __global__ __launch_bounds__(256) void states_kernel(const IO *__restrict__ q,
         vv.w = to_f32(v[tok + c0 + 3]);
         const float d = expf(g[row * H + h]);
         const float bt = beta[row * H + h];
-        __syncthreads();
 
         float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
 #pragma unroll
@@ -95,18 +98,24 @@ __global__ __launch_bounds__(256) void states_kernel(const IO *__restrict__ q,
             b.z += __shfl_xor(b.z, off); b.w += __shfl_xor(b.w, off);
         }
         if (lane < 16) {
-            red_a[w][cg] = a;
-            red_b[w][cg] = b;
+            red_a[rb][w][cg] = a;
+            red_b[rb][w][cg] = b;
         }
         float qk = sq[buf][lane] * sk[buf][lane] + sq[buf][lane + 64] * sk[buf][lane + 64];
 #pragma unroll
         for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off);
+        // the next token's q and k, published by the same barrier
+        if (t + 1 < len && tid < D) {
+            const int nb = static_cast<int>((t + 1) % 3);
+            sq[nb][tid] = to_f32(q[tok + H * D + tid]);
+            sk[nb][tid] = to_f32(k[tok + H * D + tid]);
+        }
         __syncthreads();
 
-        float4 A = red_a[0][cg], Bq = red_b[0][cg];
+        float4 A = red_a[rb][0][cg], Bq = red_b[rb][0][cg];
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) {
-            const float4 x = red_a[ww][cg], y = red_b[ww][cg];
+            const float4 x = red_a[rb][ww][cg], y = red_b[rb][ww][cg];
             A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
             Bq.x += y.x; Bq.y += y.y; Bq.z += y.z; Bq.w += y.w;
         }

@@ -248,3 +248,13 @@ def test_bad_call_raises_without_enqueueing():
     w = inputs.prefill_workload(1, 8, 1, seed=13, device=DEV)
     with pytest.raises(GdnError):
         gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, None, 48)
+
+
+def test_prefill_packed_longest_first_with_ties_and_empty():
+    # a packed batch small enough to be walked longest first, with equal
+    # lengths (ties go by index) and an empty sequence; every sequence in full
+    w = inputs.varlen_workload([64, 5, 64, 0, 5, 200, 130, 64], H=3, seed=71, device=DEV)
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, cu_seqlens=w.cu_seqlens)
+    check_prefill(w, O, S_T, Or, Sr, label="longest first")
+    assert torch.equal(S_T[3], w.S0[3]), "the empty sequence keeps its state"
