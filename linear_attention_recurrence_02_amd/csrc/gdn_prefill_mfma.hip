@@ -39,9 +39,10 @@
 //   * producer waves 4..7 prepare chunk c+1 while the consumers work on chunk
 //     c: the Gram tiles K K^T and K Q^T (exact products of fp16 copies of the
 //     bf16 inputs, fp32 accumulation) with the decay and beta applied on the
-//     accumulators; T_ii by back substitution in fp32 (one block per wave) and
-//     M_ij = T_ii N_ij; and the staging of chunk c+2 (rows prefetched into
-//     registers a period earlier, converted to fp16).
+//     accumulators; T_ii (one block per wave) by the page's exact block
+//     doubling on the matrix cores (or, selectable, by fp32 back
+//     substitution) and M_ij = T_ii N_ij; and the staging of chunk c+2 (rows
+//     prefetched into registers a period earlier, converted to fp16).
 //   Each chunk period has three barrier-separated phases:
 //     1: consumers D, state update (chunk c)  | producers Gram tiles (c+1),
 //                                            |   store V (c+1)
@@ -53,7 +54,13 @@
 //   Each array is written in a phase in which nobody reads it: K, Q and the
 //   per-token scalars are double-buffered, everything else is single.
 //   The two roles run as two separate loops under a wave-uniform branch and
-//   execute the same number of barriers (1 + 3 (nch + 1)).
+//   execute the same number of barriers (1 + 3 (nch + 1)).  Phase 2 is the
+//   producers' critical phase, so they take wave priority in it.
+// Template variants: kGated fuses the block's gated RMS norm into the output
+// step (the gate rows fetched into LDS a period ahead; the consumer waves
+// exchange per-row sums through LDS); kDoubling picks the T_ii method; kRank
+// walks a packed batch longest first (each workgroup ranks the sequence
+// lengths before the roles split, one barrier that both roles execute).
 // Every matrix operand is rounded once to fp16 (11 significant bits); the
 // state, the accumulators and the per-token scalars stay fp32.
 
