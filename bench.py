@@ -148,15 +148,26 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold):
     return dict(units=units, wall_s=wall, gpu_ms=gpu_ms, eager_s=eager, workload=w)
 
 
-def bench_prefill(torch, gdn, w, iters, warmup, gate=None):
+def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
     """The prompt form over workload w; with gate = (z, norm_w, eps) the form
-    with the gated RMS norm on the output (gdn_chunk_prefill_gated)."""
+    with the gated RMS norm on the output (gdn_chunk_prefill_gated); with
+    segment_len the segmented form (gdn_chunk_prefill_segmented; its
+    workspace is allocated before the timed calls)."""
     O = torch.empty_like(w.v)
     N = w.q.shape[0] if w.cu_seqlens is None else w.cu_seqlens.numel() - 1
     S_T = torch.empty((N, w.q.shape[2], DK, DV), dtype=torch.float32, device="cuda")
+    ws = None
+    if segment_len is not None:
+        B_, T_, H_ = w.q.shape[:3]
+        need = gdn.load_library().gdn_chunk_prefill_segmented_workspace(
+            1 if w.q.dtype == torch.bfloat16 else 0, B_, T_, H_, segment_len)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def call():
-        if gate is None:
+        if segment_len is not None:
+            gdn.gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, w.chunk,
+                                            segment_len, workspace=ws, O=O, S_T=S_T)
+        elif gate is None:
             gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
                                   O=O, S_T=S_T)
         else:
@@ -191,7 +202,9 @@ def bench_prefill(torch, gdn, w, iters, warmup, gate=None):
     if gate is not None:
         nbytes += tokens * H * DV * esz          # the gate rows z
     return {
-        "workload": w.name + ("_gated_norm" if gate is not None else ""), "tokens": tokens, "heads": H, "chunk": w.chunk,
+        "workload": w.name + ("_gated_norm" if gate is not None else "")
+                    + (f"_segmented_{segment_len}" if segment_len is not None else ""),
+        "tokens": tokens, "heads": H, "chunk": w.chunk,
         "seconds": t, "tokens_per_s": tokens / t,
         "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
         "alg_flops": flops, "alg_bytes": nbytes,
@@ -412,6 +425,13 @@ def main():
                 f"{r['seconds']*1e3:.3f} ms, MFMA {100*r['mfma_frac']:.1f}%, "
                 f"HBM {100*r['hbm_frac']:.1f}%")
             pre[r["workload"]] = r
+            if w.name == "long_prefill":
+                # the same workload with each sequence cut into 16 segments
+                rs = bench_prefill(torch, gdn, w, args.prefill_iters, 2, segment_len=256)
+                log(f"prefill {rs['workload']}: {rs['tokens_per_s']:.3e} tok/s, "
+                    f"{rs['seconds']*1e3:.3f} ms, MFMA {100*rs['mfma_frac']:.1f}%, "
+                    f"HBM {100*rs['hbm_frac']:.1f}%")
+                pre[rs["workload"]] = rs
             if w.name == "large_prefill":
                 r["roofline"]["traffic"] = read_traffic(
                     "prefill_large", source_digest("gdn_prefill_mfma.hip"))

@@ -139,6 +139,45 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
                          float *S_T, void *stream);
 
 /*
+ * gdn_chunk_prefill_segmented -- gdn_chunk_prefill for a uniform batch, with
+ * each sequence cut into segments of segment_len tokens that are walked in
+ * parallel.  Over a segment the recurrence is affine in the entering state,
+ * S_out = M S_in + B (the prompt form's state update, Qwen3.5-9B-npu model
+ * page, "How it works" -> "Gated DeltaNet on the NPU", composed over the
+ * segment's chunks).  The call runs the prompt form over all segments at once
+ * three times -- for B (from a zero state), for M (with v = 0 from the
+ * identity) and, after a scan S_in(p+1) = M_p S_in(p) + B_p over each
+ * sequence's segments, for O and the end states from the true S_in -- so that
+ * a batch of a few long sequences keeps every CU busy.  The result equals
+ * gdn_chunk_prefill's up to rounding (the scan adds one fp32 product per
+ * segment boundary).
+ *
+ *   q, k, v, g, beta, S0, B, T, H, dk, dv, chunk, O, S_T: as for
+ *               gdn_chunk_prefill with cu_seqlens = NULL (B sequences of T tokens).
+ *   segment_len a positive multiple of chunk; with one segment (T <= segment_len)
+ *               the call is gdn_chunk_prefill and needs no workspace.
+ *   workspace   caller-owned device memory of at least
+ *               gdn_chunk_prefill_segmented_workspace(io_dtype, B, T, H, segment_len)
+ *               bytes, 256-byte aligned, overlapping no argument; its contents
+ *               are scratch between calls.  Calls sharing a workspace must not
+ *               run concurrently.
+ *   workspace_bytes  its size.
+ *   GDN_ERR_INVALID_ARG for a bad segment_len or a missing or short workspace,
+ *   GDN_ERR_ALIAS if it overlaps an argument.
+ */
+int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int io_dtype,
+                                const float *g, const float *beta, const float *S0, int64_t B,
+                                int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                                int64_t segment_len, void *workspace, int64_t workspace_bytes,
+                                void *O, float *S_T, void *stream);
+
+/* Bytes of workspace gdn_chunk_prefill_segmented needs for these sizes (one
+ * state of 64 KiB per segment and head three times, a zero copy of v and the
+ * segment offsets), or -1 if the sizes are invalid. */
+int64_t gdn_chunk_prefill_segmented_workspace(int io_dtype, int64_t B, int64_t T, int64_t H,
+                                              int64_t segment_len);
+
+/*
  * gdn_chunk_prefill_gated -- gdn_chunk_prefill with the gated RMS norm that
  * follows the recurrence in a Gated DeltaNet block (Qwen3.5-4B -- Hexagon NPU
  * (QHexRT) -- v81 page, the opening description of the text decoder: a short

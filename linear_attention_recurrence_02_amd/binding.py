@@ -21,6 +21,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_ex",
+            "gdn_chunk_prefill_segmented", "gdn_chunk_prefill_segmented_workspace",
             "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step")
 GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
 
@@ -59,6 +60,11 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_prefill_ex.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                          i64, i64, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.gdn_chunk_prefill_ex.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_segmented.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64,
+                                                i64, i64, i64, i64, i64, vp, i64, vp, vp, vp]
+    lib.gdn_chunk_prefill_segmented.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_segmented_workspace.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+    lib.gdn_chunk_prefill_segmented_workspace.restype = i64
     lib.gdn_chunk_prefill_gated.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64,
                                             i64, i64, i64, i64, i64, vp, vp, ctypes.c_float,
                                             vp, vp, vp]
@@ -151,6 +157,43 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
         st = load_library().gdn_chunk_prefill(*args, *out)
     else:
         st = load_library().gdn_chunk_prefill_ex(*args, int(inverse), *out)
+    _check(st)
+    return O, S_T
+
+
+def gdn_chunk_prefill_segmented(q, k, v, g, beta, S0=None, chunk=64, segment_len=256, *,
+                                workspace=None, O=None, S_T=None, stream=None):
+    """The prompt form over a uniform batch with each sequence cut into
+    segments walked in parallel (see include/gdn.h).  ``workspace``: a uint8
+    device tensor of at least gdn_chunk_prefill_segmented_workspace bytes, or
+    None to allocate one here.  Returns (O, S_T)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype \
+            or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape [B, T, H, d] and dtype")
+    if g.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("g and beta must be [B, T, H]")
+    lib = load_library()
+    need = lib.gdn_chunk_prefill_segmented_workspace(_io_dtype(q), B, T, H, int(segment_len))
+    if need < 0:
+        raise ValueError("invalid sizes for the segmented prompt form")
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if O is None:
+        O = torch.empty_like(v)
+    if S_T is None:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+    if O.dtype != q.dtype or O.shape != v.shape:
+        raise ValueError("O must match v's shape and dtype")
+    if S_T.shape != (B, H, dk, dv) or (S0 is not None and S0.shape != (B, H, dk, dv)):
+        raise ValueError("S0 / S_T must be [B, H, dk, dv]")
+    st = lib.gdn_chunk_prefill_segmented(
+        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+        _ptr(S0, torch.float32, "S0"), B, T, H, dk, dv, int(chunk), int(segment_len),
+        _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+        _ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
     _check(st)
     return O, S_T
 

@@ -102,9 +102,95 @@ int launch_prefill(const gdn::PrefillArgs &a, void *stream) {
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+// Workspace of the segmented prompt form: the refined offsets, a zero copy
+// of v, and three arrays of one state per (segment, head).  Offsets are
+// 256-byte aligned; returns the total, or -1 for sizes it cannot hold.
+struct SegLayout {
+    int64_t P, cu, vzero, vzero_bytes, s1, m, b, total;
+};
+
+bool seg_layout(int io_dtype, int64_t N, int64_t T, int64_t H, int64_t L, SegLayout &w) {
+    if (!dims_ok(N) || !dims_ok(T) || H <= 0 || H >= 65536 || L <= 0) return false;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return false;
+    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
+    w.P = T == 0 ? 1 : (T + L - 1) / L;
+    const int64_t units = N * w.P * H;
+    if (N * w.P >= kMaxDim || units >= kMaxDim) return false;
+    if (N * T > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return false;
+    auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t state = gdn::kHeadDim * gdn::kHeadDim * 4;
+    w.cu = 0;
+    w.vzero = up((N * w.P + 1) * 4);
+    w.vzero_bytes = up(N * T * H * gdn::kHeadDim * esz);
+    w.s1 = w.vzero + w.vzero_bytes;
+    w.m = w.s1 + up(units * state);
+    w.b = w.m + up(units * state);
+    w.total = w.b + up(units * state);
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+int64_t gdn_chunk_prefill_segmented_workspace(int io_dtype, int64_t B, int64_t T, int64_t H,
+                                              int64_t segment_len) {
+    SegLayout w;
+    return seg_layout(io_dtype, B, T, H, segment_len, w) ? w.total : -1;
+}
+
+int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int io_dtype,
+                                const float *g, const float *beta, const float *S0, int64_t B,
+                                int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                                int64_t segment_len, void *workspace, int64_t workspace_bytes,
+                                void *O, float *S_T, void *stream) {
+    gdn::PrefillArgs a{};
+    int64_t tok_bytes = 0;
+    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, nullptr, B, T, H, dk, dv, chunk,
+                                 O, S_T, a, tok_bytes);
+    if (st != GDN_OK) return st;
+    if (segment_len <= 0 || segment_len % chunk != 0) return GDN_ERR_INVALID_ARG;
+    SegLayout w;
+    if (!seg_layout(io_dtype, B, T, H, segment_len, w)) return GDN_ERR_INVALID_ARG;
+    if (w.P == 1 || B == 0) return launch_prefill(a, stream);   // one segment: the plain form
+    if (!workspace || workspace_bytes < w.total || !aligned(workspace, 256))
+        return GDN_ERR_INVALID_ARG;
+    const int64_t gb = B * T * H * 4, st_bytes = B * H * gdn::kHeadDim * gdn::kHeadDim * 4;
+    const Range rw = span_of(workspace, w.total);
+    for (Range r : {span_of(q, tok_bytes), span_of(k, tok_bytes), span_of(v, tok_bytes),
+                    span_of(g, gb), span_of(beta, gb), span_of(O, tok_bytes),
+                    span_of(S_T, st_bytes), S0 ? span_of(S0, st_bytes) : Range{0, 0}})
+        if (overlap(rw, r)) return GDN_ERR_ALIAS;
+
+    char *ws = static_cast<char *>(workspace);
+    int32_t *cu = reinterpret_cast<int32_t *>(ws + w.cu);
+    void *vzero = ws + w.vzero;
+    float *s1 = reinterpret_cast<float *>(ws + w.s1);   // identity states, then S_in
+    float *m = reinterpret_cast<float *>(ws + w.m);     // state maps
+    float *b = reinterpret_cast<float *>(ws + w.b);     // zero-start states, then end states
+    const int64_t Ns = B * w.P;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto run = [&](const void *vv, const float *s0, float *st_out) {
+        gdn::PrefillArgs r = a;
+        r.v = vv;
+        r.S0 = s0;
+        r.S_T = st_out;
+        r.cu_seqlens = cu;
+        r.N = Ns;
+        r.T = B * T;
+        return launch_prefill(r, stream);
+    };
+    if (gdn::launch_segment_init(cu, B, T, w.P, segment_len, vzero, w.vzero_bytes, s1, Ns * H, s) !=
+        hipSuccess)
+        return GDN_ERR_HIP;
+    int rc = run(v, nullptr, b);                       // B: each segment from zero
+    if (rc == GDN_OK) rc = run(vzero, s1, m);          // M: V = 0 from the identity
+    if (rc != GDN_OK) return rc;
+    if (gdn::launch_segment_scan(m, b, S0, s1, B, H, w.P, s) != hipSuccess) return GDN_ERR_HIP;
+    rc = run(v, s1, b);                                // O and the end states from S_in
+    if (rc != GDN_OK) return rc;
+    return gdn::launch_segment_gather(b, S_T, B, H, w.P, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
 
 int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
                       const float *g, const float *beta, const float *S0,

@@ -130,6 +130,32 @@ def test_prefill_ex_validation(lib):
         assert ex(inv, N=0) == binding.GDN_OK
 
 
+def test_prefill_segmented_validation(lib):
+    W = A + 2048 * MB
+    need = lib.gdn_chunk_prefill_segmented_workspace(1, 2, 1000, 2, 256)
+    # 2 x 4 segments x 2 heads x 64 KiB three times, a zero copy of v, the offsets
+    assert need >= 3 * 16 * 65536 + 2 * 1000 * 2 * 256
+    assert lib.gdn_chunk_prefill_segmented_workspace(1, 2, 1000, 2, 0) == -1
+    assert lib.gdn_chunk_prefill_segmented_workspace(7, 2, 1000, 2, 256) == -1
+
+    def seg(**kw):
+        a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB, beta=A + 200 * MB,
+                 S0=A + 256 * MB, B=2, T=1000, H=2, chunk=64, L=256, ws=W, wsb=need,
+                 O=A + 512 * MB, S_T=A + 768 * MB)
+        a.update(kw)
+        return lib.gdn_chunk_prefill_segmented(a["q"], a["k"], a["v"], a["dtype"], a["g"],
+                                               a["beta"], a["S0"], a["B"], a["T"], a["H"], 128,
+                                               128, a["chunk"], a["L"], a["ws"], a["wsb"], a["O"],
+                                               a["S_T"], None)
+    assert seg(L=100) == binding.GDN_ERR_INVALID_ARG               # not a multiple of chunk
+    assert seg(ws=None) == binding.GDN_ERR_INVALID_ARG
+    assert seg(wsb=need - 1) == binding.GDN_ERR_INVALID_ARG
+    assert seg(ws=W + 16) == binding.GDN_ERR_INVALID_ARG            # not 256-byte aligned
+    assert seg(ws=A + 128 * MB + 4096) == binding.GDN_ERR_ALIAS    # workspace over v
+    assert seg(q=None) == binding.GDN_ERR_INVALID_ARG
+    assert seg(B=0) == binding.GDN_OK
+
+
 def gated(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB,
           beta=A + 200 * MB, S0=A + 256 * MB, cu=None, N=2, T=64, H=2, dk=128,
           dv=128, chunk=64, z=A + 1024 * MB, w=A + 1100 * MB, eps=1e-6, Y=A + 512 * MB,
