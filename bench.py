@@ -414,6 +414,18 @@ def main():
         }
         log(f"decode: {state_gbs:.1f} GB/s state, {avg_launch*1e6:.2f} us/step "
             f"(eager {dec['eager_s']*1e6/K:.2f} us/step)")
+        if not args.cold:
+            # the same steps over eight state batches in turn (512 MiB, twice the
+            # last-level cache), so that every step reads its state from HBM
+            cold = bench_decode(torch, gdn, inputs, K, args.warmup, True)
+            cold_launch = cold["gpu_ms"] / 1e3 / K
+            result["decode"]["cold_avg_launch_us"] = cold_launch * 1e6
+            result["decode"]["cold_state_gbs"] = K * units * 2 * STATE_BYTES / cold["wall_s"] / 1e9
+            result["decode"]["cold_hbm_frac"] = alg / cold_launch / HBM_PEAK
+            log(f"decode, 8 rotating state batches: {cold_launch*1e6:.2f} us/step, "
+                f"HBM {100*alg/cold_launch/HBM_PEAK:.1f}%")
+            del cold
+            torch.cuda.empty_cache()
 
     if args.only in (None, "prefill"):
         pre = {}
