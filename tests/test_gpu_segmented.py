@@ -45,15 +45,16 @@ def test_long_workload_segmented():
     check(w, O, S_T, "long, 16 segments")
 
 
-@pytest.mark.parametrize("L", [64, 256, 512])
-def test_slow_decay_carries_state_across_segments(L):
+@pytest.mark.parametrize("T,L", [(1000, 64), (1000, 256), (1000, 384), (1000, 512), (2100, 64)])
+def test_slow_decay_carries_state_across_segments(T, L):
     # decay slow enough that the state entering each segment matters; the last
-    # segment is partial
-    w = inputs.prefill_workload(2, 1000, 2, chunk=64, seed=81, device=DEV)
+    # segment is partial.  Segment counts 16, 4, 3, 2 and 33: the scan's
+    # step count P - 1 both odd and even
+    w = inputs.prefill_workload(2, T, 2, chunk=64, seed=81, device=DEV)
     w.g.mul_(0.02)
     O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, 64, L)
     torch.cuda.synchronize()
-    check(w, O, S_T, f"slow decay, segments of {L}")
+    check(w, O, S_T, f"slow decay, T={T}, segments of {L}")
 
 
 def test_fp32_vector_kernel_segments():
