@@ -97,8 +97,9 @@ int check_prefill(const void *q, const void *k, const void *v, int io_dtype, con
 int launch_prefill(const gdn::PrefillArgs &a, void *stream) {
     if (a.N == 0) return GDN_OK;   // nothing to do
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = gdn::prefill_mfma_supports(a) ? gdn::launch_prefill_mfma(a, s)
-                                                 : gdn::launch_prefill_valu(a, s);
+    hipError_t e = gdn::prefill_short_pays(a)     ? gdn::launch_prefill_short(a, s)
+                   : gdn::prefill_mfma_supports(a) ? gdn::launch_prefill_mfma(a, s)
+                                                   : gdn::launch_prefill_valu(a, s);
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
@@ -217,9 +218,11 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
     const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
                                  dv, chunk, O, S_T, a, tok_bytes);
     if (st != GDN_OK) return st;
-    if (inverse != GDN_INVERSE_DEFAULT)
+    if (inverse != GDN_INVERSE_DEFAULT) {
         a.inverse = inverse == GDN_INVERSE_DOUBLING ? gdn::kInverseDoubling
                                                     : gdn::kInverseSubstitution;
+        a.short_ok = false;
+    }
     return launch_prefill(a, stream);
 }
 

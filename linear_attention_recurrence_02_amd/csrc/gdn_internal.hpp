@@ -35,6 +35,9 @@ struct PrefillArgs {
     // How the matrix-core kernel forms the diagonal 16 x 16 blocks of
     // (I + N)^-1 (the vector kernel always substitutes column by column).
     int inverse = kInverseDoubling;
+    // Whether a batch of short sequences may take the 16-token kernel (off
+    // when the caller names the matrix-core kernel's inverse method).
+    bool short_ok = true;
 };
 
 struct DecodeArgs {
@@ -74,6 +77,8 @@ hipError_t launch_preop(const PreopArgs &p, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
 bool prefill_mfma_supports(const PrefillArgs &a);
+hipError_t launch_prefill_short(const PrefillArgs &a, hipStream_t stream);
+bool prefill_short_pays(const PrefillArgs &a);
 // The prompt form keeping the state after every token in S_tok (chunk unused).
 hipError_t launch_prefill_states(const PrefillArgs &a, float *S_tok, hipStream_t stream);
 

@@ -1,0 +1,108 @@
+// Matrix-core helpers shared by the prompt-form kernels: operand types, the
+// gfx950 fp16 products, conversions, the LDS transpose load and DPP prefix
+// sums.  Internal to libgdn; every function is inlined into its kernel.
+#pragma once
+
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+typedef _Float16 f16;
+typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16;
+typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ f16x4 zh4() {
+    const f16 z = static_cast<f16>(0.f);
+    return f16x4{z, z, z, z};
+}
+__device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+__device__ __forceinline__ f16x4 h4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+__device__ __forceinline__ f32x4 f4(f16x4 x) { return __builtin_convertvector(x, f32x4); }
+__device__ __forceinline__ f16x4 neg(f16x4 x) {
+    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(f16x4, __builtin_bit_cast(u32x2, x) ^ 0x80008000u);
+}
+__device__ __forceinline__ f16x4 rd4(const f16 *p) { return *reinterpret_cast<const f16x4 *>(p); }
+__device__ __forceinline__ f16x8 rd8(const f16 *p) { return *reinterpret_cast<const f16x8 *>(p); }
+
+// Hide a lane index from loop-invariant code motion: values derived from it
+// are then recomputed in each period instead of being held in registers across
+// the whole chunk loop.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// Scheduling barrier: the compiler moves no instruction across it, so the
+// reads issued above it overlap the products issued below it.
+__device__ __forceinline__ void fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// LDS transpose load: in each group of 16 lanes, lane L passes the address of
+// halves 4(L%4)..+3 of row L/4 of a 4 x 16 block and receives column L of the
+// block (its 4 rows in order).
+__device__ __forceinline__ f16x4 rd_tr(const f16 *p) {
+    typedef __fp16 v4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+    typedef __attribute__((address_space(3))) v4 lds_v4;
+    return __builtin_bit_cast(f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_v4 *)(p)));
+}
+
+// Eight bf16 (one 16-byte load) to fp16; bf16 values inside the fp16 range are
+// exact in fp16.
+__device__ __forceinline__ f16x8 bf_to_h8(f32x4 raw) {
+    const u32x4 w = __builtin_bit_cast(u32x4, raw);
+    f16x8 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        r[2 * i] = static_cast<f16>(__uint_as_float(w[i] << 16));
+        r[2 * i + 1] = static_cast<f16>(__uint_as_float(w[i] & 0xffff0000u));
+    }
+    return r;
+}
+
+// The K = 16 product (one 16 x 16 tile, four k per lane group: lane l holds
+// A[l % 16][4 (l / 16) ..+3] and B[4 (l / 16) ..+3][l % 16]; the result lane
+// holds rows 4 (l / 16) ..+3 of column l % 16).
+__device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts
+// within each row of 16 lanes, then the last lane of row 0 (of rows 0..1) is
+// added to rows 1 and 3 (rows 2 and 3).  Lanes a shift leaves without a source
+// add zero.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true);
+    return v + __builtin_bit_cast(float, t);
+}
+__device__ __forceinline__ float wave_prefix_sum(float x) {
+    x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_add<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+    x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
+    return x;
+}
+// Inclusive prefix sum within each row of 16 lanes.
+__device__ __forceinline__ float row16_prefix_sum(float x) {
+    x = dpp_add<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_add<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_add<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_add<0x118, 0xf>(x);   // row_shr:8
+    return x;
+}
+
+}  // namespace
+}  // namespace gdn
