@@ -14,8 +14,10 @@ does not pace the GPU.  `value` is the state traffic those K steps move
 The same run times the prompt form (gdn_chunk_prefill) on the large prefill
 (B=8, H=32, T=16384, chunk 64, bf16, zero S0) and on the long, packed
 variable-length and speculative-verify workloads, and reports their tokens/s
-and roofline fractions under "prefill".  All inputs are seeded synthetic draws
-made on the device before any timing starts.
+and roofline fractions under "prefill".  Each such figure is the median over
+three runs of --prefill-iters back-to-back calls between one pair of events,
+so that the host's launch work overlaps the GPU's.  All inputs are seeded
+synthetic draws made on the device before any timing starts.
 
 The CPU oracle is timed on a bounded sample of the decode workload (and of the
 large prefill) on this host's cores as `cpu_baseline`; it is a reported
@@ -148,6 +150,22 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold):
     return dict(units=units, wall_s=wall, gpu_ms=gpu_ms, eager_s=eager, workload=w)
 
 
+def time_calls(torch, call, iters, reps=3):
+    """Seconds per call: ``iters`` calls back to back between one pair of events
+    on the current stream (so that the host's launch work overlaps the GPU's),
+    the median over ``reps`` such runs."""
+    per_call = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            call()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) / 1e3 / iters)
+    return statistics.median(per_call)
+
+
 def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
     """The prompt form over workload w; with gate = (z, norm_w, eps) the form
     with the gated RMS norm on the output (gdn_chunk_prefill_gated); with
@@ -181,15 +199,7 @@ def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
         call()
         torch.cuda.synchronize()
         n += 1
-    times = []
-    for _ in range(iters):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / 1e3)
-    t = statistics.median(times)
+    t = time_calls(torch, call, iters)
     H = w.q.shape[2]
     if w.cu_seqlens is None:
         lengths = [w.q.shape[1]] * w.q.shape[0]
@@ -226,16 +236,9 @@ def bench_states(torch, gdn, w, iters):
                                S_tok=S_tok)
         torch.cuda.synchronize()
         n += 1
-    times = []
-    for _ in range(iters):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        gdn.gdn_prefill_states(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, O=O,
-                               S_tok=S_tok)
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / 1e3)
-    t = statistics.median(times)
+    t = time_calls(torch, lambda: gdn.gdn_prefill_states(w.q, w.k, w.v, w.g, w.beta, w.S0,
+                                                         w.cu_seqlens, O=O, S_tok=S_tok),
+                   iters)
     rows = B * T
     nseq = len(w.meta["lengths"]) if w.cu_seqlens is not None else B
     esz = w.q.element_size()
@@ -267,15 +270,7 @@ def bench_preop(torch, gdn, p, iters):
         call()
         torch.cuda.synchronize()
         n += 1
-    times = []
-    for _ in range(iters):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1) / 1e3)
-    t = statistics.median(times)
+    t = time_calls(torch, call, iters)
     rows = B * T
     esz = p.xq.element_size()
     # projections in and q/k/v out, gate inputs in and g/beta out, plus each
@@ -345,7 +340,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--prefill-iters", type=int, default=5)
+    ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--cold", action="store_true",
                     help="rotate 8 state batches (512 MiB) so the state cannot stay in cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -437,6 +432,10 @@ def main():
                 f"{r['seconds']*1e3:.3f} ms, MFMA {100*r['mfma_frac']:.1f}%, "
                 f"HBM {100*r['hbm_frac']:.1f}%")
             pre[r["workload"]] = r
+            if w.name == "verify":
+                r["roofline"]["traffic"] = read_traffic(
+                    "prefill_short_verify",
+                    source_digest("gdn_prefill_short.hip", "gdn_mfma.hpp"))
             if w.name == "long_prefill":
                 # the same workload with each sequence cut into 16 segments
                 rs = bench_prefill(torch, gdn, w, args.prefill_iters, 2, segment_len=256)
@@ -446,14 +445,14 @@ def main():
                 pre[rs["workload"]] = rs
             if w.name == "large_prefill":
                 r["roofline"]["traffic"] = read_traffic(
-                    "prefill_large", source_digest("gdn_prefill_mfma.hip"))
+                    "prefill_large", source_digest("gdn_prefill_mfma.hip", "gdn_mfma.hpp"))
                 if not args.no_cpu_baseline:
                     r["cpu_baseline"] = cpu_baseline_prefill(w)
                 # the same workload with the gated RMS norm fused on the output
                 rg = bench_prefill(torch, gdn, w, args.prefill_iters, 2,
                                    gate=inputs.norm_gate(w))
                 rg["roofline"]["traffic"] = read_traffic(
-                    "prefill_large_gated", source_digest("gdn_prefill_mfma.hip"))
+                    "prefill_large_gated", source_digest("gdn_prefill_mfma.hip", "gdn_mfma.hpp"))
                 log(f"prefill {rg['workload']}: {rg['tokens_per_s']:.3e} tok/s, "
                     f"{rg['seconds']*1e3:.3f} ms, HBM {100*rg['hbm_frac']:.1f}%")
                 pre[rg["workload"]] = rg
