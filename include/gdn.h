@@ -101,7 +101,11 @@ const char *gdn_status_string(int status);
  *               wrong results, never an out-of-bounds access.  Zero-length
  *               sequences are allowed (S_T[n] = S0[n], no rows of O).
  *   chunk       16, 32 or 64 (the page's prompt-block sizes); the result does
- *               not depend on it beyond rounding.
+ *               not depend on it beyond rounding, so it is a tiling choice.  A
+ *               bf16 batch of short sequences (at most 16 tokens per sequence
+ *               on average: T <= 16 for a uniform batch, T <= 16 N for a packed
+ *               one, as in a speculative verify pass) is tiled by 16 whatever
+ *               the chunk, on a kernel that runs two sequence-heads per CU.
  *   O           same shape and dtype as v; rows of the call's tokens are all
  *               written.
  *   S_T         [N, H, 128, 128] fp32, the state after each sequence's last
@@ -126,8 +130,10 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
  * (GDN_INVERSE_DOUBLING) and applies the block structure above it by block
  * forward substitution.  GDN_INVERSE_SUBSTITUTION forms the diagonal blocks by
  * fp32 back substitution instead.  Both reach the same result up to rounding.
- * The choice applies to bf16 inputs at chunk 64 (the matrix-core kernel); the
- * other configurations substitute column by column and ignore it.
+ * The choice applies to bf16 inputs at chunk 64 (the matrix-core kernel), and
+ * naming it keeps such calls on that kernel even for batches of short
+ * sequences; the other configurations substitute column by column and ignore
+ * it.
  *
  *   inverse     a gdn_inverse value (else GDN_ERR_UNSUPPORTED).
  *   Every other argument: as for gdn_chunk_prefill.
