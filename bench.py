@@ -103,7 +103,7 @@ def read_traffic(kernel_tag, digest):
         return None
 
 
-def bench_decode(torch, gdn, inputs, steps, warmup, cold):
+def bench_decode(torch, gdn, inputs, steps, warmup, cold, streaming=False):
     w = inputs.batched_decode(device="cuda", steps=steps)
     B, H = w.meta["B"], w.meta["H"]
     units = B * H
@@ -114,7 +114,8 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold):
     scratch = w.S0.clone()
     for i in range(warmup):
         s = i % steps
-        gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], scratch, o=outs[s])
+        gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], scratch, o=outs[s],
+                            streaming=streaming)
     torch.cuda.synchronize()
     # capture the K steps once
     graph = torch.cuda.CUDAGraph()
@@ -122,7 +123,7 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold):
     with torch.cuda.graph(graph, stream=cap):
         for s in range(steps):
             gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s],
-                                states[s % nbuf], o=outs[s])
+                                states[s % nbuf], o=outs[s], streaming=streaming)
     torch.cuda.synchronize()
     graph.replay()          # untimed replay (first-replay setup cost)
     torch.cuda.synchronize()
@@ -144,7 +145,7 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold):
     t1 = time.perf_counter()
     for s in range(steps):
         gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], states[s % nbuf],
-                            o=outs[s])
+                            o=outs[s], streaming=streaming)
     torch.cuda.synchronize()
     eager = time.perf_counter() - t1
     return dict(units=units, wall_s=wall, gpu_ms=gpu_ms, eager_s=eager, workload=w)
@@ -343,6 +344,9 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=10)
     ap.add_argument("--cold", action="store_true",
                     help="rotate 8 state batches (512 MiB) so the state cannot stay in cache")
+    ap.add_argument("--streaming", action="store_true",
+                    help="time the decode with non-temporal state loads and stores "
+                         "(gdn_decode_step_ex, GDN_STATE_STREAMING)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -390,7 +394,8 @@ def main():
     dec = None
     if args.only in (None, "decode"):
         log("decode: generating inputs and capturing the step graph ...")
-        dec = bench_decode(torch, gdn, inputs, args.steps, args.warmup, args.cold)
+        dec = bench_decode(torch, gdn, inputs, args.steps, args.warmup, args.cold,
+                           args.streaming)
         K = args.steps
         units = dec["units"]
         state_gbs = K * units * 2 * STATE_BYTES / dec["wall_s"] / 1e9
@@ -406,21 +411,28 @@ def main():
             "alg_bytes_per_launch": alg,
             "eager_launch_state_gbs": K * units * 2 * STATE_BYTES / dec["eager_s"] / 1e9,
             "cold_rotating_8_batches": bool(args.cold),
+            "streaming_state": bool(args.streaming),
         }
         log(f"decode: {state_gbs:.1f} GB/s state, {avg_launch*1e6:.2f} us/step "
             f"(eager {dec['eager_s']*1e6/K:.2f} us/step)")
-        if not args.cold:
+        if not args.cold and not args.streaming:
             # the same steps over eight state batches in turn (512 MiB, twice the
-            # last-level cache), so that every step reads its state from HBM
-            cold = bench_decode(torch, gdn, inputs, K, args.warmup, True)
-            cold_launch = cold["gpu_ms"] / 1e3 / K
-            result["decode"]["cold_avg_launch_us"] = cold_launch * 1e6
-            result["decode"]["cold_state_gbs"] = K * units * 2 * STATE_BYTES / cold["wall_s"] / 1e9
-            result["decode"]["cold_hbm_frac"] = alg / cold_launch / HBM_PEAK
-            log(f"decode, 8 rotating state batches: {cold_launch*1e6:.2f} us/step, "
-                f"HBM {100*alg/cold_launch/HBM_PEAK:.1f}%")
-            del cold
-            torch.cuda.empty_cache()
+            # last-level cache), so that every step reads its state from HBM;
+            # with plain and with non-temporal state access, and the latter on
+            # the one batch too
+            for tag, cold_, streaming_ in (("cold", True, False),
+                                           ("cold_streaming", True, True),
+                                           ("streaming", False, True)):
+                r_ = bench_decode(torch, gdn, inputs, K, args.warmup, cold_, streaming_)
+                launch = r_["gpu_ms"] / 1e3 / K
+                result["decode"][f"{tag}_avg_launch_us"] = launch * 1e6
+                result["decode"][f"{tag}_state_gbs"] = K * units * 2 * STATE_BYTES / r_["wall_s"] / 1e9
+                result["decode"][f"{tag}_hbm_frac"] = alg / launch / HBM_PEAK
+                log(f"decode, {'8 rotating state batches' if cold_ else 'one batch'}"
+                    f"{', non-temporal state' if streaming_ else ''}: {launch*1e6:.2f} us/step, "
+                    f"HBM {100*alg/launch/HBM_PEAK:.1f}%")
+                del r_
+                torch.cuda.empty_cache()
 
     if args.only in (None, "prefill"):
         pre = {}

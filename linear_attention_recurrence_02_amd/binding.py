@@ -22,8 +22,10 @@ GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = r
 GDN_F32, GDN_BF16 = 0, 1
 EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_ex",
             "gdn_chunk_prefill_segmented", "gdn_chunk_prefill_segmented_workspace",
-            "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step")
+            "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step",
+            "gdn_decode_step_ex")
 GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
+GDN_STATE_CACHED, GDN_STATE_STREAMING = 0, 1
 
 _lib = None
 
@@ -75,6 +77,9 @@ def load_library(path: Optional[str] = None):
     lib.gdn_decode_step.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i64,
                                     i64, vp, vp]
     lib.gdn_decode_step.restype = ctypes.c_int
+    lib.gdn_decode_step_ex.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i64,
+                                       i64, ctypes.c_int, vp, vp]
+    lib.gdn_decode_step_ex.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -314,9 +319,12 @@ def gdn_prefill_states(q, k, v, g, beta, S0=None, cu_seqlens=None, *, O=None, S_
     return O, S_tok
 
 
-def gdn_decode_step(q, k, v, g, beta, S, *, o=None, stream=None):
+def gdn_decode_step(q, k, v, g, beta, S, *, o=None, stream=None, streaming=False):
     """One token for each of B x H states, S [B, H, 128, 128] fp32 updated in
-    place.  q, k, v: [B, H, 128]; g, beta: [B, H] fp32.  Returns o [B, H, 128]."""
+    place.  q, k, v: [B, H, 128]; g, beta: [B, H] fp32.  Returns o [B, H, 128].
+    streaming=True moves the state with non-temporal loads and stores
+    (gdn_decode_step_ex with GDN_STATE_STREAMING): same result, faster when
+    the state is not in cache."""
     B, H, dk = q.shape
     dv = v.shape[-1]
     if k.shape != q.shape or v.shape[:2] != (B, H) or k.dtype != q.dtype \
@@ -326,9 +334,13 @@ def gdn_decode_step(q, k, v, g, beta, S, *, o=None, stream=None):
         raise ValueError("g, beta must be [B, H]; S [B, H, dk, dv]")
     if o is None:
         o = torch.empty_like(v)
-    st = load_library().gdn_decode_step(
-        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
-        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
-        _ptr(S, torch.float32, "S"), B, H, dk, dv, _ptr(o, q.dtype, "o"), _stream(stream))
+    args = (_ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+            _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+            _ptr(S, torch.float32, "S"), B, H, dk, dv)
+    tail = (_ptr(o, q.dtype, "o"), _stream(stream))
+    if streaming:
+        st = load_library().gdn_decode_step_ex(*args, GDN_STATE_STREAMING, *tail)
+    else:
+        st = load_library().gdn_decode_step(*args, *tail)
     _check(st)
     return o

@@ -348,9 +348,10 @@ int gdn_preop(const void *xq, const void *xk, const void *xv, int io_dtype, cons
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
-                    const float *g, const float *beta, float *S, int64_t B,
-                    int64_t H, int64_t dk, int64_t dv, void *o, void *stream) {
+namespace {
+int decode_step(const void *q, const void *k, const void *v, int io_dtype, const float *g,
+                const float *beta, float *S, int64_t B, int64_t H, int64_t dk, int64_t dv,
+                void *o, bool stream_state, void *stream) {
     if (!q || !k || !v || !g || !beta || !S || !o) return GDN_ERR_INVALID_ARG;
     if (!dims_ok(B) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
     if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
@@ -372,8 +373,26 @@ int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
         if (overlap(rS, r)) return GDN_ERR_ALIAS;
     if (units == 0) return GDN_OK;
     gdn::DecodeArgs a{q, k, v, g, beta, S, units, io_dtype == GDN_BF16, o};
+    a.stream_state = stream_state;
     hipError_t e = gdn::launch_decode(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+}  // namespace
+
+int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
+                    const float *g, const float *beta, float *S, int64_t B,
+                    int64_t H, int64_t dk, int64_t dv, void *o, void *stream) {
+    return decode_step(q, k, v, io_dtype, g, beta, S, B, H, dk, dv, o, false, stream);
+}
+
+int gdn_decode_step_ex(const void *q, const void *k, const void *v, int io_dtype,
+                       const float *g, const float *beta, float *S, int64_t B,
+                       int64_t H, int64_t dk, int64_t dv, int state_hint, void *o,
+                       void *stream) {
+    if (state_hint != GDN_STATE_CACHED && state_hint != GDN_STATE_STREAMING)
+        return GDN_ERR_UNSUPPORTED;
+    return decode_step(q, k, v, io_dtype, g, beta, S, B, H, dk, dv, o,
+                       state_hint == GDN_STATE_STREAMING, stream);
 }
 
 }  // extern "C"

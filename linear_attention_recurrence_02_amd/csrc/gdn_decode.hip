@@ -15,14 +15,37 @@
 // loads are issued before any arithmetic; the column sums a and b are reduced
 // over the 16 row phases (lanes l, l^16, l^32 by cross-lane swaps, then the 4
 // waves through LDS), after which each thread writes its rows back with
-// 16-byte stores.
+// 16-byte stores.  kStream marks the state loads and stores non-temporal,
+// which streams state that is not in cache faster (the plain form keeps a
+// small batch stepped over and over in the last-level cache).
 
 #include "gdn_internal.hpp"
 
 namespace gdn {
 namespace {
 
-template <typename IO>
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+template <bool kStream>
+__device__ __forceinline__ float4 load_state(const float *p) {
+    if constexpr (kStream) {
+        const f32x4v t = __builtin_nontemporal_load(reinterpret_cast<const f32x4v *>(p));
+        return make_float4(t.x, t.y, t.z, t.w);
+    } else {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+}
+template <bool kStream>
+__device__ __forceinline__ void store_state(float *p, float4 x) {
+    if constexpr (kStream) {
+        const f32x4v t = {x.x, x.y, x.z, x.w};
+        __builtin_nontemporal_store(t, reinterpret_cast<f32x4v *>(p));
+    } else {
+        *reinterpret_cast<float4 *>(p) = x;
+    }
+}
+
+template <typename IO, bool kStream>
 __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
                                                      const IO *__restrict__ k,
                                                      const IO *__restrict__ v,
@@ -44,7 +67,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
     float4 s[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-        s[m] = *reinterpret_cast<const float4 *>(Su + (rp + 16 * m) * kHeadDim + 4 * cg);
+        s[m] = load_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 4 * cg);
 
     if (tid < kHeadDim) {
         sq[tid] = to_f32(q[u * kHeadDim + tid]);
@@ -105,7 +128,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
         x.y = d * x.y + kr * dl.y;
         x.z = d * x.z + kr * dl.z;
         x.w = d * x.w + kr * dl.w;
-        *reinterpret_cast<float4 *>(Su + (rp + 16 * m) * kHeadDim + 4 * cg) = x;
+        store_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 4 * cg, x);
     }
     if (rp == 0) {
         IO *ou = o + u * kHeadDim + c0;
@@ -118,18 +141,20 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+template <typename IO>
+void launch_decode_io(const DecodeArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(2 * a.units)), block(256);
-    if (a.bf16) {
-        using T = __hip_bfloat16;
-        decode_kernel<T><<<grid, block, 0, stream>>>(
-            static_cast<const T *>(a.q), static_cast<const T *>(a.k),
-            static_cast<const T *>(a.v), a.g, a.beta, a.S, static_cast<T *>(a.o));
-    } else {
-        decode_kernel<float><<<grid, block, 0, stream>>>(
-            static_cast<const float *>(a.q), static_cast<const float *>(a.k),
-            static_cast<const float *>(a.v), a.g, a.beta, a.S, static_cast<float *>(a.o));
-    }
+    auto kern = a.stream_state ? decode_kernel<IO, true> : decode_kernel<IO, false>;
+    kern<<<grid, block, 0, stream>>>(static_cast<const IO *>(a.q), static_cast<const IO *>(a.k),
+                                     static_cast<const IO *>(a.v), a.g, a.beta, a.S,
+                                     static_cast<IO *>(a.o));
+}
+
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
+    if (a.bf16)
+        launch_decode_io<__hip_bfloat16>(a, stream);
+    else
+        launch_decode_io<float>(a, stream);
     return hipGetLastError();
 }
 

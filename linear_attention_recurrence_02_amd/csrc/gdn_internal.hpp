@@ -47,6 +47,10 @@ struct DecodeArgs {
     int64_t units;              // B * H
     bool bf16;
     void *o;
+    // Non-temporal state loads and stores: for states that are not in cache
+    // anyway (many layers or batches in turn), at the cost of the cache
+    // benefit when one small batch is stepped over and over.
+    bool stream_state = false;
 };
 
 // A validated pre-operation call (conv FIFO, silu, L2 norm, gates).

@@ -226,6 +226,25 @@ def test_decode_rejects_bad_calls(lib):
     assert decode(lib, B=0) == binding.GDN_OK
 
 
+def test_decode_ex_validation(lib):
+    def ex(hint, **kw):
+        a = dict(q=A, k=A + MB, v=A + 2 * MB, dtype=1, g=A + 3 * MB, beta=A + 4 * MB,
+                 S=A + 8 * MB, B=4, H=2, dk=128, dv=128, o=A + 64 * MB)
+        a.update(kw)
+        return lib.gdn_decode_step_ex(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"],
+                                      a["S"], a["B"], a["H"], a["dk"], a["dv"], hint, a["o"],
+                                      None)
+    # an unknown hint is refused before any other check or launch
+    assert ex(2) == binding.GDN_ERR_UNSUPPORTED
+    assert ex(-1) == binding.GDN_ERR_UNSUPPORTED
+    # the rest validates exactly as gdn_decode_step
+    for hint in (binding.GDN_STATE_CACHED, binding.GDN_STATE_STREAMING):
+        assert ex(hint, S=None) == binding.GDN_ERR_INVALID_ARG
+        assert ex(hint, dk=64) == binding.GDN_ERR_UNSUPPORTED
+        assert ex(hint, o=A + 8 * MB) == binding.GDN_ERR_ALIAS
+        assert ex(hint, B=0) == binding.GDN_OK
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(1, 4, 1, 128)

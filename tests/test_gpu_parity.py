@@ -155,6 +155,20 @@ def test_decode_fp32_io():
 
 # --- edge cases --------------------------------------------------------------
 
+@pytest.mark.parametrize("io_dtype", [torch.bfloat16, torch.float32])
+def test_streaming_decode_matches_cached_bit_for_bit(io_dtype):
+    # gdn_decode_step_ex(GDN_STATE_STREAMING) changes only how the state is
+    # moved: 20 steps of the batched-decode shape give the same o and S
+    w = inputs.decode_workload(20, 64, 16, io_dtype=io_dtype, seed=11, device=DEV)
+    S1, S2 = w.S0.clone(), w.S0.clone()
+    for s in range(20):
+        o1 = gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], S1)
+        o2 = gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s], S2, streaming=True)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2), s
+    assert torch.equal(S1, S2)
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64])
 @pytest.mark.parametrize("T", [1, 17, 63, 64, 65, 130])
 def test_prefill_tails_bf16(chunk, T):
