@@ -99,7 +99,13 @@ const char *gdn_status_string(int status);
  *               offsets must start at 0, never decrease and end at T; they are
  *               read on the device and clamped to [0, T], so a bad array gives
  *               wrong results, never an out-of-bounds access.  Zero-length
- *               sequences are allowed (S_T[n] = S0[n], no rows of O).
+ *               sequences are allowed (S_T[n] = S0[n], no rows of O).  For
+ *               debugging, with the environment variable GDN_CHECK_SEQLENS
+ *               set (to anything but "0"), every call that takes cu_seqlens
+ *               copies it to the host first, synchronising the stream (so not
+ *               under graph capture), and returns GDN_ERR_INVALID_ARG, with
+ *               nothing enqueued, for offsets that do not start at 0, decrease,
+ *               or do not end at T.
  *   chunk       16, 32 or 64 (the page's prompt-block sizes); the result does
  *               not depend on it beyond rounding, so it is a tiling choice.  A
  *               bf16 batch of short sequences (at most 16 tokens per sequence

@@ -1,11 +1,15 @@
 // libgdn C ABI: argument validation and launch selection (see include/gdn.h).
-// Nothing here allocates or synchronises; a rejected call enqueues nothing.
+// Nothing here allocates device memory or synchronises (except the opt-in
+// debugging check of packed offsets below); a rejected call enqueues nothing.
 
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
 #include <cfloat>
 #include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
 
 namespace {
 
@@ -28,6 +32,25 @@ bool overlap(Range a, Range b) {
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
 bool dims_ok(int64_t x) { return x >= 0 && x < kMaxDim; }
+
+// Opt-in debugging check of packed offsets: with GDN_CHECK_SEQLENS set (to
+// anything but "0"), cu_seqlens is copied to the host on the caller's stream,
+// which is then synchronised, and must start at 0, never decrease and end at
+// T.  Without it the kernels read the offsets on the device and clamp them.
+int check_seqlens_debug(const int32_t *cu, int64_t N, int64_t T, void *stream) {
+    const char *env = std::getenv("GDN_CHECK_SEQLENS");
+    if (!cu || !env || !*env || std::strcmp(env, "0") == 0) return GDN_OK;
+    std::vector<int32_t> h(static_cast<size_t>(N) + 1);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s) !=
+            hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+        return GDN_ERR_HIP;
+    if (h[0] != 0 || h[static_cast<size_t>(N)] != T) return GDN_ERR_INVALID_ARG;
+    for (int64_t n = 0; n < N; ++n)
+        if (h[static_cast<size_t>(n) + 1] < h[static_cast<size_t>(n)]) return GDN_ERR_INVALID_ARG;
+    return GDN_OK;
+}
 
 }  // namespace
 
@@ -202,7 +225,9 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
     int64_t tok_bytes = 0;
     const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
                                  dv, chunk, O, S_T, a, tok_bytes);
-    return st != GDN_OK ? st : launch_prefill(a, stream);
+    if (st != GDN_OK) return st;
+    if (const int sc = check_seqlens_debug(cu_seqlens, B_or_N, T, stream)) return sc;
+    return launch_prefill(a, stream);
 }
 
 int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dtype,
@@ -218,6 +243,7 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
     const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
                                  dv, chunk, O, S_T, a, tok_bytes);
     if (st != GDN_OK) return st;
+    if (const int sc = check_seqlens_debug(cu_seqlens, B_or_N, T, stream)) return sc;
     if (inverse != GDN_INVERSE_DEFAULT) {
         a.inverse = inverse == GDN_INVERSE_DOUBLING ? gdn::kInverseDoubling
                                                     : gdn::kInverseSubstitution;
@@ -246,6 +272,7 @@ int gdn_chunk_prefill_gated(const void *q, const void *k, const void *v, int io_
                 rST = span_of(S_T, a.N * H * gdn::kHeadDim * gdn::kHeadDim * 4);
     for (Range r : {rz, rw})
         if (overlap(rY, r) || overlap(rST, r)) return GDN_ERR_ALIAS;
+    if (const int sc = check_seqlens_debug(cu_seqlens, B_or_N, T, stream)) return sc;
     // z is NULL only in a call without token rows, where the plain form does
     // the same work (S_T = S0)
     a.z = z;
@@ -293,6 +320,7 @@ int gdn_prefill_states(const void *q, const void *k, const void *v, int io_dtype
     gdn::PrefillArgs a{q, k, v, g, beta, S0, cu_seqlens, N, T, H, 0,
                        io_dtype == GDN_BF16, O, nullptr};
     if (N == 0) return GDN_OK;
+    if (const int sc = check_seqlens_debug(cu_seqlens, N, T, stream)) return sc;
     hipError_t e = gdn::launch_prefill_states(a, S_tok, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
@@ -342,6 +370,7 @@ int gdn_preop(const void *xq, const void *xk, const void *xv, int io_dtype, cons
         if (overlap(o, rsi)) return GDN_ERR_ALIAS;
     if (overlap(rso, rsi) && rso.lo != rsi.lo) return GDN_ERR_ALIAS;   // in place or apart
     if (N == 0) return GDN_OK;
+    if (const int sc = check_seqlens_debug(cu_seqlens, N, T, stream)) return sc;
     gdn::PreopArgs p{xq, xk, xv, a, b, conv_w, state_in, state_out, cu_seqlens, N, T, rows, H,
                      eps, io_dtype == GDN_BF16, q, k, v, g, beta};
     const hipError_t e = gdn::launch_preop(p, static_cast<hipStream_t>(stream));

@@ -272,3 +272,27 @@ def test_prefill_packed_longest_first_with_ties_and_empty():
     Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, cu_seqlens=w.cu_seqlens)
     check_prefill(w, O, S_T, Or, Sr, label="longest first")
     assert torch.equal(S_T[3], w.S0[3]), "the empty sequence keeps its state"
+
+
+def test_seqlens_debug_check_refuses_bad_offsets(monkeypatch):
+    # With GDN_CHECK_SEQLENS set, packed offsets are checked on a host copy and
+    # a malformed array is refused with nothing enqueued (outputs untouched).
+    from linear_attention_recurrence_02_amd.binding import GDN_ERR_INVALID_ARG, gdn_prefill_states
+    w = inputs.varlen_workload([10, 20, 2], H=2, seed=97, device=DEV)
+    monkeypatch.setenv("GDN_CHECK_SEQLENS", "1")
+    O, S_T = run_prefill(w)
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens)
+    check_prefill(w, O, S_T, Or, Sr, label="checked offsets")
+    for bad in ([0, 20, 10, 32], [0, 10, 30, 31], [1, 10, 30, 32]):
+        cu = torch.tensor(bad, dtype=torch.int32, device=DEV)
+        O = torch.full_like(w.v, 7.0)
+        S_T = torch.full_like(w.S0, 7.0)
+        with pytest.raises(GdnError) as e:
+            gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, cu, 64, O=O, S_T=S_T)
+        assert e.value.status == GDN_ERR_INVALID_ARG, bad
+        S_tok = torch.full((1, 32, 2, 128, 128), 7.0, device=DEV)
+        with pytest.raises(GdnError) as e:
+            gdn_prefill_states(w.q, w.k, w.v, w.g, w.beta, w.S0, cu, O=O, S_tok=S_tok)
+        assert e.value.status == GDN_ERR_INVALID_ARG, bad
+        torch.cuda.synchronize()
+        assert bool((O == 7).all()) and bool((S_T == 7).all()) and bool((S_tok == 7).all())
