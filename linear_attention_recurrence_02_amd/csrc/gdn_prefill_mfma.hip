@@ -488,21 +488,39 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q,
     f16x4 Wr[3][2], Ur[3][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
+        // Two K = 16 products share one K = 32 product where a pair exists;
+        // a lone one (block 0's P K, block 2's M_21 W_1) takes a K = 16
+        // product rather than a zero-padded K = 32 one
         f32x4 aw[2], au[2];
-        const f16x4 m0 = i >= 1 ? mm[oblk(i > 0 ? i : 1, 0)] : zh4();
-        const f16x8 a0w = cat(pw[i], m0);
-        const f16x8 a0u = cat(pu[i], m0);
-#pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
-            aw[cc] = mfma(a0w, cat(kx[i][cc], i >= 1 ? Wr[0][cc] : zh4()), zero4());
-            au[cc] = mfma(a0u, cat(vx[i][cc], i >= 1 ? Ur[0][cc] : zh4()), zero4());
-        }
-        if (i >= 2) {
-            const f16x8 a1 = cat(mm[oblk(i, 1)], i == 3 ? mm[oblk(3, 2)] : zh4());
+        if (i == 0) {
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                aw[cc] = mfma(a1, cat(Wr[1][cc], i == 3 ? Wr[2][cc] : zh4()), aw[cc]);
-                au[cc] = mfma(a1, cat(Ur[1][cc], i == 3 ? Ur[2][cc] : zh4()), au[cc]);
+                aw[cc] = mfma16(pw[0], kx[0][cc], zero4());
+                au[cc] = mfma16(pu[0], vx[0][cc], zero4());
+            }
+        } else {
+            const f16x4 m0 = mm[oblk(i > 0 ? i : 1, 0)];
+            const f16x8 a0w = cat(pw[i], m0);
+            const f16x8 a0u = cat(pu[i], m0);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                aw[cc] = mfma(a0w, cat(kx[i][cc], Wr[0][cc]), zero4());
+                au[cc] = mfma(a0u, cat(vx[i][cc], Ur[0][cc]), zero4());
+            }
+        }
+        if (i == 2) {
+            const f16x4 a1 = mm[oblk(2, 1)];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                aw[cc] = mfma16(a1, Wr[1][cc], aw[cc]);
+                au[cc] = mfma16(a1, Ur[1][cc], au[cc]);
+            }
+        } else if (i == 3) {
+            const f16x8 a1 = cat(mm[oblk(3, 1)], mm[oblk(3, 2)]);
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                aw[cc] = mfma(a1, cat(Wr[1][cc], Wr[2][cc]), aw[cc]);
+                au[cc] = mfma(a1, cat(Ur[1][cc], Ur[2][cc]), au[cc]);
             }
         }
 #pragma unroll
