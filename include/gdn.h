@@ -174,8 +174,9 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
  *               are scratch between calls.  Calls sharing a workspace must not
  *               run concurrently.
  *   workspace_bytes  its size.
- *   GDN_ERR_INVALID_ARG for a bad segment_len or a missing or short workspace,
- *   GDN_ERR_ALIAS if it overlaps an argument.
+ *   B * T must be below 2^31 (the segments' offsets are int32).
+ *   GDN_ERR_INVALID_ARG for a bad segment_len, B * T too large, or a missing or
+ *   short workspace; GDN_ERR_ALIAS if the workspace overlaps an argument.
  */
 int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int io_dtype,
                                 const float *g, const float *beta, const float *S0, int64_t B,

@@ -140,6 +140,7 @@ bool seg_layout(int io_dtype, int64_t N, int64_t T, int64_t H, int64_t L, SegLay
     w.P = T == 0 ? 1 : (T + L - 1) / L;
     const int64_t units = N * w.P * H;
     if (N * w.P >= kMaxDim || units >= kMaxDim) return false;
+    if (N * T >= kMaxDim) return false;            // the segment offsets are int32
     if (N * T > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return false;
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     const int64_t state = gdn::kHeadDim * gdn::kHeadDim * 4;

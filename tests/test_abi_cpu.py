@@ -137,6 +137,9 @@ def test_prefill_segmented_validation(lib):
     assert need >= 3 * 16 * 65536 + 2 * 1000 * 2 * 256
     assert lib.gdn_chunk_prefill_segmented_workspace(1, 2, 1000, 2, 0) == -1
     assert lib.gdn_chunk_prefill_segmented_workspace(7, 2, 1000, 2, 256) == -1
+    # B * T rows must fit the int32 segment offsets
+    assert lib.gdn_chunk_prefill_segmented_workspace(1, 2, 1 << 30, 1, 1 << 20) == -1
+    assert lib.gdn_chunk_prefill_segmented_workspace(1, 1, (1 << 30) - 1, 1, 1 << 20) > 0
 
     def seg(**kw):
         a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB, beta=A + 200 * MB,
