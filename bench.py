@@ -284,6 +284,18 @@ def bench_preop(torch, gdn, p, iters):
     }
 
 
+def cpu_model():
+    """The host CPU's model name, from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline_decode(w, target_s=12.0):
     """The oracle, as it stands, on the first n steps of the decode workload,
     n sized from a timed probe so that the sample takes about target_s."""
@@ -302,7 +314,7 @@ def cpu_baseline_decode(w, target_s=12.0):
     dt = time.perf_counter() - t0
     units = w.q.shape[1] * w.q.shape[2]
     return {"value": n * units * 2 * STATE_BYTES / dt / 1e9, "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"first {n} steps of the B=64 x H=16 decode batch "
                       f"({dt:.1f} s, fp64, {threads} threads)"}
 
@@ -331,7 +343,7 @@ def cpu_baseline_prefill(w, target_s=12.0):
         dt += time.perf_counter() - t0
         done += len(hs)
     return {"value": n_units * T / H / dt, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": f"{n_units} (sequence, head) units x {T} tokens of the large prefill "
                       f"({dt:.1f} s of oracle time), scaled to tokens of {H} heads"}
 
@@ -460,6 +472,7 @@ def main():
                     "prefill_large", source_digest("gdn_prefill_mfma.hip", "gdn_mfma.hpp"))
                 if not args.no_cpu_baseline:
                     r["cpu_baseline"] = cpu_baseline_prefill(w)
+                    r["cpu_baseline"]["gpu_over_cpu"] = r["tokens_per_s"] / r["cpu_baseline"]["value"]
                 # the same workload with the gated RMS norm fused on the output
                 rg = bench_prefill(torch, gdn, w, args.prefill_iters, 2,
                                    gate=inputs.norm_gate(w))
@@ -492,6 +505,7 @@ def main():
     if dec is not None and not args.no_cpu_baseline:
         log("cpu baseline: timing the oracle on a sample of the decode workload ...")
         result["cpu_baseline"] = cpu_baseline_decode(dec["workload"])
+        result["cpu_baseline"]["gpu_over_cpu"] = result["value"] / result["cpu_baseline"]["value"]
     print(json.dumps(result), flush=True)
 
 
