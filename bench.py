@@ -177,15 +177,14 @@ def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
     S_T = torch.empty((N, w.q.shape[2], DK, DV), dtype=torch.float32, device="cuda")
     ws = None
     if segment_len is not None:
-        B_, T_, H_ = w.q.shape[:3]
-        need = gdn.load_library().gdn_chunk_prefill_segmented_workspace(
-            1 if w.q.dtype == torch.bfloat16 else 0, B_, T_, H_, segment_len)
+        need = gdn.segmented_workspace_bytes(w.q, segment_len, w.cu_seqlens)
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device="cuda")
 
     def call():
         if segment_len is not None:
             gdn.gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, w.chunk,
-                                            segment_len, workspace=ws, O=O, S_T=S_T)
+                                            segment_len, cu_seqlens=w.cu_seqlens,
+                                            workspace=ws, O=O, S_T=S_T)
         elif gate is None:
             gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
                                   O=O, S_T=S_T)
@@ -467,6 +466,17 @@ def main():
                     f"{rs['seconds']*1e3:.3f} ms, MFMA {100*rs['mfma_frac']:.1f}%, "
                     f"HBM {100*rs['hbm_frac']:.1f}%")
                 pre[rs["workload"]] = rs
+                # a packed serving batch: one 16384-token prompt among 31 of 256
+                # tokens (not one of the specified workloads: it shows where the
+                # packed segmented form pays)
+                wp = inputs.varlen_workload([16384] + [256] * 31, H=16, seed=0,
+                                            name="packed_long_among_short", device="cuda")
+                for seg_len in (None, 2048):
+                    rp = bench_prefill(torch, gdn, wp, args.prefill_iters, 2, segment_len=seg_len)
+                    log(f"prefill {rp['workload']}: {rp['tokens_per_s']:.3e} tok/s, "
+                        f"{rp['seconds']*1e3:.3f} ms")
+                    pre[rp["workload"]] = rp
+                del wp
             if w.name == "large_prefill":
                 r["roofline"]["traffic"] = read_traffic(
                     "prefill_large", source_digest("gdn_prefill_mfma.hip", "gdn_mfma.hpp"))

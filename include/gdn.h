@@ -151,43 +151,50 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
                          float *S_T, void *stream);
 
 /*
- * gdn_chunk_prefill_segmented -- gdn_chunk_prefill for a uniform batch, with
- * each sequence cut into segments of segment_len tokens that are walked in
- * parallel.  Over a segment the recurrence is affine in the entering state,
- * S_out = M S_in + B (the prompt form's state update, Qwen3.5-9B-npu model
- * page, "How it works" -> "Gated DeltaNet on the NPU", composed over the
- * segment's chunks).  The call runs the prompt form over all segments at once
- * three times -- for B (from a zero state), for M (with v = 0 from the
- * identity) and, after a scan S_in(p+1) = M_p S_in(p) + B_p over each
- * sequence's segments, for O and the end states from the true S_in -- so that
- * a batch of a few long sequences keeps every CU busy.  The result equals
- * gdn_chunk_prefill's up to rounding (the scan adds one fp32 product per
- * segment boundary).
+ * gdn_chunk_prefill_segmented -- gdn_chunk_prefill with each sequence cut into
+ * segments of segment_len tokens that are walked in parallel.  Over a segment
+ * the recurrence is affine in the entering state, S_out = M S_in + B (the
+ * prompt form's state update, Qwen3.5-9B-npu model page, "How it works" ->
+ * "Gated DeltaNet on the NPU", composed over the segment's chunks).  The call
+ * runs the prompt form over all segments at once three times -- for B (from a
+ * zero state), for M (with v = 0 from the identity) and, after a scan
+ * S_in(p+1) = M_p S_in(p) + B_p over each sequence's segments, for O and the end
+ * states from the true S_in -- so that a batch of a few long sequences keeps
+ * every CU busy.  The result equals gdn_chunk_prefill's up to rounding (the scan
+ * adds one fp32 product per segment boundary).  It triples the prompt-form
+ * work, so it pays only when the plain call would leave most CUs idle.
  *
- *   q, k, v, g, beta, S0, B, T, H, dk, dv, chunk, O, S_T: as for
- *               gdn_chunk_prefill with cu_seqlens = NULL (B sequences of T tokens).
- *   segment_len a positive multiple of chunk; with one segment (T <= segment_len)
- *               the call is gdn_chunk_prefill and needs no workspace.
+ *   q, k, v, g, beta, S0, cu_seqlens, B_or_N, T, H, dk, dv, chunk, O, S_T: as for
+ *               gdn_chunk_prefill, uniform or packed.  Each sequence gets
+ *               max(1, ceil(length / segment_len)) segments.
+ *   segment_len a positive multiple of chunk.  A uniform batch with
+ *               T <= segment_len is the plain gdn_chunk_prefill and needs no
+ *               workspace.
  *   workspace   caller-owned device memory of at least
- *               gdn_chunk_prefill_segmented_workspace(io_dtype, B, T, H, segment_len)
- *               bytes, 256-byte aligned, overlapping no argument; its contents
- *               are scratch between calls.  Calls sharing a workspace must not
- *               run concurrently.
+ *               gdn_chunk_prefill_segmented_workspace(io_dtype, cu_seqlens,
+ *               B_or_N, T, H, segment_len) bytes, 256-byte aligned, overlapping
+ *               no argument; its contents are scratch between calls.  Calls
+ *               sharing a workspace must not run concurrently.
  *   workspace_bytes  its size.
- *   B * T must be below 2^31 (the segments' offsets are int32).
- *   GDN_ERR_INVALID_ARG for a bad segment_len, B * T too large, or a missing or
+ *   The token rows (B * T, or T when packed) must be below 2^31: the segments'
+ *   offsets are int32.
+ *   GDN_ERR_INVALID_ARG for a bad segment_len, too many rows, or a missing or
  *   short workspace; GDN_ERR_ALIAS if the workspace overlaps an argument.
  */
 int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int io_dtype,
-                                const float *g, const float *beta, const float *S0, int64_t B,
-                                int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
-                                int64_t segment_len, void *workspace, int64_t workspace_bytes,
-                                void *O, float *S_T, void *stream);
+                                const float *g, const float *beta, const float *S0,
+                                const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
+                                int64_t dk, int64_t dv, int64_t chunk, int64_t segment_len,
+                                void *workspace, int64_t workspace_bytes, void *O, float *S_T,
+                                void *stream);
 
-/* Bytes of workspace gdn_chunk_prefill_segmented needs for these sizes (one
- * state of 64 KiB per segment and head three times, a zero copy of v and the
- * segment offsets), or -1 if the sizes are invalid. */
-int64_t gdn_chunk_prefill_segmented_workspace(int io_dtype, int64_t B, int64_t T, int64_t H,
+/* Bytes of workspace gdn_chunk_prefill_segmented needs for these sizes, or -1
+ * if they are invalid: per segment and head, three states of 64 KiB (a
+ * uniform batch has B ceil(T / segment_len) segments; a packed one is sized
+ * for N + ceil(T / segment_len)), plus a zero copy of v and the segments'
+ * offsets.  cu_seqlens is not read: only whether it is NULL matters. */
+int64_t gdn_chunk_prefill_segmented_workspace(int io_dtype, const int32_t *cu_seqlens,
+                                              int64_t B_or_N, int64_t T, int64_t H,
                                               int64_t segment_len);
 
 /*

@@ -62,10 +62,11 @@ def load_library(path: Optional[str] = None):
     lib.gdn_chunk_prefill_ex.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
                                          i64, i64, i64, i64, ctypes.c_int, vp, vp, vp]
     lib.gdn_chunk_prefill_ex.restype = ctypes.c_int
-    lib.gdn_chunk_prefill_segmented.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64,
-                                                i64, i64, i64, i64, i64, vp, i64, vp, vp, vp]
+    lib.gdn_chunk_prefill_segmented.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64,
+                                                i64, i64, i64, i64, i64, i64, vp, i64, vp, vp,
+                                                vp]
     lib.gdn_chunk_prefill_segmented.restype = ctypes.c_int
-    lib.gdn_chunk_prefill_segmented_workspace.argtypes = [ctypes.c_int, i64, i64, i64, i64]
+    lib.gdn_chunk_prefill_segmented_workspace.argtypes = [ctypes.c_int, vp, i64, i64, i64, i64]
     lib.gdn_chunk_prefill_segmented_workspace.restype = i64
     lib.gdn_chunk_prefill_gated.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64,
                                             i64, i64, i64, i64, i64, vp, vp, ctypes.c_float,
@@ -166,37 +167,53 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
     return O, S_T
 
 
+def segmented_workspace_bytes(q, segment_len, cu_seqlens=None):
+    """Bytes of workspace gdn_chunk_prefill_segmented needs for q's shape and
+    dtype ([B, T, H, 128], or a packed [1, T, H, 128] with ``cu_seqlens``), or
+    ValueError for sizes it cannot take."""
+    B, T, H, _ = q.shape
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    need = load_library().gdn_chunk_prefill_segmented_workspace(
+        _io_dtype(q), _ptr(cu_seqlens, torch.int32, "cu_seqlens"), N, T, H, int(segment_len))
+    if need < 0:
+        raise ValueError("invalid sizes for the segmented prompt form")
+    return need
+
+
 def gdn_chunk_prefill_segmented(q, k, v, g, beta, S0=None, chunk=64, segment_len=256, *,
-                                workspace=None, O=None, S_T=None, stream=None):
-    """The prompt form over a uniform batch with each sequence cut into
-    segments walked in parallel (see include/gdn.h).  ``workspace``: a uint8
-    device tensor of at least gdn_chunk_prefill_segmented_workspace bytes, or
-    None to allocate one here.  Returns (O, S_T)."""
+                                cu_seqlens=None, workspace=None, O=None, S_T=None, stream=None):
+    """The prompt form with each sequence cut into segments walked in parallel
+    (see include/gdn.h); a uniform batch, or a packed one with ``cu_seqlens``
+    (int32 [N+1] device offsets, B == 1).  ``workspace``: a uint8 device tensor
+    of at least gdn_chunk_prefill_segmented_workspace bytes, or None to allocate
+    one here.  Returns (O, S_T)."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed batches (cu_seqlens) need B == 1")
     if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype \
             or v.dtype != q.dtype:
         raise ValueError("q, k, v must share shape [B, T, H, d] and dtype")
     if g.shape != (B, T, H) or beta.shape != (B, T, H):
         raise ValueError("g and beta must be [B, T, H]")
     lib = load_library()
-    need = lib.gdn_chunk_prefill_segmented_workspace(_io_dtype(q), B, T, H, int(segment_len))
-    if need < 0:
-        raise ValueError("invalid sizes for the segmented prompt form")
+    cu = _ptr(cu_seqlens, torch.int32, "cu_seqlens")
+    need = segmented_workspace_bytes(q, segment_len, cu_seqlens)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     if O is None:
         O = torch.empty_like(v)
     if S_T is None:
-        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=q.device)
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
     if O.dtype != q.dtype or O.shape != v.shape:
         raise ValueError("O must match v's shape and dtype")
-    if S_T.shape != (B, H, dk, dv) or (S0 is not None and S0.shape != (B, H, dk, dv)):
-        raise ValueError("S0 / S_T must be [B, H, dk, dv]")
+    if S_T.shape != (N, H, dk, dv) or (S0 is not None and S0.shape != (N, H, dk, dv)):
+        raise ValueError("S0 / S_T must be [N, H, dk, dv]")
     st = lib.gdn_chunk_prefill_segmented(
         _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
         _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
-        _ptr(S0, torch.float32, "S0"), B, T, H, dk, dv, int(chunk), int(segment_len),
+        _ptr(S0, torch.float32, "S0"), cu, N, T, H, dk, dv, int(chunk), int(segment_len),
         _ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
         _ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
     _check(st)

@@ -126,27 +126,33 @@ int launch_prefill(const gdn::PrefillArgs &a, void *stream) {
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
-// Workspace of the segmented prompt form: the refined offsets, a zero copy
-// of v, and three arrays of one state per (segment, head).  Offsets are
-// 256-byte aligned; returns the total, or -1 for sizes it cannot hold.
+// Workspace of the segmented prompt form: the segments' offsets, each
+// sequence's first segment, a zero copy of v, and three arrays of one state per
+// (segment, head).  A uniform batch has N ceil(T / L) segments (at least N); a
+// packed one at most N + ceil(T / L), each sequence rounding up once.  Parts are
+// 256-byte aligned; false for sizes it cannot hold.
 struct SegLayout {
-    int64_t P, cu, vzero, vzero_bytes, s1, m, b, total;
+    int64_t Ns, rows, cu, seg, vzero, vzero_bytes, s1, m, b, total;
 };
 
-bool seg_layout(int io_dtype, int64_t N, int64_t T, int64_t H, int64_t L, SegLayout &w) {
+bool seg_layout(int io_dtype, bool packed, int64_t N, int64_t T, int64_t H, int64_t L,
+                SegLayout &w) {
     if (!dims_ok(N) || !dims_ok(T) || H <= 0 || H >= 65536 || L <= 0) return false;
     if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return false;
     const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
-    w.P = T == 0 ? 1 : (T + L - 1) / L;
-    const int64_t units = N * w.P * H;
-    if (N * w.P >= kMaxDim || units >= kMaxDim) return false;
-    if (N * T >= kMaxDim) return false;            // the segment offsets are int32
-    if (N * T > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return false;
+    const int64_t per = (T + L - 1) / L;
+    w.rows = packed ? T : N * T;
+    if (w.rows >= kMaxDim) return false;           // the segments' offsets are int32
+    w.Ns = packed ? N + per : N * (per > 0 ? per : 1);
+    const int64_t units = w.Ns * H;
+    if (w.Ns >= kMaxDim || units >= kMaxDim) return false;
+    if (w.rows > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return false;
     auto up = [](int64_t x) { return (x + 255) / 256 * 256; };
     const int64_t state = gdn::kHeadDim * gdn::kHeadDim * 4;
     w.cu = 0;
-    w.vzero = up((N * w.P + 1) * 4);
-    w.vzero_bytes = up(N * T * H * gdn::kHeadDim * esz);
+    w.seg = up((w.Ns + 1) * 4);
+    w.vzero = w.seg + up((N + 1) * 4);
+    w.vzero_bytes = up(w.rows * H * gdn::kHeadDim * esz);
     w.s1 = w.vzero + w.vzero_bytes;
     w.m = w.s1 + up(units * state);
     w.b = w.m + up(units * state);
@@ -158,42 +164,50 @@ bool seg_layout(int io_dtype, int64_t N, int64_t T, int64_t H, int64_t L, SegLay
 
 extern "C" {
 
-int64_t gdn_chunk_prefill_segmented_workspace(int io_dtype, int64_t B, int64_t T, int64_t H,
+int64_t gdn_chunk_prefill_segmented_workspace(int io_dtype, const int32_t *cu_seqlens,
+                                              int64_t B_or_N, int64_t T, int64_t H,
                                               int64_t segment_len) {
     SegLayout w;
-    return seg_layout(io_dtype, B, T, H, segment_len, w) ? w.total : -1;
+    return seg_layout(io_dtype, cu_seqlens != nullptr, B_or_N, T, H, segment_len, w) ? w.total
+                                                                                      : -1;
 }
 
 int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int io_dtype,
-                                const float *g, const float *beta, const float *S0, int64_t B,
-                                int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
-                                int64_t segment_len, void *workspace, int64_t workspace_bytes,
-                                void *O, float *S_T, void *stream) {
+                                const float *g, const float *beta, const float *S0,
+                                const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
+                                int64_t dk, int64_t dv, int64_t chunk, int64_t segment_len,
+                                void *workspace, int64_t workspace_bytes, void *O, float *S_T,
+                                void *stream) {
     gdn::PrefillArgs a{};
     int64_t tok_bytes = 0;
-    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, nullptr, B, T, H, dk, dv, chunk,
-                                 O, S_T, a, tok_bytes);
+    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
+                                 dv, chunk, O, S_T, a, tok_bytes);
     if (st != GDN_OK) return st;
     if (segment_len <= 0 || segment_len % chunk != 0) return GDN_ERR_INVALID_ARG;
+    const int64_t N = B_or_N;
     SegLayout w;
-    if (!seg_layout(io_dtype, B, T, H, segment_len, w)) return GDN_ERR_INVALID_ARG;
-    if (w.P == 1 || B == 0) return launch_prefill(a, stream);   // one segment: the plain form
+    if (!seg_layout(io_dtype, cu_seqlens != nullptr, N, T, H, segment_len, w))
+        return GDN_ERR_INVALID_ARG;
+    if (const int sc = check_seqlens_debug(cu_seqlens, N, T, stream)) return sc;
+    // a uniform batch of one segment per sequence is the plain form
+    if (N == 0 || (!cu_seqlens && T <= segment_len)) return launch_prefill(a, stream);
     if (!workspace || workspace_bytes < w.total || !aligned(workspace, 256))
         return GDN_ERR_INVALID_ARG;
-    const int64_t gb = B * T * H * 4, st_bytes = B * H * gdn::kHeadDim * gdn::kHeadDim * 4;
+    const int64_t gb = w.rows * H * 4, st_bytes = N * H * gdn::kHeadDim * gdn::kHeadDim * 4;
     const Range rw = span_of(workspace, w.total);
     for (Range r : {span_of(q, tok_bytes), span_of(k, tok_bytes), span_of(v, tok_bytes),
                     span_of(g, gb), span_of(beta, gb), span_of(O, tok_bytes),
-                    span_of(S_T, st_bytes), S0 ? span_of(S0, st_bytes) : Range{0, 0}})
+                    span_of(S_T, st_bytes), S0 ? span_of(S0, st_bytes) : Range{0, 0},
+                    cu_seqlens ? span_of(cu_seqlens, (N + 1) * 4) : Range{0, 0}})
         if (overlap(rw, r)) return GDN_ERR_ALIAS;
 
     char *ws = static_cast<char *>(workspace);
-    int32_t *cu = reinterpret_cast<int32_t *>(ws + w.cu);
+    int32_t *cu = reinterpret_cast<int32_t *>(ws + w.cu);    // the segments' offsets
+    int32_t *seg = reinterpret_cast<int32_t *>(ws + w.seg);  // each sequence's first segment
     void *vzero = ws + w.vzero;
     float *s1 = reinterpret_cast<float *>(ws + w.s1);   // identity states, then S_in
     float *m = reinterpret_cast<float *>(ws + w.m);     // state maps
     float *b = reinterpret_cast<float *>(ws + w.b);     // zero-start states, then end states
-    const int64_t Ns = B * w.P;
     hipStream_t s = static_cast<hipStream_t>(stream);
     auto run = [&](const void *vv, const float *s0, float *st_out) {
         gdn::PrefillArgs r = a;
@@ -201,20 +215,21 @@ int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int
         r.S0 = s0;
         r.S_T = st_out;
         r.cu_seqlens = cu;
-        r.N = Ns;
-        r.T = B * T;
+        r.N = w.Ns;
+        r.T = w.rows;
         return launch_prefill(r, stream);
     };
-    if (gdn::launch_segment_init(cu, B, T, w.P, segment_len, vzero, w.vzero_bytes, s1, Ns * H, s) !=
-        hipSuccess)
+    if (gdn::launch_segment_plan(cu_seqlens, N, T, segment_len, w.Ns, seg, cu, s) != hipSuccess ||
+        gdn::launch_segment_fill(vzero, w.vzero_bytes, s1, w.Ns * H, s) != hipSuccess)
         return GDN_ERR_HIP;
     int rc = run(v, nullptr, b);                       // B: each segment from zero
     if (rc == GDN_OK) rc = run(vzero, s1, m);          // M: V = 0 from the identity
     if (rc != GDN_OK) return rc;
-    if (gdn::launch_segment_scan(m, b, S0, s1, B, H, w.P, s) != hipSuccess) return GDN_ERR_HIP;
+    if (gdn::launch_segment_scan(m, b, S0, s1, seg, N, H, s) != hipSuccess) return GDN_ERR_HIP;
     rc = run(v, s1, b);                                // O and the end states from S_in
     if (rc != GDN_OK) return rc;
-    return gdn::launch_segment_gather(b, S_T, B, H, w.P, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+    return gdn::launch_segment_gather(b, S0, seg, S_T, N, H, s) == hipSuccess ? GDN_OK
+                                                                               : GDN_ERR_HIP;
 }
 
 int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,

@@ -70,13 +70,14 @@ struct PreopArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Helpers of the segmented prompt form (see gdn_segmented.hip).
-hipError_t launch_segment_init(int32_t *cu, int64_t N, int64_t T, int64_t P, int64_t L,
-                               void *vzero, int64_t vzero_bytes, float *sid, int64_t units,
+hipError_t launch_segment_plan(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
+                               int32_t *seg, int32_t *cu_out, hipStream_t stream);
+hipError_t launch_segment_fill(void *vzero, int64_t vzero_bytes, float *sid, int64_t units,
                                hipStream_t stream);
 hipError_t launch_segment_scan(const float *M, const float *B, const float *S0, float *Sin,
-                               int64_t N, int64_t H, int64_t P, hipStream_t stream);
-hipError_t launch_segment_gather(const float *Sout, float *S_T, int64_t N, int64_t H, int64_t P,
-                                 hipStream_t stream);
+                               const int32_t *seg, int64_t N, int64_t H, hipStream_t stream);
+hipError_t launch_segment_gather(const float *Sout, const float *S0, const int32_t *seg,
+                                 float *S_T, int64_t N, int64_t H, hipStream_t stream);
 hipError_t launch_preop(const PreopArgs &p, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);

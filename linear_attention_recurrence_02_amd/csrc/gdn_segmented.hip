@@ -1,6 +1,7 @@
 // Helpers of the segmented prompt form (context parallelism on one GPU).
 //
-// A sequence is cut into P segments of L tokens.  Over a segment the
+// Each sequence is cut into segments of L tokens (at least one, so an empty
+// sequence has one empty segment).  Over a segment the
 // recurrence is affine in the state that enters it: S_out = M S_in + B, with
 // M (dk x dk) the segment's state map (the prompt form run with V = 0 from
 // S = I) and B (dk x dv) the state the segment reaches from zero.  Both come
@@ -11,9 +12,10 @@
 // kernel from those states produces O and the segment end states.  Each run
 // keeps the whole GPU busy even when a batch holds only a few long sequences.
 //
-// This file holds the small kernels around those runs: the refined offsets,
-// the zero values and identity states the map run needs, the scan, and the
-// gather of each sequence's final state.
+// This file holds the small kernels around those runs: the plan (each
+// sequence's first segment and the segments' offsets, for a uniform or a
+// packed batch), the zero values and identity states the map run needs, the
+// scan, and the gather of each sequence's final state.
 
 #include "gdn_internal.hpp"
 
@@ -24,19 +26,55 @@ constexpr int D = kHeadDim;
 constexpr int kCols = 8;        // state columns per scan workgroup
 constexpr int64_t kState = int64_t(D) * D;
 
-// cu[s] for s = 0..N*P: segment p of sequence n starts at n T + p L (clamped
-// to the sequence's end); zero values; one identity state per segment unit.
-__global__ __launch_bounds__(256) void segment_init_kernel(int32_t *cu, int64_t N, int64_t T,
-                                                           int64_t P, int64_t L, uint4 *vzero,
-                                                           int64_t vzero16, float *sid,
-                                                           int64_t units) {
+// The plan, by one workgroup of 1024 threads: sequence n (rows [start, start
+// + len), from cu_seqlens clamped as the prompt kernels clamp it, or n T .. for
+// a uniform batch) gets P_n = max(1, ceil(len / L)) segments, numbered from
+// seg[n] = P_0 + .. + P_{n-1}; segment seg[n] + j starts at row start + j L.
+// The numbering is capped at Ns, the workspace's segment count (reached only
+// by offsets that overlap, which give wrong results but stay in bounds); the
+// segments past the last sequence start, and end, at the last row.
+__global__ __launch_bounds__(1024) void segment_plan_kernel(const int32_t *__restrict__ cu_in,
+                                                            int64_t N, int64_t T, int64_t L,
+                                                            int64_t Ns, int32_t *__restrict__ seg,
+                                                            int32_t *__restrict__ cu_out) {
+    __shared__ int64_t sc[1024];
+    const int tid = threadIdx.x;
+    const int64_t rows = cu_in ? T : N * T;
+    int64_t running = 0;
+    for (int64_t base = 0; base < N; base += 1024) {
+        const int64_t n = base + tid;
+        int64_t start = 0, len = 0, p = 0;
+        if (n < N) {
+            sequence_span(cu_in, n, T, start, len);
+            p = len > 0 ? (len + L - 1) / L : 1;
+        }
+        sc[tid] = p;
+        __syncthreads();
+        for (int off = 1; off < 1024; off <<= 1) {           // inclusive scan
+            const int64_t x = tid >= off ? sc[tid - off] : 0;
+            __syncthreads();
+            sc[tid] += x;
+            __syncthreads();
+        }
+        const int64_t incl = running + sc[tid], total = sc[1023];
+        if (n < N) {
+            const int64_t s0 = incl - p < Ns ? incl - p : Ns, s1 = incl < Ns ? incl : Ns;
+            seg[n] = static_cast<int32_t>(s0);
+            for (int64_t s = s0; s < s1; ++s) cu_out[s] = static_cast<int32_t>(start + (s - s0) * L);
+        }
+        running += total;
+        __syncthreads();                                      // sc is reused
+    }
+    const int64_t used = running < Ns ? running : Ns;
+    if (tid == 0) seg[N] = static_cast<int32_t>(used);
+    for (int64_t s = used + tid; s <= Ns; s += 1024) cu_out[s] = static_cast<int32_t>(rows);
+}
+
+// Zero values; one identity state per segment unit.
+__global__ __launch_bounds__(256) void segment_fill_kernel(uint4 *vzero, int64_t vzero16,
+                                                           float *sid, int64_t units) {
     const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
     const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    for (int64_t s = i0; s <= N * P; s += stride) {
-        const int64_t n = s / P, p = s % P;
-        const int64_t r = n * T + (p * L < T ? p * L : T);
-        cu[s] = static_cast<int32_t>(s == N * P ? N * T : r);
-    }
     for (int64_t i = i0; i < vzero16; i += stride) vzero[i] = make_uint4(0u, 0u, 0u, 0u);
     static_assert(kState / 4 == 4096 && D == 128, "index bits below");
     for (int64_t i = i0; i < units * (kState / 4); i += stride) {
@@ -89,11 +127,14 @@ __device__ __forceinline__ void scan_fold(float (&v)[32], bool upper) {
 __global__ __launch_bounds__(512) void segment_scan_kernel(const float *__restrict__ M,
                                                            const float *__restrict__ B,
                                                            const float *__restrict__ S0,
-                                                           float *__restrict__ Sin, int64_t H,
-                                                           int64_t P) {
+                                                           float *__restrict__ Sin,
+                                                           const int32_t *__restrict__ seg,
+                                                           int64_t H) {
     static_assert(kCols == 8 && D == 128, "thread layout below");
     const int64_t nh = blockIdx.x;                 // sequence n, head h: n * H + h
     const int64_t n = nh / H, h = nh % H;
+    const int64_t first = seg[n], P = seg[n + 1] - first;   // this sequence's segments
+    if (P <= 0) return;                            // (capped plan: nothing to scan)
     const int c0 = kCols * blockIdx.y;             // columns c0 .. c0 + 7
     const int t = threadIdx.x, s = t & 15, g = t >> 4;
     const int row0 = 4 * g;                        // rows row0 .. row0 + 3
@@ -109,7 +150,7 @@ __global__ __launch_bounds__(512) void segment_scan_kernel(const float *__restri
         if (S0) x = *reinterpret_cast<const float2 *>(S0 + nh * kState + r * D + c0 + c);
         *reinterpret_cast<float2 *>(&Ss[0][scan_slot(r, c >> 2) + (c & 3)]) = x;
     }
-    auto unit = [&](int64_t p) { return (n * P + p) * H + h; };   // segment unit index
+    auto unit = [&](int64_t p) { return (first + p) * H + h; };   // segment unit index
     auto load = [&](int64_t p, float4 (&dst)[8], float2 &bdst) {
         const float *mp = M + unit(p) * kState + row0 * D + 8 * s;
 #pragma unroll
@@ -186,36 +227,50 @@ __global__ __launch_bounds__(512) void segment_scan_kernel(const float *__restri
     }
 }
 
-// S_T of sequence n = the end state of its last segment.
+// S_T of sequence n = the end state of its last segment (its S0, or zero, if
+// a capped plan left it none).
 __global__ __launch_bounds__(256) void segment_gather_kernel(const float *__restrict__ Sout,
-                                                             float *__restrict__ S_T, int64_t H,
-                                                             int64_t P) {
+                                                             const float *__restrict__ S0,
+                                                             const int32_t *__restrict__ seg,
+                                                             float *__restrict__ S_T, int64_t H) {
     const int64_t nh = blockIdx.x, n = nh / H, h = nh % H;
-    const float4 *src = reinterpret_cast<const float4 *>(Sout + ((n * P + P - 1) * H + h) * kState);
+    const int64_t last = static_cast<int64_t>(seg[n + 1]) - 1;
     float4 *dst = reinterpret_cast<float4 *>(S_T + nh * kState);
-    for (int i = threadIdx.x; i < kState / 4; i += 256) dst[i] = src[i];
+    if (last >= seg[n]) {
+        const float4 *src = reinterpret_cast<const float4 *>(Sout + (last * H + h) * kState);
+        for (int i = threadIdx.x; i < kState / 4; i += 256) dst[i] = src[i];
+    } else {
+        const float4 *src = S0 ? reinterpret_cast<const float4 *>(S0 + nh * kState) : nullptr;
+        for (int i = threadIdx.x; i < kState / 4; i += 256)
+            dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
 }
 
 }  // namespace
 
-hipError_t launch_segment_init(int32_t *cu, int64_t N, int64_t T, int64_t P, int64_t L,
-                               void *vzero, int64_t vzero_bytes, float *sid, int64_t units,
+hipError_t launch_segment_plan(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
+                               int32_t *seg, int32_t *cu_out, hipStream_t stream) {
+    segment_plan_kernel<<<1, 1024, 0, stream>>>(cu_in, N, T, L, Ns, seg, cu_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_segment_fill(void *vzero, int64_t vzero_bytes, float *sid, int64_t units,
                                hipStream_t stream) {
-    segment_init_kernel<<<1024, 256, 0, stream>>>(cu, N, T, P, L, static_cast<uint4 *>(vzero),
-                                                   vzero_bytes / 16, sid, units);
+    segment_fill_kernel<<<1024, 256, 0, stream>>>(static_cast<uint4 *>(vzero), vzero_bytes / 16,
+                                                   sid, units);
     return hipGetLastError();
 }
 
 hipError_t launch_segment_scan(const float *M, const float *B, const float *S0, float *Sin,
-                               int64_t N, int64_t H, int64_t P, hipStream_t stream) {
+                               const int32_t *seg, int64_t N, int64_t H, hipStream_t stream) {
     segment_scan_kernel<<<dim3(static_cast<unsigned>(N * H), D / kCols), 512, 0, stream>>>(
-        M, B, S0, Sin, H, P);
+        M, B, S0, Sin, seg, H);
     return hipGetLastError();
 }
 
-hipError_t launch_segment_gather(const float *Sout, float *S_T, int64_t N, int64_t H, int64_t P,
-                                 hipStream_t stream) {
-    segment_gather_kernel<<<static_cast<unsigned>(N * H), 256, 0, stream>>>(Sout, S_T, H, P);
+hipError_t launch_segment_gather(const float *Sout, const float *S0, const int32_t *seg,
+                                 float *S_T, int64_t N, int64_t H, hipStream_t stream) {
+    segment_gather_kernel<<<static_cast<unsigned>(N * H), 256, 0, stream>>>(Sout, S0, seg, S_T, H);
     return hipGetLastError();
 }
 

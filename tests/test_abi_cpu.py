@@ -132,24 +132,29 @@ def test_prefill_ex_validation(lib):
 
 def test_prefill_segmented_validation(lib):
     W = A + 2048 * MB
-    need = lib.gdn_chunk_prefill_segmented_workspace(1, 2, 1000, 2, 256)
+    ws = lib.gdn_chunk_prefill_segmented_workspace
+    need = ws(1, None, 2, 1000, 2, 256)
     # 2 x 4 segments x 2 heads x 64 KiB three times, a zero copy of v, the offsets
     assert need >= 3 * 16 * 65536 + 2 * 1000 * 2 * 256
-    assert lib.gdn_chunk_prefill_segmented_workspace(1, 2, 1000, 2, 0) == -1
-    assert lib.gdn_chunk_prefill_segmented_workspace(7, 2, 1000, 2, 256) == -1
-    # B * T rows must fit the int32 segment offsets
-    assert lib.gdn_chunk_prefill_segmented_workspace(1, 2, 1 << 30, 1, 1 << 20) == -1
-    assert lib.gdn_chunk_prefill_segmented_workspace(1, 1, (1 << 30) - 1, 1, 1 << 20) > 0
+    assert ws(1, None, 2, 1000, 2, 0) == -1
+    assert ws(7, None, 2, 1000, 2, 256) == -1
+    # a packed batch of N sequences and T rows is sized for N + ceil(T / L) segments
+    packed = ws(1, A, 3, 2000, 2, 256)
+    assert packed >= 3 * (3 + 8) * 2 * 65536 + 2000 * 2 * 256
+    # the rows (B * T, or T when packed) must fit the int32 segment offsets
+    assert ws(1, None, 2, 1 << 30, 1, 1 << 20) == -1
+    assert ws(1, None, 1, (1 << 30) - 1, 1, 1 << 20) > 0
+    assert ws(1, A, 2, 1 << 31, 1, 1 << 20) == -1
 
     def seg(**kw):
         a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB, beta=A + 200 * MB,
-                 S0=A + 256 * MB, B=2, T=1000, H=2, chunk=64, L=256, ws=W, wsb=need,
+                 S0=A + 256 * MB, cu=None, B=2, T=1000, H=2, chunk=64, L=256, ws=W, wsb=need,
                  O=A + 512 * MB, S_T=A + 768 * MB)
         a.update(kw)
         return lib.gdn_chunk_prefill_segmented(a["q"], a["k"], a["v"], a["dtype"], a["g"],
-                                               a["beta"], a["S0"], a["B"], a["T"], a["H"], 128,
-                                               128, a["chunk"], a["L"], a["ws"], a["wsb"], a["O"],
-                                               a["S_T"], None)
+                                               a["beta"], a["S0"], a["cu"], a["B"], a["T"],
+                                               a["H"], 128, 128, a["chunk"], a["L"], a["ws"],
+                                               a["wsb"], a["O"], a["S_T"], None)
     assert seg(L=100) == binding.GDN_ERR_INVALID_ARG               # not a multiple of chunk
     assert seg(ws=None) == binding.GDN_ERR_INVALID_ARG
     assert seg(wsb=need - 1) == binding.GDN_ERR_INVALID_ARG
@@ -157,6 +162,10 @@ def test_prefill_segmented_validation(lib):
     assert seg(ws=A + 128 * MB + 4096) == binding.GDN_ERR_ALIAS    # workspace over v
     assert seg(q=None) == binding.GDN_ERR_INVALID_ARG
     assert seg(B=0) == binding.GDN_OK
+    # packed: the workspace must hold the packed bound and must not cover the offsets
+    cu = A + 1500 * MB
+    assert seg(cu=cu, B=3, T=2000, wsb=packed - 1) == binding.GDN_ERR_INVALID_ARG
+    assert seg(cu=cu, B=3, T=2000, wsb=packed, ws=cu - 256) == binding.GDN_ERR_ALIAS
 
 
 def gated(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB,

@@ -24,8 +24,9 @@ def say(*a):
 
 
 def check(w, O, S_T, label, S0=None):
-    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0 if S0 is None else S0)
-    spans = spans_of(w.q.shape[0], w.q.shape[1])
+    Or, Sr = oracle.prefill(w.q, w.k, w.v, w.g, w.beta, w.S0 if S0 is None else S0,
+                            w.cu_seqlens)
+    spans = spans_of(w.q.shape[0], w.q.shape[1], w.cu_seqlens)
     H = w.q.shape[2]
     eo, es = worst_slice_error(O, Or, spans, H), worst_slice_error(S_T, Sr)
     say(f"[{label}] worst slice error O={eo:.3e} S_T={es:.3e}")
@@ -83,3 +84,52 @@ def test_one_segment_is_the_plain_form():
     O2, S2 = gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, None, 64)
     torch.cuda.synchronize()
     assert torch.equal(O1, O2) and torch.equal(S1, S2)
+
+
+# packed batches: empty sequences, sequences shorter than a segment, partial last
+# segments and sequences of several segments side by side
+PACKED = [1000, 0, 37, 300, 129, 64]
+
+
+@pytest.mark.parametrize("L", [64, 128, 256])
+def test_packed_batch_segmented(L):
+    w = inputs.varlen_workload(PACKED, H=3, seed=86, device=DEV)
+    w.g.mul_(0.05)      # slow decay, so that the entering states matter
+    O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, 64, L,
+                                         cu_seqlens=w.cu_seqlens)
+    torch.cuda.synchronize()
+    check(w, O, S_T, f"packed {PACKED}, segments of {L}")
+
+
+def test_packed_zero_and_in_place_state():
+    w = inputs.varlen_workload(PACKED, H=2, s0=False, seed=87, device=DEV)
+    O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, None, 64, 128,
+                                         cu_seqlens=w.cu_seqlens)
+    torch.cuda.synchronize()
+    check(w, O, S_T, "packed, zero S0")
+    w = inputs.varlen_workload(PACKED, H=2, seed=88, device=DEV)
+    S = w.S0.clone()
+    O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, S, 64, 128,
+                                         cu_seqlens=w.cu_seqlens, S_T=S)
+    torch.cuda.synchronize()
+    assert S_T.data_ptr() == S.data_ptr()
+    check(w, O, S_T, "packed, in place", S0=w.S0)
+
+
+def test_packed_fp32_vector_kernel():
+    w = inputs.varlen_workload([90, 0, 33, 5], H=2, chunk=16, io_dtype=torch.float32,
+                               seed=89, device=DEV)
+    O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, 16, 32,
+                                         cu_seqlens=w.cu_seqlens)
+    torch.cuda.synchronize()
+    check(w, O, S_T, "packed fp32, segments of 32")
+
+
+def test_packed_long_sequence_among_short_ones():
+    # one 4096-token sequence with 15 short ones: the serving case the packed
+    # form is for
+    w = inputs.varlen_workload([4096] + [16] * 15, H=4, seed=90, device=DEV)
+    O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, 64, 256,
+                                         cu_seqlens=w.cu_seqlens)
+    torch.cuda.synchronize()
+    check(w, O, S_T, "one long among short, segments of 256")
