@@ -219,8 +219,8 @@ int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int
         r.T = w.rows;
         return launch_prefill(r, stream);
     };
-    if (gdn::launch_segment_plan(cu_seqlens, N, T, segment_len, w.Ns, seg, cu, s) != hipSuccess ||
-        gdn::launch_segment_fill(vzero, w.vzero_bytes, s1, w.Ns * H, s) != hipSuccess)
+    if (gdn::launch_segment_prep(cu_seqlens, N, T, segment_len, w.Ns, seg, cu, vzero, w.vzero_bytes,
+                                 s1, w.Ns * H, s) != hipSuccess)
         return GDN_ERR_HIP;
     int rc = run(v, nullptr, b);                       // B: each segment from zero
     if (rc == GDN_OK) rc = run(vzero, s1, m);          // M: V = 0 from the identity

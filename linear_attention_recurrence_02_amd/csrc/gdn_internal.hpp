@@ -70,10 +70,9 @@ struct PreopArgs {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 // Helpers of the segmented prompt form (see gdn_segmented.hip).
-hipError_t launch_segment_plan(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
-                               int32_t *seg, int32_t *cu_out, hipStream_t stream);
-hipError_t launch_segment_fill(void *vzero, int64_t vzero_bytes, float *sid, int64_t units,
-                               hipStream_t stream);
+hipError_t launch_segment_prep(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
+                               int32_t *seg, int32_t *cu_out, void *vzero, int64_t vzero_bytes,
+                               float *sid, int64_t units, hipStream_t stream);
 hipError_t launch_segment_scan(const float *M, const float *B, const float *S0, float *Sin,
                                const int32_t *seg, int64_t N, int64_t H, hipStream_t stream);
 hipError_t launch_segment_gather(const float *Sout, const float *S0, const int32_t *seg,

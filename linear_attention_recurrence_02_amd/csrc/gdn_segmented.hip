@@ -26,55 +26,57 @@ constexpr int D = kHeadDim;
 constexpr int kCols = 8;        // state columns per scan workgroup
 constexpr int64_t kState = int64_t(D) * D;
 
-// The plan, by one workgroup of 1024 threads: sequence n (rows [start, start
-// + len), from cu_seqlens clamped as the prompt kernels clamp it, or n T .. for
-// a uniform batch) gets P_n = max(1, ceil(len / L)) segments, numbered from
-// seg[n] = P_0 + .. + P_{n-1}; segment seg[n] + j starts at row start + j L.
-// The numbering is capped at Ns, the workspace's segment count (reached only
-// by offsets that overlap, which give wrong results but stay in bounds); the
-// segments past the last sequence start, and end, at the last row.
-__global__ __launch_bounds__(1024) void segment_plan_kernel(const int32_t *__restrict__ cu_in,
-                                                            int64_t N, int64_t T, int64_t L,
-                                                            int64_t Ns, int32_t *__restrict__ seg,
-                                                            int32_t *__restrict__ cu_out) {
-    __shared__ int64_t sc[1024];
+// One launch prepares the three runs.  Workgroup 0 makes the plan: sequence n
+// (rows [start, start + len), from cu_seqlens clamped as the prompt kernels
+// clamp it, or n T .. for a uniform batch) gets P_n = max(1, ceil(len / L))
+// segments, numbered from seg[n] = P_0 + .. + P_{n-1}; segment seg[n] + j
+// starts at row start + j L.  The numbering is capped at Ns, the workspace's
+// segment count (reached only by offsets that overlap, which give wrong
+// results but stay in bounds); the segments past the last sequence start, and
+// end, at the last row.  The other workgroups write the zero values and one
+// identity state per segment unit.
+constexpr int kPrepThreads = 256;
+__global__ __launch_bounds__(kPrepThreads) void segment_prep_kernel(
+    const int32_t *__restrict__ cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
+    int32_t *__restrict__ seg, int32_t *__restrict__ cu_out, uint4 *__restrict__ vzero,
+    int64_t vzero16, float *__restrict__ sid, int64_t units) {
     const int tid = threadIdx.x;
-    const int64_t rows = cu_in ? T : N * T;
-    int64_t running = 0;
-    for (int64_t base = 0; base < N; base += 1024) {
-        const int64_t n = base + tid;
-        int64_t start = 0, len = 0, p = 0;
-        if (n < N) {
-            sequence_span(cu_in, n, T, start, len);
-            p = len > 0 ? (len + L - 1) / L : 1;
-        }
-        sc[tid] = p;
-        __syncthreads();
-        for (int off = 1; off < 1024; off <<= 1) {           // inclusive scan
-            const int64_t x = tid >= off ? sc[tid - off] : 0;
+    if (blockIdx.x == 0) {
+        __shared__ int64_t sc[kPrepThreads];
+        const int64_t rows = cu_in ? T : N * T;
+        int64_t running = 0;
+        for (int64_t base = 0; base < N; base += kPrepThreads) {
+            const int64_t n = base + tid;
+            int64_t start = 0, len = 0, p = 0;
+            if (n < N) {
+                sequence_span(cu_in, n, T, start, len);
+                p = len > 0 ? (len + L - 1) / L : 1;
+            }
+            sc[tid] = p;
             __syncthreads();
-            sc[tid] += x;
-            __syncthreads();
+            for (int off = 1; off < kPrepThreads; off <<= 1) {   // inclusive scan
+                const int64_t x = tid >= off ? sc[tid - off] : 0;
+                __syncthreads();
+                sc[tid] += x;
+                __syncthreads();
+            }
+            const int64_t incl = running + sc[tid], total = sc[kPrepThreads - 1];
+            if (n < N) {
+                const int64_t s0 = incl - p < Ns ? incl - p : Ns, s1 = incl < Ns ? incl : Ns;
+                seg[n] = static_cast<int32_t>(s0);
+                for (int64_t s = s0; s < s1; ++s)
+                    cu_out[s] = static_cast<int32_t>(start + (s - s0) * L);
+            }
+            running += total;
+            __syncthreads();                                      // sc is reused
         }
-        const int64_t incl = running + sc[tid], total = sc[1023];
-        if (n < N) {
-            const int64_t s0 = incl - p < Ns ? incl - p : Ns, s1 = incl < Ns ? incl : Ns;
-            seg[n] = static_cast<int32_t>(s0);
-            for (int64_t s = s0; s < s1; ++s) cu_out[s] = static_cast<int32_t>(start + (s - s0) * L);
-        }
-        running += total;
-        __syncthreads();                                      // sc is reused
+        const int64_t used = running < Ns ? running : Ns;
+        if (tid == 0) seg[N] = static_cast<int32_t>(used);
+        for (int64_t s = used + tid; s <= Ns; s += kPrepThreads) cu_out[s] = static_cast<int32_t>(rows);
+        return;
     }
-    const int64_t used = running < Ns ? running : Ns;
-    if (tid == 0) seg[N] = static_cast<int32_t>(used);
-    for (int64_t s = used + tid; s <= Ns; s += 1024) cu_out[s] = static_cast<int32_t>(rows);
-}
-
-// Zero values; one identity state per segment unit.
-__global__ __launch_bounds__(256) void segment_fill_kernel(uint4 *vzero, int64_t vzero16,
-                                                           float *sid, int64_t units) {
-    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
-    const int64_t i0 = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t stride = static_cast<int64_t>(gridDim.x - 1) * kPrepThreads;
+    const int64_t i0 = static_cast<int64_t>(blockIdx.x - 1) * kPrepThreads + tid;
     for (int64_t i = i0; i < vzero16; i += stride) vzero[i] = make_uint4(0u, 0u, 0u, 0u);
     static_assert(kState / 4 == 4096 && D == 128, "index bits below");
     for (int64_t i = i0; i < units * (kState / 4); i += stride) {
@@ -248,16 +250,12 @@ __global__ __launch_bounds__(256) void segment_gather_kernel(const float *__rest
 
 }  // namespace
 
-hipError_t launch_segment_plan(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
-                               int32_t *seg, int32_t *cu_out, hipStream_t stream) {
-    segment_plan_kernel<<<1, 1024, 0, stream>>>(cu_in, N, T, L, Ns, seg, cu_out);
-    return hipGetLastError();
-}
-
-hipError_t launch_segment_fill(void *vzero, int64_t vzero_bytes, float *sid, int64_t units,
-                               hipStream_t stream) {
-    segment_fill_kernel<<<1024, 256, 0, stream>>>(static_cast<uint4 *>(vzero), vzero_bytes / 16,
-                                                   sid, units);
+hipError_t launch_segment_prep(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
+                               int32_t *seg, int32_t *cu_out, void *vzero, int64_t vzero_bytes,
+                               float *sid, int64_t units, hipStream_t stream) {
+    segment_prep_kernel<<<1025, kPrepThreads, 0, stream>>>(cu_in, N, T, L, Ns, seg, cu_out,
+                                                          static_cast<uint4 *>(vzero),
+                                                          vzero_bytes / 16, sid, units);
     return hipGetLastError();
 }
 
