@@ -167,6 +167,49 @@ def time_calls(torch, call, iters, reps=3):
     return statistics.median(per_call)
 
 
+def bench_decode_preop(torch, gdn, inputs, steps):
+    """Decode steps from the raw projections at the batched-decode shape (64 x 16),
+    each form captured as one graph of ``steps`` steps: the fused
+    gdn_decode_step_preop (one kernel a step) against gdn_preop followed by
+    gdn_decode_step (three).  The same token's projections feed every step (the
+    time does not depend on the values).  Returns microseconds per step."""
+    p = inputs.preop_inputs(64, 1, 16, seed=5, device="cuda")
+    S = inputs.decode_workload(1, 64, 16, seed=6, device="cuda").S0.clone()
+    state = p.state.clone()
+    x3 = [t[:, 0].contiguous() for t in (p.xq, p.xk, p.xv)]
+    a2, b2 = p.a[:, 0].contiguous(), p.b[:, 0].contiguous()
+    o = torch.empty_like(x3[2])
+    pre = [torch.empty_like(p.xq) for _ in range(3)] + [torch.empty_like(p.a) for _ in range(2)]
+
+    def fused():
+        gdn.gdn_decode_step_preop(*x3, a2, b2, p.conv_w, state, S, o=o)
+
+    def separate():
+        gdn.gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, state, out=pre)
+        gdn.gdn_decode_step(pre[0][:, 0], pre[1][:, 0], pre[2][:, 0], pre[3][:, 0],
+                            pre[4][:, 0], S, o=o)
+
+    out = {}
+    for name, f in (("fused", fused), ("separate", separate)):
+        for _ in range(3):
+            f()
+        torch.cuda.synchronize()
+        graph, cap = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+        with torch.cuda.graph(graph, stream=cap):
+            for _ in range(steps):
+                f()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = e0.elapsed_time(e1) * 1e3 / steps
+        del graph
+    return out
+
+
 def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
     """The prompt form over workload w; with gate = (z, norm_w, eps) the form
     with the gated RMS norm on the output (gdn_chunk_prefill_gated); with
@@ -444,6 +487,14 @@ def main():
                     f"HBM {100*alg/launch/HBM_PEAK:.1f}%")
                 del r_
                 torch.cuda.empty_cache()
+
+    if args.only in (None, "decode") and not args.cold and not args.streaming:
+        dp = bench_decode_preop(torch, gdn, inputs, min(args.steps, 200))
+        result["decode"]["preop_fused_us"] = dp["fused"]
+        result["decode"]["preop_then_decode_us"] = dp["separate"]
+        log(f"decode from raw projections: fused {dp['fused']:.2f} us/step, "
+            f"pre-operations then decode {dp['separate']:.2f} us/step")
+        torch.cuda.empty_cache()
 
     if args.only in (None, "prefill"):
         pre = {}

@@ -332,6 +332,35 @@ int gdn_decode_step_ex(const void *q, const void *k, const void *v, int io_dtype
                        int64_t H, int64_t dk, int64_t dv, int state_hint, void *o,
                        void *stream);
 
+/*
+ * gdn_decode_step_preop -- the decode step with the block's pre-operations
+ * fused in front: from the raw per-token projections and gate inputs of one
+ * token per (sequence, head), with each sequence's conv FIFO read and advanced,
+ * to o and the updated state, in one launch.  The pre-operations are
+ * gdn_preop's (its page citations and formulas): a causal conv over the three
+ * FIFO rows and the token, silu, q and k divided by sqrt(sum y^2 + eps),
+ * g = -softplus(a), beta = sigmoid(b); the step is gdn_decode_step's.  q, k and
+ * v are kept in fp32 between the two, so the result is gdn_preop followed by
+ * gdn_decode_step without the rounding of q, k, v to the io dtype in between.
+ *
+ *   xq, xk, xv  [B, H, 128] io_dtype, 16-byte aligned
+ *   a, b        [B, H] fp32
+ *   conv_w      [3, H, 128, 4] fp32, 16-byte aligned (as for gdn_preop)
+ *   state_in    [B, 3, H, 3, 128] io_dtype, rows oldest first; state_out the
+ *               same shape, either exactly state_in (advanced in place) or
+ *               disjoint
+ *   eps         finite and >= 0
+ *   S, B, H, dk, dv, o: as for gdn_decode_step; state_hint as for
+ *               gdn_decode_step_ex.
+ *   o, S and state_out must not overlap the inputs or each other (save
+ *   state_out == state_in) (GDN_ERR_ALIAS).
+ */
+int gdn_decode_step_preop(const void *xq, const void *xk, const void *xv, int io_dtype,
+                          const float *a, const float *b, const float *conv_w,
+                          const void *state_in, void *state_out, float eps, float *S, int64_t B,
+                          int64_t H, int64_t dk, int64_t dv, int state_hint, void *o,
+                          void *stream);
+
 #ifdef __cplusplus
 }
 #endif

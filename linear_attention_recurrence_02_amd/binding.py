@@ -23,7 +23,7 @@ GDN_F32, GDN_BF16 = 0, 1
 EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_ex",
             "gdn_chunk_prefill_segmented", "gdn_chunk_prefill_segmented_workspace",
             "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step",
-            "gdn_decode_step_ex")
+            "gdn_decode_step_ex", "gdn_decode_step_preop")
 GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
 GDN_STATE_CACHED, GDN_STATE_STREAMING = 0, 1
 
@@ -81,6 +81,10 @@ def load_library(path: Optional[str] = None):
     lib.gdn_decode_step_ex.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, i64, i64, i64,
                                        i64, ctypes.c_int, vp, vp]
     lib.gdn_decode_step_ex.restype = ctypes.c_int
+    lib.gdn_decode_step_preop.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
+                                          ctypes.c_float, vp, i64, i64, i64, i64, ctypes.c_int,
+                                          vp, vp]
+    lib.gdn_decode_step_preop.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -359,5 +363,41 @@ def gdn_decode_step(q, k, v, g, beta, S, *, o=None, stream=None, streaming=False
         st = load_library().gdn_decode_step_ex(*args, GDN_STATE_STREAMING, *tail)
     else:
         st = load_library().gdn_decode_step(*args, *tail)
+    _check(st)
+    return o
+
+
+def gdn_decode_step_preop(xq, xk, xv, a, b, conv_w, state, S, eps=1e-6, *, state_out=None,
+                          o=None, stream=None, streaming=False):
+    """One decode step from the raw projections: the pre-operations (conv FIFO,
+    silu, L2 norm of q and k, gates) and the step in one launch.
+
+    xq, xk, xv: [B, H, 128] (bf16 or fp32); a, b: [B, H] fp32;
+    conv_w: [3, H, 128, 4] fp32; state: [B, 3, H, 3, 128] with xq's dtype,
+    advanced in place unless ``state_out`` is given; S: [B, H, 128, 128] fp32,
+    updated in place.  streaming=True moves S with non-temporal loads and
+    stores.  Returns o [B, H, 128]."""
+    B, H, dk = xq.shape
+    dv = xv.shape[-1]
+    if xk.shape != xq.shape or xv.shape[:2] != (B, H) or xk.dtype != xq.dtype \
+            or xv.dtype != xq.dtype:
+        raise ValueError("xq, xk, xv must share shape [B, H, d] and dtype")
+    if a.shape != (B, H) or b.shape != (B, H) or S.shape != (B, H, dk, dv):
+        raise ValueError("a, b must be [B, H]; S [B, H, dk, dv]")
+    if conv_w.shape != (3, H, dk, 4) or state.shape != (B, 3, H, 3, dk) or state.dtype != xq.dtype:
+        raise ValueError("conv_w must be [3, H, 128, 4]; state [B, 3, H, 3, 128] with xq's dtype")
+    if state_out is None:
+        state_out = state
+    elif state_out.shape != state.shape or state_out.dtype != state.dtype:
+        raise ValueError("state_out must match state")
+    if o is None:
+        o = torch.empty_like(xv)
+    st = load_library().gdn_decode_step_preop(
+        _ptr(xq, name="xq"), _ptr(xk, name="xk"), _ptr(xv, name="xv"), _io_dtype(xq),
+        _ptr(a, torch.float32, "a"), _ptr(b, torch.float32, "b"),
+        _ptr(conv_w, torch.float32, "conv_w"), _ptr(state, xq.dtype, "state"),
+        _ptr(state_out, xq.dtype, "state_out"), float(eps), _ptr(S, torch.float32, "S"),
+        B, H, dk, dv, GDN_STATE_STREAMING if streaming else GDN_STATE_CACHED,
+        _ptr(o, xq.dtype, "o"), _stream(stream))
     _check(st)
     return o

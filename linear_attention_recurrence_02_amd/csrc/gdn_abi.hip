@@ -430,6 +430,49 @@ int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
     return decode_step(q, k, v, io_dtype, g, beta, S, B, H, dk, dv, o, false, stream);
 }
 
+int gdn_decode_step_preop(const void *xq, const void *xk, const void *xv, int io_dtype,
+                          const float *a, const float *b, const float *conv_w,
+                          const void *state_in, void *state_out, float eps, float *S, int64_t B,
+                          int64_t H, int64_t dk, int64_t dv, int state_hint, void *o,
+                          void *stream) {
+    if (state_hint != GDN_STATE_CACHED && state_hint != GDN_STATE_STREAMING)
+        return GDN_ERR_UNSUPPORTED;
+    if (!xq || !xk || !xv || !a || !b || !conv_w || !state_in || !state_out || !S || !o)
+        return GDN_ERR_INVALID_ARG;
+    if (!dims_ok(B) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (dk != gdn::kHeadDim || dv != gdn::kHeadDim) return GDN_ERR_UNSUPPORTED;
+    if (!(eps >= 0.f && eps <= FLT_MAX)) return GDN_ERR_INVALID_ARG;
+    for (const void *p : {xq, xk, xv, static_cast<const void *>(conv_w), state_in,
+                          static_cast<const void *>(state_out), static_cast<const void *>(S),
+                          static_cast<const void *>(o)})
+        if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    if (!aligned(a, 4) || !aligned(b, 4)) return GDN_ERR_INVALID_ARG;
+    const int64_t units = B * H;
+    if (units >= kMaxDim) return GDN_ERR_INVALID_ARG;
+    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t vec = units * gdn::kHeadDim * esz, gbytes = units * 4;
+    const int64_t fifo = units * 3 * 3 * gdn::kHeadDim * esz;
+    const Range rxq = span_of(xq, vec), rxk = span_of(xk, vec), rxv = span_of(xv, vec),
+                ra = span_of(a, gbytes), rb = span_of(b, gbytes),
+                rw = span_of(conv_w, 3 * H * gdn::kHeadDim * 4 * 4),
+                rsi = span_of(state_in, fifo), rso = span_of(state_out, fifo),
+                rS = span_of(S, units * gdn::kHeadDim * gdn::kHeadDim * 4), ro = span_of(o, vec);
+    // outputs (o, S, the new FIFO) apart from every input and from each other;
+    // the FIFO may be advanced in place
+    for (Range out : {ro, rS, rso})
+        for (Range in : {rxq, rxk, rxv, ra, rb, rw})
+            if (overlap(out, in)) return GDN_ERR_ALIAS;
+    if (overlap(ro, rS) || overlap(ro, rso) || overlap(rS, rso)) return GDN_ERR_ALIAS;
+    if (overlap(ro, rsi) || overlap(rS, rsi)) return GDN_ERR_ALIAS;
+    if (overlap(rso, rsi) && rso.lo != rsi.lo) return GDN_ERR_ALIAS;
+    if (units == 0) return GDN_OK;
+    gdn::DecodePreopArgs p{xq, xk, xv, a, b, conv_w, state_in, state_out, eps, S, units, H,
+                           io_dtype == GDN_BF16, o, state_hint == GDN_STATE_STREAMING};
+    const hipError_t e = gdn::launch_decode_preop(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 int gdn_decode_step_ex(const void *q, const void *k, const void *v, int io_dtype,
                        const float *g, const float *beta, float *S, int64_t B,
                        int64_t H, int64_t dk, int64_t dv, int state_hint, void *o,

@@ -139,7 +139,152 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
     }
 }
 
+// The decode step with the block's pre-operations in front, for one token per
+// sequence: from the raw projections xq, xk, xv and the gate inputs a, b, with
+// each sequence's causal-conv FIFO read and advanced, to o and the new state.
+// The pre-operations are those of gdn_preop (conv over the FIFO rows and the
+// token, silu, L2 norm of q and k, g = -softplus(a), beta = sigmoid(b)); q, k
+// and v stay fp32 on chip.  One 512-thread workgroup per head state: its two
+// halves do the two 64-column halves exactly as decode_kernel does, after the
+// workgroup has made q, k, v, g and beta in LDS.  The workgroup owns its head's
+// FIFO rows, so they can be advanced in place.  The state loads are issued
+// first, so that their latency covers the pre-operations.
+template <typename IO, bool kStream>
+__global__ __launch_bounds__(512) void decode_preop_kernel(
+    const IO *__restrict__ xq, const IO *__restrict__ xk, const IO *__restrict__ xv,
+    const float *__restrict__ ga, const float *__restrict__ gb, const float *__restrict__ conv_w,
+    const IO *state_in, IO *state_out, float eps, float *__restrict__ S, int64_t H,
+    IO *__restrict__ o) {
+    const int64_t u = blockIdx.x;               // head state n * H + h
+    const int64_t n = u / H, h = u % H;
+    const int tid = threadIdx.x;
+    const int half = tid >> 8, t = tid & 255;   // value columns [64 half, 64 half + 64)
+    const int lane = t & 63, w = t >> 6;
+    const int cg = lane & 15;
+    const int rp = 4 * w + (lane >> 4);
+    float *Su = S + u * (kHeadDim * kHeadDim) + 64 * half;
+
+    __shared__ float sq[kHeadDim], sk[kHeadDim], sv[kHeadDim];
+    __shared__ float nrm[2][2];                 // (q, k) x two waves: partial sums of y^2
+    __shared__ float sgate[2];                  // g, beta
+    __shared__ float4 red_a[2][4][16], red_b[2][4][16];
+
+    float4 s[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) s[m] = load_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 4 * cg);
+
+    // pre-operations: thread tid < 384 makes channel c of stream st (q, k, v)
+    float y = 0.f;
+    const int st = tid >> 7, c = tid & (kHeadDim - 1);
+    if (tid < 3 * kHeadDim) {
+        const IO *x = st == 0 ? xq : (st == 1 ? xk : xv);
+        const int64_t fi = ((n * 3 + st) * H + h) * 3 * kHeadDim + c;   // FIFO row j at fi + j D
+        const IO r0 = state_in[fi], r1 = state_in[fi + kHeadDim], r2 = state_in[fi + 2 * kHeadDim];
+        const IO xr = x[u * kHeadDim + c];
+        const float4 wc = *reinterpret_cast<const float4 *>(conv_w + ((st * H + h) * kHeadDim + c) * 4);
+        const float cv = wc.x * to_f32(r0) + wc.y * to_f32(r1) + wc.z * to_f32(r2) + wc.w * to_f32(xr);
+        y = cv * __builtin_amdgcn_rcpf(1.f + __expf(-cv));
+        // the FIFO's rows move up by one (all three were read above, by this thread)
+        state_out[fi] = r1;
+        state_out[fi + kHeadDim] = r2;
+        state_out[fi + 2 * kHeadDim] = xr;
+        if (st < 2) {
+            float ss = y * y;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+            if (lane == 0) nrm[st][(tid >> 6) & 1] = ss;
+        }
+    } else if (tid == 3 * kHeadDim) {
+        const float av = ga[u], bv = gb[u];
+        // softplus(av) = max(av, 0) + log1p(exp(-|av|)), without overflow
+        sgate[0] = -(fmaxf(av, 0.f) + log1pf(__expf(-fabsf(av))));
+        sgate[1] = 1.f / (1.f + __expf(-bv));
+    }
+    __syncthreads();
+    if (tid < 3 * kHeadDim) {
+        if (st < 2) y *= rsqrtf(nrm[st][0] + nrm[st][1] + eps);
+        (st == 0 ? sq : (st == 1 ? sk : sv))[c] = y;
+    }
+    __syncthreads();
+
+    // the step itself, as decode_kernel, per half
+    const int c0 = 64 * half + 4 * cg;
+    const float4 vv = make_float4(sv[c0], sv[c0 + 1], sv[c0 + 2], sv[c0 + 3]);
+    const float d = expf(sgate[0]);
+    const float bt = sgate[1];
+    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float kr = sk[rp + 16 * m], qr = sq[rp + 16 * m];
+        a.x += s[m].x * kr; a.y += s[m].y * kr; a.z += s[m].z * kr; a.w += s[m].w * kr;
+        b.x += s[m].x * qr; b.y += s[m].y * qr; b.z += s[m].z * qr; b.w += s[m].w * qr;
+    }
+#pragma unroll
+    for (int off = 16; off <= 32; off <<= 1) {
+        a.x += __shfl_xor(a.x, off); a.y += __shfl_xor(a.y, off);
+        a.z += __shfl_xor(a.z, off); a.w += __shfl_xor(a.w, off);
+        b.x += __shfl_xor(b.x, off); b.y += __shfl_xor(b.y, off);
+        b.z += __shfl_xor(b.z, off); b.w += __shfl_xor(b.w, off);
+    }
+    if (lane < 16) {
+        red_a[half][w][cg] = a;
+        red_b[half][w][cg] = b;
+    }
+    float qk = sq[lane] * sk[lane] + sq[lane + 64] * sk[lane + 64];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off);
+    __syncthreads();
+
+    float4 A = red_a[half][0][cg], Bq = red_b[half][0][cg];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) {
+        const float4 x = red_a[half][ww][cg], yq = red_b[half][ww][cg];
+        A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
+        Bq.x += yq.x; Bq.y += yq.y; Bq.z += yq.z; Bq.w += yq.w;
+    }
+    float4 dl;
+    dl.x = bt * (vv.x - d * A.x);
+    dl.y = bt * (vv.y - d * A.y);
+    dl.z = bt * (vv.z - d * A.z);
+    dl.w = bt * (vv.w - d * A.w);
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+        const float kr = sk[rp + 16 * m];
+        float4 x = s[m];
+        x.x = d * x.x + kr * dl.x;
+        x.y = d * x.y + kr * dl.y;
+        x.z = d * x.z + kr * dl.z;
+        x.w = d * x.w + kr * dl.w;
+        store_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 4 * cg, x);
+    }
+    if (rp == 0) {
+        IO *ou = o + u * kHeadDim + c0;
+        ou[0] = from_f32<IO>(d * Bq.x + qk * dl.x);
+        ou[1] = from_f32<IO>(d * Bq.y + qk * dl.y);
+        ou[2] = from_f32<IO>(d * Bq.z + qk * dl.z);
+        ou[3] = from_f32<IO>(d * Bq.w + qk * dl.w);
+    }
+}
+
 }  // namespace
+
+template <typename IO>
+void launch_decode_preop_io(const DecodePreopArgs &a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.units)), block(512);
+    auto kern = a.stream_state ? decode_preop_kernel<IO, true> : decode_preop_kernel<IO, false>;
+    kern<<<grid, block, 0, stream>>>(
+        static_cast<const IO *>(a.xq), static_cast<const IO *>(a.xk), static_cast<const IO *>(a.xv),
+        a.a, a.b, a.conv_w, static_cast<const IO *>(a.state_in), static_cast<IO *>(a.state_out),
+        a.eps, a.S, a.H, static_cast<IO *>(a.o));
+}
+
+hipError_t launch_decode_preop(const DecodePreopArgs &a, hipStream_t stream) {
+    if (a.bf16)
+        launch_decode_preop_io<__hip_bfloat16>(a, stream);
+    else
+        launch_decode_preop_io<float>(a, stream);
+    return hipGetLastError();
+}
 
 template <typename IO>
 void launch_decode_io(const DecodeArgs &a, hipStream_t stream) {

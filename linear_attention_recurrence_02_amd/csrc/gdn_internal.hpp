@@ -53,6 +53,21 @@ struct DecodeArgs {
     bool stream_state = false;
 };
 
+// A validated decode step with the pre-operations fused in front.
+struct DecodePreopArgs {
+    const void *xq, *xk, *xv;   // raw projections [units, 128]
+    const float *a, *b;         // gate inputs [units]
+    const float *conv_w;        // [3, H, 128, 4]
+    const void *state_in;       // FIFO [N, 3, H, 3, 128] io dtype
+    void *state_out;            // same shape: exactly state_in, or disjoint
+    float eps;
+    float *S;                   // [units, 128, 128]
+    int64_t units, H;
+    bool bf16;
+    void *o;
+    bool stream_state;
+};
+
 // A validated pre-operation call (conv FIFO, silu, L2 norm, gates).
 struct PreopArgs {
     const void *xq, *xk, *xv;   // raw projections [rows, H, 128]
@@ -69,6 +84,7 @@ struct PreopArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_decode_preop(const DecodePreopArgs &a, hipStream_t stream);
 // Helpers of the segmented prompt form (see gdn_segmented.hip).
 hipError_t launch_segment_prep(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
                                int32_t *seg, int32_t *cu_out, void *vzero, int64_t vzero_bytes,

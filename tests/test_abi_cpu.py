@@ -257,6 +257,31 @@ def test_decode_ex_validation(lib):
         assert ex(hint, B=0) == binding.GDN_OK
 
 
+def test_decode_preop_validation(lib):
+    def dp(**kw):
+        a = dict(xq=A, xk=A + MB, xv=A + 2 * MB, dtype=1, a=A + 3 * MB, b=A + 4 * MB,
+                 w=A + 5 * MB, si=A + 6 * MB, so=A + 6 * MB, eps=1e-6, S=A + 16 * MB, B=4, H=2,
+                 dk=128, dv=128, hint=0, o=A + 64 * MB)
+        a.update(kw)
+        return lib.gdn_decode_step_preop(a["xq"], a["xk"], a["xv"], a["dtype"], a["a"], a["b"],
+                                         a["w"], a["si"], a["so"], a["eps"], a["S"], a["B"],
+                                         a["H"], a["dk"], a["dv"], a["hint"], a["o"], None)
+    assert dp(hint=2) == binding.GDN_ERR_UNSUPPORTED
+    assert dp(dtype=3) == binding.GDN_ERR_UNSUPPORTED
+    assert dp(dk=64) == binding.GDN_ERR_UNSUPPORTED
+    assert dp(w=None) == binding.GDN_ERR_INVALID_ARG
+    assert dp(si=None) == binding.GDN_ERR_INVALID_ARG
+    assert dp(eps=-1.0) == binding.GDN_ERR_INVALID_ARG
+    assert dp(eps=float("inf")) == binding.GDN_ERR_INVALID_ARG
+    assert dp(xq=A + 8) == binding.GDN_ERR_INVALID_ARG                  # misaligned
+    assert dp(o=A + 16 * MB) == binding.GDN_ERR_ALIAS                   # o over S
+    assert dp(S=A) == binding.GDN_ERR_ALIAS                             # S over xq
+    assert dp(so=A + 6 * MB + 256) == binding.GDN_ERR_ALIAS             # FIFO partly in place
+    assert dp(so=A + 3 * MB) == binding.GDN_ERR_ALIAS                   # new FIFO over a
+    assert dp(B=0) == binding.GDN_OK
+    assert dp(so=A + 8 * MB, B=0) == binding.GDN_OK                     # out of place
+
+
 def test_binding_refuses_host_tensors():
     import torch
     x = torch.zeros(1, 4, 1, 128)

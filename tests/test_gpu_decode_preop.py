@@ -1,0 +1,116 @@
+"""GPU parity of gdn_decode_step_preop (the decode step with the pre-operations
+fused in front) against the fp64 oracle chain oracle.preop -> oracle.decode,
+through the C ABI.
+
+The chain keeps q, k, v in fp64 between the two steps, as the fused kernel keeps
+them in fp32, so the decode bar applies as it is: o within 2e-3 per slice with
+its bf16 rounding allowed elementwise, S within 2e-3 (1e-5 for fp32 inputs); the
+FIFO holds copies of raw rows and must match bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_attention_recurrence_02_amd import inputs
+from linear_attention_recurrence_02_amd.binding import gdn_decode_step_preop
+from metrics import TOL_BF16, TOL_F32, bf16_output_ok, worst_slice_error
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def draw_steps(B, H, steps, io_dtype, seed):
+    """``steps`` one-token pre-operation inputs for a batch of B x H, a FIFO
+    state, conv weights and a decode state S0."""
+    p = inputs.preop_inputs(B, steps, H, io_dtype=io_dtype, seed=seed, device=DEV)
+    w = inputs.decode_workload(1, B, H, io_dtype=io_dtype, seed=seed + 1, device=DEV)
+    return p, w.S0
+
+
+def run_chain(B, H, steps, io_dtype, seed, streaming=False, out_of_place=False):
+    p, S0 = draw_steps(B, H, steps, io_dtype, seed)
+    S = S0.clone()
+    state = p.state.clone()
+    os_ = []
+    for t in range(steps):
+        sl = lambda x: x[:, t].contiguous()
+        if out_of_place:
+            new_state = torch.empty_like(state)
+            o = gdn_decode_step_preop(sl(p.xq), sl(p.xk), sl(p.xv), sl(p.a), sl(p.b), p.conv_w,
+                                      state, S, state_out=new_state, streaming=streaming)
+            torch.cuda.synchronize()
+            state = new_state
+        else:
+            o = gdn_decode_step_preop(sl(p.xq), sl(p.xk), sl(p.xv), sl(p.a), sl(p.b), p.conv_w,
+                                      state, S, streaming=streaming)
+        os_.append(o.clone())
+    torch.cuda.synchronize()
+    # the oracle chain, step by step, from the same inputs
+    Sr = S0
+    st_r = p.state
+    ors = []
+    for t in range(steps):
+        sl = lambda x: x[:, t:t + 1]
+        q, k, v, g, beta, st_r = oracle.preop(sl(p.xq), sl(p.xk), sl(p.xv), sl(p.a), sl(p.b),
+                                              p.conv_w, st_r)
+        o_r, Sr = oracle.decode(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], Sr)
+        ors.append(o_r)
+    return p, os_, S, state, ors, Sr, st_r
+
+
+def check(label, io_dtype, os_, S, state, ors, Sr, st_r):
+    B, H = S.shape[:2]
+    spans = [(b, 0, 1) for b in range(B)]
+    tol = TOL_F32 if io_dtype == torch.float32 else TOL_BF16
+    worst = 0.0
+    for t, (o, o_r) in enumerate(zip(os_, ors)):
+        if io_dtype == torch.float32:
+            e = worst_slice_error(o[:, None], o_r[:, None], spans, H)
+            worst = max(worst, e)
+            assert e <= tol, (label, t, e)
+        else:
+            ok, ratio = bf16_output_ok(o[:, None], o_r[:, None], tol, spans, H)
+            worst = max(worst, ratio)
+            assert ok, (label, t, ratio)
+    es = worst_slice_error(S, Sr)
+    say(f"[{label}] o worst {worst:.3e}, S {es:.3e}")
+    assert es <= tol, (label, es)
+    assert np.array_equal(state.double().cpu().numpy(), np.asarray(st_r)), label
+
+
+@pytest.mark.parametrize("io_dtype", [torch.bfloat16, torch.float32])
+def test_fused_steps_match_the_oracle_chain(io_dtype):
+    # five steps in a row: the FIFO and the state carry over
+    p, os_, S, state, ors, Sr, st_r = run_chain(8, 4, 5, io_dtype, seed=61)
+    check(f"fused x5 {io_dtype}", io_dtype, os_, S, state, ors, Sr, st_r)
+
+
+def test_fused_out_of_place_fifo_and_streaming():
+    p, os_, S, state, ors, Sr, st_r = run_chain(8, 4, 3, torch.bfloat16, seed=62,
+                                                streaming=True, out_of_place=True)
+    check("fused x3, FIFO out of place, streaming state", torch.bfloat16, os_, S, state, ors,
+          Sr, st_r)
+
+
+def test_fused_decode_shape_one_step():
+    # the batched-decode shape: 64 sequences x 16 heads
+    p, os_, S, state, ors, Sr, st_r = run_chain(64, 16, 1, torch.bfloat16, seed=63)
+    check("fused, 64 x 16", torch.bfloat16, os_, S, state, ors, Sr, st_r)
+
+
+def test_streaming_hint_is_bit_identical():
+    p, S0 = draw_steps(16, 4, 1, torch.bfloat16, seed=64)
+    outs = []
+    for streaming in (False, True):
+        S, st = S0.clone(), p.state.clone()
+        o = gdn_decode_step_preop(p.xq[:, 0].contiguous(), p.xk[:, 0].contiguous(),
+                                  p.xv[:, 0].contiguous(), p.a[:, 0].contiguous(),
+                                  p.b[:, 0].contiguous(), p.conv_w, st, S, streaming=streaming)
+        torch.cuda.synchronize()
+        outs.append((o, S, st))
+    assert all(torch.equal(x, y) for x, y in zip(outs[0], outs[1]))
