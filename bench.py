@@ -170,8 +170,8 @@ def time_calls(torch, call, iters, reps=3):
 def bench_decode_preop(torch, gdn, inputs, steps):
     """Decode steps from the raw projections at the batched-decode shape (64 x 16),
     each form captured as one graph of ``steps`` steps: the fused
-    gdn_decode_step_preop (one kernel a step) against gdn_preop followed by
-    gdn_decode_step (three).  The same token's projections feed every step (the
+    gdn_decode_step_preop (one kernel a step; also with the gated norm on the
+    output) against gdn_preop followed by gdn_decode_step (three).  The same token's projections feed every step (the
     time does not depend on the values).  Returns microseconds per step."""
     p = inputs.preop_inputs(64, 1, 16, seed=5, device="cuda")
     S = inputs.decode_workload(1, 64, 16, seed=6, device="cuda").S0.clone()
@@ -181,8 +181,15 @@ def bench_decode_preop(torch, gdn, inputs, steps):
     o = torch.empty_like(x3[2])
     pre = [torch.empty_like(p.xq) for _ in range(3)] + [torch.empty_like(p.a) for _ in range(2)]
 
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    gate = (torch.randn(64, 16, 128, generator=gen, device="cuda").to(p.xq.dtype),
+            0.5 + torch.rand(128, generator=gen, device="cuda"), 1e-6)
+
     def fused():
         gdn.gdn_decode_step_preop(*x3, a2, b2, p.conv_w, state, S, o=o)
+
+    def fused_gated():
+        gdn.gdn_decode_step_preop(*x3, a2, b2, p.conv_w, state, S, gate=gate, o=o)
 
     def separate():
         gdn.gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, state, out=pre)
@@ -190,7 +197,7 @@ def bench_decode_preop(torch, gdn, inputs, steps):
                             pre[4][:, 0], S, o=o)
 
     out = {}
-    for name, f in (("fused", fused), ("separate", separate)):
+    for name, f in (("fused", fused), ("fused_gated", fused_gated), ("separate", separate)):
         for _ in range(3):
             f()
         torch.cuda.synchronize()
@@ -491,8 +498,10 @@ def main():
     if args.only in (None, "decode") and not args.cold and not args.streaming:
         dp = bench_decode_preop(torch, gdn, inputs, min(args.steps, 200))
         result["decode"]["preop_fused_us"] = dp["fused"]
+        result["decode"]["preop_gated_fused_us"] = dp["fused_gated"]
         result["decode"]["preop_then_decode_us"] = dp["separate"]
-        log(f"decode from raw projections: fused {dp['fused']:.2f} us/step, "
+        log(f"decode from raw projections: fused {dp['fused']:.2f} us/step "
+            f"({dp['fused_gated']:.2f} with the gated norm), "
             f"pre-operations then decode {dp['separate']:.2f} us/step")
         torch.cuda.empty_cache()
 

@@ -350,16 +350,21 @@ int gdn_decode_step_ex(const void *q, const void *k, const void *v, int io_dtype
  *               same shape, either exactly state_in (advanced in place) or
  *               disjoint
  *   eps         finite and >= 0
+ *   z, norm_w, norm_eps  NULL z gives the step's o.  Otherwise o receives the
+ *               block's gated RMS norm of it, as gdn_chunk_prefill_gated
+ *               applies it: y = norm_w o / sqrt(mean(o^2) + norm_eps) silu(z),
+ *               on the fp32 o, with z [B, H, 128] io_dtype (16-byte aligned),
+ *               norm_w [128] fp32 and norm_eps finite and >= 0.
  *   S, B, H, dk, dv, o: as for gdn_decode_step; state_hint as for
  *               gdn_decode_step_ex.
- *   o, S and state_out must not overlap the inputs or each other (save
- *   state_out == state_in) (GDN_ERR_ALIAS).
+ *   o, S and state_out must not overlap the inputs (z and norm_w included) or
+ *   each other (save state_out == state_in) (GDN_ERR_ALIAS).
  */
 int gdn_decode_step_preop(const void *xq, const void *xk, const void *xv, int io_dtype,
                           const float *a, const float *b, const float *conv_w,
-                          const void *state_in, void *state_out, float eps, float *S, int64_t B,
-                          int64_t H, int64_t dk, int64_t dv, int state_hint, void *o,
-                          void *stream);
+                          const void *state_in, void *state_out, float eps, const void *z,
+                          const float *norm_w, float norm_eps, float *S, int64_t B, int64_t H,
+                          int64_t dk, int64_t dv, int state_hint, void *o, void *stream);
 
 #ifdef __cplusplus
 }

@@ -82,8 +82,8 @@ def load_library(path: Optional[str] = None):
                                        i64, ctypes.c_int, vp, vp]
     lib.gdn_decode_step_ex.restype = ctypes.c_int
     lib.gdn_decode_step_preop.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
-                                          ctypes.c_float, vp, i64, i64, i64, i64, ctypes.c_int,
-                                          vp, vp]
+                                          ctypes.c_float, vp, vp, ctypes.c_float, vp, i64, i64,
+                                          i64, i64, ctypes.c_int, vp, vp]
     lib.gdn_decode_step_preop.restype = ctypes.c_int
     if path is None:
         _lib = lib
@@ -368,15 +368,17 @@ def gdn_decode_step(q, k, v, g, beta, S, *, o=None, stream=None, streaming=False
 
 
 def gdn_decode_step_preop(xq, xk, xv, a, b, conv_w, state, S, eps=1e-6, *, state_out=None,
-                          o=None, stream=None, streaming=False):
+                          gate=None, o=None, stream=None, streaming=False):
     """One decode step from the raw projections: the pre-operations (conv FIFO,
     silu, L2 norm of q and k, gates) and the step in one launch.
 
     xq, xk, xv: [B, H, 128] (bf16 or fp32); a, b: [B, H] fp32;
     conv_w: [3, H, 128, 4] fp32; state: [B, 3, H, 3, 128] with xq's dtype,
     advanced in place unless ``state_out`` is given; S: [B, H, 128, 128] fp32,
-    updated in place.  streaming=True moves S with non-temporal loads and
-    stores.  Returns o [B, H, 128]."""
+    updated in place.  gate = (z, norm_w, norm_eps) applies the gated RMS norm
+    to the output row (z [B, H, 128] with xq's dtype, norm_w [128] fp32).
+    streaming=True moves S with non-temporal loads and stores.  Returns o
+    [B, H, 128]."""
     B, H, dk = xq.shape
     dv = xv.shape[-1]
     if xk.shape != xq.shape or xv.shape[:2] != (B, H) or xk.dtype != xq.dtype \
@@ -392,11 +394,16 @@ def gdn_decode_step_preop(xq, xk, xv, a, b, conv_w, state, S, eps=1e-6, *, state
         raise ValueError("state_out must match state")
     if o is None:
         o = torch.empty_like(xv)
+    z, norm_w, norm_eps = gate if gate is not None else (None, None, 0.0)
+    if z is not None and (z.shape != xv.shape or z.dtype != xq.dtype
+                          or norm_w.shape != (dv,)):
+        raise ValueError("gate: z must match xv, norm_w be [128]")
     st = load_library().gdn_decode_step_preop(
         _ptr(xq, name="xq"), _ptr(xk, name="xk"), _ptr(xv, name="xv"), _io_dtype(xq),
         _ptr(a, torch.float32, "a"), _ptr(b, torch.float32, "b"),
         _ptr(conv_w, torch.float32, "conv_w"), _ptr(state, xq.dtype, "state"),
-        _ptr(state_out, xq.dtype, "state_out"), float(eps), _ptr(S, torch.float32, "S"),
+        _ptr(state_out, xq.dtype, "state_out"), float(eps), _ptr(z, xq.dtype, "z"),
+        _ptr(norm_w, torch.float32, "norm_w"), float(norm_eps), _ptr(S, torch.float32, "S"),
         B, H, dk, dv, GDN_STATE_STREAMING if streaming else GDN_STATE_CACHED,
         _ptr(o, xq.dtype, "o"), _stream(stream))
     _check(st)

@@ -432,9 +432,9 @@ int gdn_decode_step(const void *q, const void *k, const void *v, int io_dtype,
 
 int gdn_decode_step_preop(const void *xq, const void *xk, const void *xv, int io_dtype,
                           const float *a, const float *b, const float *conv_w,
-                          const void *state_in, void *state_out, float eps, float *S, int64_t B,
-                          int64_t H, int64_t dk, int64_t dv, int state_hint, void *o,
-                          void *stream) {
+                          const void *state_in, void *state_out, float eps, const void *z,
+                          const float *norm_w, float norm_eps, float *S, int64_t B, int64_t H,
+                          int64_t dk, int64_t dv, int state_hint, void *o, void *stream) {
     if (state_hint != GDN_STATE_CACHED && state_hint != GDN_STATE_STREAMING)
         return GDN_ERR_UNSUPPORTED;
     if (!xq || !xk || !xv || !a || !b || !conv_w || !state_in || !state_out || !S || !o)
@@ -443,6 +443,9 @@ int gdn_decode_step_preop(const void *xq, const void *xk, const void *xv, int io
     if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
     if (dk != gdn::kHeadDim || dv != gdn::kHeadDim) return GDN_ERR_UNSUPPORTED;
     if (!(eps >= 0.f && eps <= FLT_MAX)) return GDN_ERR_INVALID_ARG;
+    if (z && (!norm_w || !aligned(z, 16) || !aligned(norm_w, 4) ||
+              !(norm_eps >= 0.f && norm_eps <= FLT_MAX)))
+        return GDN_ERR_INVALID_ARG;
     for (const void *p : {xq, xk, xv, static_cast<const void *>(conv_w), state_in,
                           static_cast<const void *>(state_out), static_cast<const void *>(S),
                           static_cast<const void *>(o)})
@@ -460,8 +463,10 @@ int gdn_decode_step_preop(const void *xq, const void *xk, const void *xv, int io
                 rS = span_of(S, units * gdn::kHeadDim * gdn::kHeadDim * 4), ro = span_of(o, vec);
     // outputs (o, S, the new FIFO) apart from every input and from each other;
     // the FIFO may be advanced in place
+    const Range rz = z ? span_of(z, vec) : Range{0, 0},
+                rnw = z ? span_of(norm_w, gdn::kHeadDim * 4) : Range{0, 0};
     for (Range out : {ro, rS, rso})
-        for (Range in : {rxq, rxk, rxv, ra, rb, rw})
+        for (Range in : {rxq, rxk, rxv, ra, rb, rw, rz, rnw})
             if (overlap(out, in)) return GDN_ERR_ALIAS;
     if (overlap(ro, rS) || overlap(ro, rso) || overlap(rS, rso)) return GDN_ERR_ALIAS;
     if (overlap(ro, rsi) || overlap(rS, rsi)) return GDN_ERR_ALIAS;
@@ -469,6 +474,9 @@ int gdn_decode_step_preop(const void *xq, const void *xk, const void *xv, int io
     if (units == 0) return GDN_OK;
     gdn::DecodePreopArgs p{xq, xk, xv, a, b, conv_w, state_in, state_out, eps, S, units, H,
                            io_dtype == GDN_BF16, o, state_hint == GDN_STATE_STREAMING};
+    p.z = z;
+    p.norm_w = norm_w;
+    p.norm_eps = norm_eps;
     const hipError_t e = gdn::launch_decode_preop(p, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }

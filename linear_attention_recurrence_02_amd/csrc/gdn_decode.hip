@@ -148,12 +148,15 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
 // halves do the two 64-column halves exactly as decode_kernel does, after the
 // workgroup has made q, k, v, g and beta in LDS.  The workgroup owns its head's
 // FIFO rows, so they can be advanced in place.  The state loads are issued
-// first, so that their latency covers the pre-operations.
-template <typename IO, bool kStream>
+// first, so that their latency covers the pre-operations.  kGated applies the
+// block's gated RMS norm to the output row, y = w o / sqrt(mean(o^2) + eps)
+// silu(z), on the fp32 o, the whole row being in this workgroup.
+template <typename IO, bool kStream, bool kGated>
 __global__ __launch_bounds__(512) void decode_preop_kernel(
     const IO *__restrict__ xq, const IO *__restrict__ xk, const IO *__restrict__ xv,
     const float *__restrict__ ga, const float *__restrict__ gb, const float *__restrict__ conv_w,
-    const IO *state_in, IO *state_out, float eps, float *__restrict__ S, int64_t H,
+    const IO *state_in, IO *state_out, float eps, const IO *__restrict__ z,
+    const float *__restrict__ norm_w, float norm_eps, float *__restrict__ S, int64_t H,
     IO *__restrict__ o) {
     const int64_t u = blockIdx.x;               // head state n * H + h
     const int64_t n = u / H, h = u % H;
@@ -257,12 +260,32 @@ __global__ __launch_bounds__(512) void decode_preop_kernel(
         x.w = d * x.w + kr * dl.w;
         store_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 4 * cg, x);
     }
+    // lanes 0..15 of each half's first wave (rp = 0) own the output columns c0..c0+3
+    float ov[4] = {d * Bq.x + qk * dl.x, d * Bq.y + qk * dl.y, d * Bq.z + qk * dl.z,
+                   d * Bq.w + qk * dl.w};
+    if constexpr (kGated) {
+        __shared__ float osq[2];
+        if (w == 0) {
+            float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
+#pragma unroll
+            for (int off = 8; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);   // lanes 0..15
+            if (lane == 0) osq[half] = ss;
+        }
+        __syncthreads();
+        if (rp == 0) {
+            const float rs = __builtin_amdgcn_rsqf((osq[0] + osq[1]) * (1.f / kHeadDim) + norm_eps);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float zf = to_f32(z[u * kHeadDim + c0 + e]);
+                const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-zf));
+                ov[e] = norm_w[c0 + e] * (ov[e] * rs) * (zf * sg);
+            }
+        }
+    }
     if (rp == 0) {
         IO *ou = o + u * kHeadDim + c0;
-        ou[0] = from_f32<IO>(d * Bq.x + qk * dl.x);
-        ou[1] = from_f32<IO>(d * Bq.y + qk * dl.y);
-        ou[2] = from_f32<IO>(d * Bq.z + qk * dl.z);
-        ou[3] = from_f32<IO>(d * Bq.w + qk * dl.w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ou[e] = from_f32<IO>(ov[e]);
     }
 }
 
@@ -271,11 +294,15 @@ __global__ __launch_bounds__(512) void decode_preop_kernel(
 template <typename IO>
 void launch_decode_preop_io(const DecodePreopArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.units)), block(512);
-    auto kern = a.stream_state ? decode_preop_kernel<IO, true> : decode_preop_kernel<IO, false>;
+    auto kern = a.z ? (a.stream_state ? decode_preop_kernel<IO, true, true>
+                                      : decode_preop_kernel<IO, false, true>)
+                    : (a.stream_state ? decode_preop_kernel<IO, true, false>
+                                      : decode_preop_kernel<IO, false, false>);
     kern<<<grid, block, 0, stream>>>(
         static_cast<const IO *>(a.xq), static_cast<const IO *>(a.xk), static_cast<const IO *>(a.xv),
         a.a, a.b, a.conv_w, static_cast<const IO *>(a.state_in), static_cast<IO *>(a.state_out),
-        a.eps, a.S, a.H, static_cast<IO *>(a.o));
+        a.eps, static_cast<const IO *>(a.z), a.norm_w, a.norm_eps, a.S, a.H,
+        static_cast<IO *>(a.o));
 }
 
 hipError_t launch_decode_preop(const DecodePreopArgs &a, hipStream_t stream) {

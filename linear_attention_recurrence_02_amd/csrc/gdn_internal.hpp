@@ -66,6 +66,10 @@ struct DecodePreopArgs {
     bool bf16;
     void *o;
     bool stream_state;
+    // Gated RMS norm on the output row (null z: plain o)
+    const void *z = nullptr;
+    const float *norm_w = nullptr;
+    float norm_eps = 0.f;
 };
 
 // A validated pre-operation call (conv FIFO, silu, L2 norm, gates).

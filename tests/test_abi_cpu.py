@@ -260,12 +260,13 @@ def test_decode_ex_validation(lib):
 def test_decode_preop_validation(lib):
     def dp(**kw):
         a = dict(xq=A, xk=A + MB, xv=A + 2 * MB, dtype=1, a=A + 3 * MB, b=A + 4 * MB,
-                 w=A + 5 * MB, si=A + 6 * MB, so=A + 6 * MB, eps=1e-6, S=A + 16 * MB, B=4, H=2,
-                 dk=128, dv=128, hint=0, o=A + 64 * MB)
+                 w=A + 5 * MB, si=A + 6 * MB, so=A + 6 * MB, eps=1e-6, z=None, nw=None,
+                 neps=1e-6, S=A + 16 * MB, B=4, H=2, dk=128, dv=128, hint=0, o=A + 64 * MB)
         a.update(kw)
         return lib.gdn_decode_step_preop(a["xq"], a["xk"], a["xv"], a["dtype"], a["a"], a["b"],
-                                         a["w"], a["si"], a["so"], a["eps"], a["S"], a["B"],
-                                         a["H"], a["dk"], a["dv"], a["hint"], a["o"], None)
+                                         a["w"], a["si"], a["so"], a["eps"], a["z"], a["nw"],
+                                         a["neps"], a["S"], a["B"], a["H"], a["dk"], a["dv"],
+                                         a["hint"], a["o"], None)
     assert dp(hint=2) == binding.GDN_ERR_UNSUPPORTED
     assert dp(dtype=3) == binding.GDN_ERR_UNSUPPORTED
     assert dp(dk=64) == binding.GDN_ERR_UNSUPPORTED
@@ -280,6 +281,12 @@ def test_decode_preop_validation(lib):
     assert dp(so=A + 3 * MB) == binding.GDN_ERR_ALIAS                   # new FIFO over a
     assert dp(B=0) == binding.GDN_OK
     assert dp(so=A + 8 * MB, B=0) == binding.GDN_OK                     # out of place
+    # the gated norm: z needs norm_w and a finite eps >= 0; outputs apart from z
+    assert dp(z=A + 7 * MB) == binding.GDN_ERR_INVALID_ARG              # no norm_w
+    assert dp(z=A + 7 * MB, nw=A + 7 * MB + 65536, neps=-1.0) == binding.GDN_ERR_INVALID_ARG
+    assert dp(z=A + 7 * MB + 8, nw=A + 7 * MB + 65536) == binding.GDN_ERR_INVALID_ARG
+    assert dp(z=A + 64 * MB, nw=A + 7 * MB) == binding.GDN_ERR_ALIAS    # o over z
+    assert dp(z=A + 7 * MB, nw=A + 7 * MB + 65536, B=0) == binding.GDN_OK
 
 
 def test_binding_refuses_host_tensors():

@@ -14,7 +14,7 @@ import torch
 import oracle
 from linear_attention_recurrence_02_amd import inputs
 from linear_attention_recurrence_02_amd.binding import gdn_decode_step_preop
-from metrics import TOL_BF16, TOL_F32, bf16_output_ok, worst_slice_error
+from metrics import TOL_BF16, TOL_F32, bf16_half_ulp, bf16_output_ok, worst_slice_error
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -114,3 +114,33 @@ def test_streaming_hint_is_bit_identical():
         torch.cuda.synchronize()
         outs.append((o, S, st))
     assert all(torch.equal(x, y) for x, y in zip(outs[0], outs[1]))
+
+
+@pytest.mark.parametrize("io_dtype", [torch.bfloat16, torch.float32])
+def test_fused_gated_norm_matches_the_oracle_chain(io_dtype):
+    # pre-operations -> step -> gated RMS norm of o, in one call, against
+    # oracle.preop -> oracle.decode -> oracle.gated_rmsnorm; Y row by row
+    # (|y - r| <= tol * max_row |r|, plus half an ulp of a bf16 output)
+    B, H = 8, 4
+    p, S0 = draw_steps(B, H, 1, io_dtype, seed=65)
+    gen = torch.Generator(device=DEV).manual_seed(65 + 7919)
+    z = torch.randn(B, H, 128, generator=gen, device=DEV).to(io_dtype)
+    norm_w = 0.5 + torch.rand(128, generator=gen, device=DEV)
+    x = [t[:, 0].contiguous() for t in (p.xq, p.xk, p.xv, p.a, p.b)]
+    S, st = S0.clone(), p.state.clone()
+    y = gdn_decode_step_preop(*x, p.conv_w, st, S, gate=(z, norm_w, 1e-6))
+    torch.cuda.synchronize()
+    q, k, v, g, beta, st_r = oracle.preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, p.state)
+    o_r, S_r = oracle.decode(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0)
+    y_r = oracle.gated_rmsnorm(o_r, z, norm_w, 1e-6)
+    tol = TOL_F32 if io_dtype == torch.float32 else TOL_BF16
+    yg = y.double().cpu().numpy().reshape(-1, 128)
+    yr = np.asarray(y_r).reshape(-1, 128)
+    bound = tol * np.abs(yr).max(axis=1, keepdims=True)
+    if io_dtype == torch.bfloat16:
+        bound = bound + bf16_half_ulp(np.maximum(np.abs(yg), np.abs(yr)))
+    ratio = float((np.abs(yg - yr) / bound).max())
+    es = worst_slice_error(S, S_r)
+    say(f"[fused gated {io_dtype}] Y bound ratio {ratio:.3f}, S {es:.3e}")
+    assert ratio <= 1.0 and es <= tol
+    assert np.array_equal(st.double().cpu().numpy(), np.asarray(st_r))
