@@ -247,7 +247,7 @@ struct Producer {
         r16 = opaque(r16);
         q = opaque(q);
         const f16 *Kn = sm.K[nb], *Qn = sm.Q[nb];
-        const float *G2 = sm.G2[nb], *Bt = sm.Bt[nb], *EG = sm.EG[nb];
+        const float *G2 = sm.G2[nb], *Bt = sm.Bt[nb];
         constexpr int JM = P > IB ? P : IB;   // K row blocks read: 0..JM
         f32x4 kk[P + 1], qa[IB + 1];
 #pragma unroll
