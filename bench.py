@@ -151,6 +151,36 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold, streaming=False):
     return dict(units=units, wall_s=wall, gpu_ms=gpu_ms, eager_s=eager, workload=w)
 
 
+def state_traffic_ceiling(torch, S0, steps):
+    """Microseconds per launch for torch's in-place elementwise pass over a
+    tensor of the decode state's size (read once, written once) and for a
+    device copy of it, each captured ``steps`` times in a graph like the decode
+    steps: what moving the same bytes costs without any arithmetic."""
+    x = S0.clone()
+    y = torch.empty_like(x)
+    out = {}
+    for tag, op in (("state_rmw_ceiling_us", lambda: x.mul_(1.0)),
+                    ("state_copy_ceiling_us", lambda: y.copy_(x))):
+        op()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
+            for _ in range(steps):
+                op()
+        graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        out[tag] = e0.elapsed_time(e1) * 1e3 / steps
+        del graph
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_calls(torch, call, iters, reps=3):
     """Seconds per call: ``iters`` calls back to back between one pair of events
     on the current stream (so that the host's launch work overlaps the GPU's),
@@ -494,6 +524,14 @@ def main():
                     f"HBM {100*alg/launch/HBM_PEAK:.1f}%")
                 del r_
                 torch.cuda.empty_cache()
+            # the practical ceiling for these bytes: the same 64 MiB state read and
+            # written once per launch by torch's own kernels (an in-place
+            # elementwise pass, and a device copy into a second buffer), captured
+            # and replayed like the decode steps
+            ceil = state_traffic_ceiling(torch, dec["workload"].S0, K)
+            result["decode"].update(ceil)
+            log(f"same state bytes by torch: in-place pass {ceil['state_rmw_ceiling_us']:.2f} us, "
+                f"copy {ceil['state_copy_ceiling_us']:.2f} us per launch")
 
     if args.only in (None, "decode") and not args.cold and not args.streaming:
         dp = bench_decode_preop(torch, gdn, inputs, min(args.steps, 200))

@@ -319,10 +319,11 @@ typedef enum {
  * loaded and stored; the arithmetic, and so the result, is the same bit for bit.
  * A model steps many layers' states in turn, so by the time a layer's state is
  * read again it has left the last-level cache; for that case
- * GDN_STATE_STREAMING moves it with non-temporal loads and stores, which on
- * MI355X stream it faster (64 x 16 heads: 25.3 against 29.8 us per step when
- * eight such batches take turns).  When one batch small enough for the cache
- * is stepped over and over, GDN_STATE_CACHED is faster (22.6 against 24.8 us).
+ * GDN_STATE_STREAMING moves it with non-temporal loads and stores (and one
+ * workgroup per head state), which on MI355X streams it faster (64 x 16 heads:
+ * 24.0 against 29.0 us per step when eight such batches take turns).  When one
+ * batch small enough for the cache is stepped over and over, GDN_STATE_CACHED
+ * is faster (22.6 against 23.0 us).
  *
  *   state_hint  a gdn_state_hint value (else GDN_ERR_UNSUPPORTED).
  *   Every other argument: as for gdn_decode_step.

@@ -17,7 +17,10 @@
 // waves through LDS), after which each thread writes its rows back with
 // 16-byte stores.  kStream marks the state loads and stores non-temporal,
 // which streams state that is not in cache faster (the plain form keeps a
-// small batch stepped over and over in the last-level cache).
+// small batch stepped over and over in the last-level cache); that form runs
+// one workgroup per head state, each thread doing the same rows and columns in
+// both halves (16 loads in flight), with each half's arithmetic unchanged, so
+// the two forms give bit-identical results.
 
 #include "gdn_internal.hpp"
 
@@ -45,7 +48,10 @@ __device__ __forceinline__ void store_state(float *p, float4 x) {
     }
 }
 
-template <typename IO, bool kStream>
+// kHalves = 1: one workgroup per half; kHalves = 2: one workgroup per head
+// state, each thread doing its rows and columns in both halves, with the
+// arithmetic of each half, and its order, exactly as for kHalves = 1.
+template <typename IO, bool kStream, int kHalves>
 __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
                                                      const IO *__restrict__ k,
                                                      const IO *__restrict__ v,
@@ -53,53 +59,61 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
                                                      const float *__restrict__ beta,
                                                      float *__restrict__ S,
                                                      IO *__restrict__ o) {
-    const int64_t u = blockIdx.x >> 1;          // head state
-    const int half = blockIdx.x & 1;            // value columns [64 half, 64 half + 64)
+    const int64_t u = blockIdx.x / (2 / kHalves);                    // head state
+    const int half0 = kHalves == 2 ? 0 : static_cast<int>(blockIdx.x & 1);
     const int tid = threadIdx.x;
     const int lane = tid & 63, w = tid >> 6;
     const int cg = lane & 15;
     const int rp = 4 * w + (lane >> 4);
-    float *Su = S + u * (kHeadDim * kHeadDim) + 64 * half;
+    float *Su = S + u * (kHeadDim * kHeadDim) + 64 * half0;
 
     __shared__ float sq[kHeadDim], sk[kHeadDim];
-    __shared__ float4 red_a[4][16], red_b[4][16];
+    __shared__ float4 red_a[kHalves][4][16], red_b[kHalves][4][16];
 
-    float4 s[8];
+    float4 s[kHalves][8];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-        s[m] = load_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 4 * cg);
+    for (int hh = 0; hh < kHalves; ++hh)
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+            s[hh][m] = load_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 64 * hh + 4 * cg);
 
     if (tid < kHeadDim) {
         sq[tid] = to_f32(q[u * kHeadDim + tid]);
         sk[tid] = to_f32(k[u * kHeadDim + tid]);
     }
-    const int c0 = 64 * half + 4 * cg;          // first of this thread's 4 columns
-    float4 vv;
-    vv.x = to_f32(v[u * kHeadDim + c0]);
-    vv.y = to_f32(v[u * kHeadDim + c0 + 1]);
-    vv.z = to_f32(v[u * kHeadDim + c0 + 2]);
-    vv.w = to_f32(v[u * kHeadDim + c0 + 3]);
+    float4 vv[kHalves];
+#pragma unroll
+    for (int hh = 0; hh < kHalves; ++hh) {
+        const int c0 = 64 * (half0 + hh) + 4 * cg;   // first of this thread's 4 columns
+        vv[hh].x = to_f32(v[u * kHeadDim + c0]);
+        vv[hh].y = to_f32(v[u * kHeadDim + c0 + 1]);
+        vv[hh].z = to_f32(v[u * kHeadDim + c0 + 2]);
+        vv[hh].w = to_f32(v[u * kHeadDim + c0 + 3]);
+    }
     const float d = expf(g[u]);
     const float bt = beta[u];
     __syncthreads();
 
-    float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const float kr = sk[rp + 16 * m], qr = sq[rp + 16 * m];
-        a.x += s[m].x * kr; a.y += s[m].y * kr; a.z += s[m].z * kr; a.w += s[m].w * kr;
-        b.x += s[m].x * qr; b.y += s[m].y * qr; b.z += s[m].z * qr; b.w += s[m].w * qr;
-    }
+    for (int hh = 0; hh < kHalves; ++hh) {
+        float4 a = make_float4(0.f, 0.f, 0.f, 0.f), b = a;
 #pragma unroll
-    for (int off = 16; off <= 32; off <<= 1) {
-        a.x += __shfl_xor(a.x, off); a.y += __shfl_xor(a.y, off);
-        a.z += __shfl_xor(a.z, off); a.w += __shfl_xor(a.w, off);
-        b.x += __shfl_xor(b.x, off); b.y += __shfl_xor(b.y, off);
-        b.z += __shfl_xor(b.z, off); b.w += __shfl_xor(b.w, off);
-    }
-    if (lane < 16) {
-        red_a[w][cg] = a;
-        red_b[w][cg] = b;
+        for (int m = 0; m < 8; ++m) {
+            const float kr = sk[rp + 16 * m], qr = sq[rp + 16 * m];
+            a.x += s[hh][m].x * kr; a.y += s[hh][m].y * kr; a.z += s[hh][m].z * kr; a.w += s[hh][m].w * kr;
+            b.x += s[hh][m].x * qr; b.y += s[hh][m].y * qr; b.z += s[hh][m].z * qr; b.w += s[hh][m].w * qr;
+        }
+#pragma unroll
+        for (int off = 16; off <= 32; off <<= 1) {
+            a.x += __shfl_xor(a.x, off); a.y += __shfl_xor(a.y, off);
+            a.z += __shfl_xor(a.z, off); a.w += __shfl_xor(a.w, off);
+            b.x += __shfl_xor(b.x, off); b.y += __shfl_xor(b.y, off);
+            b.z += __shfl_xor(b.z, off); b.w += __shfl_xor(b.w, off);
+        }
+        if (lane < 16) {
+            red_a[hh][w][cg] = a;
+            red_b[hh][w][cg] = b;
+        }
     }
     // q.k, reduced within every wave (each wave needs it; no extra barrier)
     float qk = sq[lane] * sk[lane] + sq[lane + 64] * sk[lane + 64];
@@ -107,35 +121,38 @@ __global__ __launch_bounds__(256) void decode_kernel(const IO *__restrict__ q,
     for (int off = 32; off >= 1; off >>= 1) qk += __shfl_xor(qk, off);
     __syncthreads();
 
-    float4 A = red_a[0][cg], Bq = red_b[0][cg];
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) {
-        const float4 x = red_a[ww][cg], y = red_b[ww][cg];
-        A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
-        Bq.x += y.x; Bq.y += y.y; Bq.z += y.z; Bq.w += y.w;
-    }
-    float4 dl;
-    dl.x = bt * (vv.x - d * A.x);
-    dl.y = bt * (vv.y - d * A.y);
-    dl.z = bt * (vv.z - d * A.z);
-    dl.w = bt * (vv.w - d * A.w);
+    for (int hh = 0; hh < kHalves; ++hh) {
+        float4 A = red_a[hh][0][cg], Bq = red_b[hh][0][cg];
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) {
+            const float4 x = red_a[hh][ww][cg], y = red_b[hh][ww][cg];
+            A.x += x.x; A.y += x.y; A.z += x.z; A.w += x.w;
+            Bq.x += y.x; Bq.y += y.y; Bq.z += y.z; Bq.w += y.w;
+        }
+        float4 dl;
+        dl.x = bt * (vv[hh].x - d * A.x);
+        dl.y = bt * (vv[hh].y - d * A.y);
+        dl.z = bt * (vv[hh].z - d * A.z);
+        dl.w = bt * (vv[hh].w - d * A.w);
 
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-        const float kr = sk[rp + 16 * m];
-        float4 x = s[m];
-        x.x = d * x.x + kr * dl.x;
-        x.y = d * x.y + kr * dl.y;
-        x.z = d * x.z + kr * dl.z;
-        x.w = d * x.w + kr * dl.w;
-        store_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 4 * cg, x);
-    }
-    if (rp == 0) {
-        IO *ou = o + u * kHeadDim + c0;
-        ou[0] = from_f32<IO>(d * Bq.x + qk * dl.x);
-        ou[1] = from_f32<IO>(d * Bq.y + qk * dl.y);
-        ou[2] = from_f32<IO>(d * Bq.z + qk * dl.z);
-        ou[3] = from_f32<IO>(d * Bq.w + qk * dl.w);
+        for (int m = 0; m < 8; ++m) {
+            const float kr = sk[rp + 16 * m];
+            float4 x = s[hh][m];
+            x.x = d * x.x + kr * dl.x;
+            x.y = d * x.y + kr * dl.y;
+            x.z = d * x.z + kr * dl.z;
+            x.w = d * x.w + kr * dl.w;
+            store_state<kStream>(Su + (rp + 16 * m) * kHeadDim + 64 * hh + 4 * cg, x);
+        }
+        if (rp == 0) {
+            IO *ou = o + u * kHeadDim + 64 * (half0 + hh) + 4 * cg;
+            ou[0] = from_f32<IO>(d * Bq.x + qk * dl.x);
+            ou[1] = from_f32<IO>(d * Bq.y + qk * dl.y);
+            ou[2] = from_f32<IO>(d * Bq.z + qk * dl.z);
+            ou[3] = from_f32<IO>(d * Bq.w + qk * dl.w);
+        }
     }
 }
 
@@ -315,8 +332,11 @@ hipError_t launch_decode_preop(const DecodePreopArgs &a, hipStream_t stream) {
 
 template <typename IO>
 void launch_decode_io(const DecodeArgs &a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(2 * a.units)), block(256);
-    auto kern = a.stream_state ? decode_kernel<IO, true> : decode_kernel<IO, false>;
+    // Non-temporal state streams faster with one workgroup per head state (16
+    // loads in flight per thread); cached state with one per half.
+    const int halves = a.stream_state ? 2 : 1;
+    const dim3 grid(static_cast<unsigned>((2 / halves) * a.units)), block(256);
+    auto kern = a.stream_state ? decode_kernel<IO, true, 2> : decode_kernel<IO, false, 1>;
     kern<<<grid, block, 0, stream>>>(static_cast<const IO *>(a.q), static_cast<const IO *>(a.k),
                                      static_cast<const IO *>(a.v), a.g, a.beta, a.S,
                                      static_cast<IO *>(a.o));
