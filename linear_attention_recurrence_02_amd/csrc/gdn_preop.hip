@@ -10,14 +10,15 @@
 //     g_t = -softplus(a_t),  beta_t = sigmoid(b_t);
 // then the FIFO holds each sequence's last three raw rows.
 //
-// Work split (HBM-bound streaming): one 256-thread workgroup per 128 token
+// Work split (HBM-bound streaming): one 256-thread workgroup per 256 token
 // rows of one (head, stream); a thread owns 8 channels (one 16-byte row
-// segment) of 8 consecutive tokens; it loads the 11 rows those need (three
+// segment) of 16 consecutive tokens; it loads the 19 rows those need (three
 // before the first) at once, so that they are in flight together, and the 32
-// conv weights once.  Each input row is read about 11/8 times (the overlap
+// conv weights once.  Each input row is read about 19/16 times (the overlap
 // hits cache).  The 16 threads of a token row reduce the row's sum of squares
-// with lane shuffles.  Window rows before a sequence's first token come from
-// that sequence's FIFO state.
+// with lane shuffles.  When no sequence starts within a thread's window and
+// all its tokens exist, the tokens run as straight-line code; otherwise window
+// rows before a sequence's first token come from that sequence's FIFO state.
 // The FIFO update runs as a second small kernel on the same stream, after
 // every read of the old state.
 
@@ -28,8 +29,8 @@ namespace {
 
 constexpr int kK = 4;                 // conv taps
 constexpr int kW = kK - 1;            // FIFO rows
-constexpr int kTok = 8;               // tokens per thread
-constexpr int kRowsPerBlock = 128;    // 16 token groups x 8 tokens
+constexpr int kTok = 16;              // tokens per thread
+constexpr int kRowsPerBlock = 256;    // 16 token groups x 16 tokens
 
 struct Vec8 {
     float v[8];
@@ -96,14 +97,14 @@ template <> __device__ __forceinline__ void store8<float>(float *p, const float 
     *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
     *reinterpret_cast<float4 *>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
+// two values per conversion (round to nearest even, as __float2bfloat16)
 template <> __device__ __forceinline__ void store8<__hip_bfloat16>(__hip_bfloat16 *p, const float *v) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
     uint32_t w[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = __bfloat16_as_ushort(__float2bfloat16(v[2 * i]));
-        const uint32_t hi = __bfloat16_as_ushort(__float2bfloat16(v[2 * i + 1]));
-        w[i] = lo | (hi << 16);
-    }
+    for (int i = 0; i < 4; ++i)
+        w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v[2 * i], v[2 * i + 1]}, bf16x2));
     *reinterpret_cast<uint4 *>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
@@ -180,10 +181,54 @@ __global__ __launch_bounds__(256) void preop_kernel(
         const IO *p = r < 0 ? x + h * D + c0 : (r >= rows ? xb + (rows - 1 - t0) * HD : xb + (j - kW) * static_cast<int64_t>(hd));
         xr[j] = load_raw<IO>(p);
     }
+    // g and beta, one token per lane: lane L < 4 kTok of wave w takes the
+    // wave's token 4 kTok w + L of the block (in stream q's workgroups only);
+    // a lane whose group returned above has its token at or past the end
+    if (s == 0 && lane < 4 * kTok) {
+        const int64_t t = static_cast<int64_t>(blockIdx.y) * kRowsPerBlock + 4 * kTok * wave + lane;
+        if (t < rows) {
+            const int64_t gi = t * H + h;
+            const float av = a[gi], bv = b[gi];
+            // softplus(av) = max(av, 0) + log1p(exp(-|av|)), without overflow
+            g[gi] = -(fmaxf(av, 0.f) + log1pf(__expf(-fabsf(av))));
+            beta[gi] = 1.f / (1.f + __expf(-bv));
+        }
+    }
+
+    // token t0 + i from the conv window r0, r1, r2 (rows t-3 .. t-1) and row xt
+    auto emit = [&](int i, const Vec8 &r0, const Vec8 &r1, const Vec8 &r2, const Vec8 &xt) {
+        float out[8];
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float u = w[c][0] * r0.v[c] + w[c][1] * r1.v[c] + w[c][2] * r2.v[c] + w[c][3] * xt.v[c];
+            const float yv = u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
+            out[c] = yv;
+            ss += yv * yv;
+        }
+        if (s < 2) {
+            const float inv = rsqrtf(row16_sum(ss) + eps);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) out[c] *= inv;
+        }
+        store8<IO>(yb + static_cast<uint32_t>(i) * hd, out);
+    };
+
     int64_t start, end;
     int64_t n = seq_of(cu, N, T, t0, start, end);
-    // the window rows t0-3 .. t0-1, widened once; those before the sequence's
-    // start come from its FIFO state
+    if (start <= t0 - kW && t0 + kTok <= end && t0 + kTok <= rows) {
+        // the common case, uniform over the 16 lanes of the group: all 8 tokens
+        // and their window in one sequence, straight-line code
+        Vec8 wd[kW + kTok];
+#pragma unroll
+        for (int j = 0; j < kW + kTok; ++j) wd[j] = widen(xr[j]);
+#pragma unroll
+        for (int i = 0; i < kTok; ++i) emit(i, wd[i], wd[i + 1], wd[i + 2], wd[i + 3]);
+        return;
+    }
+    // a sequence starts within the window, or the rows end: the window rows
+    // t0-3 .. t0-1, widened once; those before the sequence's start come from
+    // its FIFO state
     Vec8 win[kW];
 #pragma unroll
     for (int j = 0; j < kW; ++j) {
@@ -200,32 +245,10 @@ __global__ __launch_bounds__(256) void preop_kernel(
                 for (int j = 0; j < kW; ++j) win[j] = state_row(n, j);
             }
             const Vec8 xt = widen(xr[i + kW]);
-            float out[8];
-            float ss = 0.f;
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                const float u = w[c][0] * win[0].v[c] + w[c][1] * win[1].v[c] + w[c][2] * win[2].v[c] +
-                                w[c][3] * xt.v[c];
-                const float yv = u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
-                out[c] = yv;
-                ss += yv * yv;
-            }
+            emit(i, win[0], win[1], win[2], xt);
             win[0] = win[1];
             win[1] = win[2];
             win[2] = xt;
-            if (s < 2) {
-                const float inv = rsqrtf(row16_sum(ss) + eps);
-#pragma unroll
-                for (int c = 0; c < 8; ++c) out[c] *= inv;
-            }
-            store8<IO>(yb + static_cast<uint32_t>(i) * hd, out);
-            if (s == 0 && cg == 0) {
-                const int64_t gi = t * H + h;
-                const float av = a[gi], bv = b[gi];
-                // softplus(av) = max(av, 0) + log1p(exp(-|av|)), without overflow
-                g[gi] = -(fmaxf(av, 0.f) + log1pf(__expf(-fabsf(av))));
-                beta[gi] = 1.f / (1.f + __expf(-bv));
-            }
         }
     }
 }

@@ -63,6 +63,21 @@ def test_preop_packed_with_empty_and_short_sequences_out_of_place():
     check(p, out, so, "bf16 packed")
 
 
+def test_preop_packed_starts_at_the_window_edges():
+    # A thread takes 16 consecutive rows and needs the three before them; it
+    # runs straight through when its window lies in one sequence.  Sequence
+    # starts here fall 3, 2 and 1 rows before a thread's first row, on it, and
+    # inside its rows, with lengths that make threads run past the end.
+    lengths = [13, 17, 17, 17, 1, 35, 300, 2, 3]
+    starts = np.cumsum([0] + lengths[:-1])
+    assert {int(x) % 16 for x in starts} >= {13, 14, 15, 0}
+    p = inputs.preop_inputs(0, 0, 3, lengths=lengths, seed=67, device=DEV)
+    st = p.state.clone()
+    out = gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st, p.cu_seqlens)
+    torch.cuda.synchronize()
+    check(p, out, st, "bf16 packed, starts at the window edges")
+
+
 def test_preop_fp32():
     p = inputs.preop_inputs(1, 77, 2, io_dtype=torch.float32, seed=63, device=DEV)
     st = p.state.clone()
