@@ -5,6 +5,7 @@
 #include "gdn.h"
 #include "gdn_internal.hpp"
 
+#include <atomic>
 #include <cfloat>
 #include <cstdint>
 #include <cstdlib>
@@ -70,6 +71,19 @@ const char *gdn_status_string(int status) {
 }
 
 }  // extern "C"
+
+int gdn::compute_units() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 0;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
 
 namespace {
 

@@ -105,6 +105,9 @@ hipError_t launch_prefill_short(const PrefillArgs &a, hipStream_t stream);
 bool prefill_short_pays(const PrefillArgs &a);
 // The prompt form keeping the state after every token in S_tok (chunk unused).
 hipError_t launch_prefill_states(const PrefillArgs &a, float *S_tok, hipStream_t stream);
+// Compute units of the current device, 0 if they cannot be queried (cached
+// per device; launch heuristics use it).
+int compute_units();
 
 // ---- small device helpers -------------------------------------------------
 

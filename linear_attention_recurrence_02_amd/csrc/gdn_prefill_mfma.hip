@@ -942,16 +942,8 @@ bool prefill_mfma_supports(const PrefillArgs &a) { return a.bf16 && a.chunk == C
 // by every workgroup) only costs.
 bool rank_longest_first_pays(const PrefillArgs &a) {
     if (!a.cu_seqlens || a.N > kMaxRankedSequences) return false;
-    static int cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            return false;
-        cus[dev] = n;
-    }
-    return a.N * a.H <= 4 * static_cast<int64_t>(cus[dev]);
+    const int cus = compute_units();
+    return cus > 0 && a.N * a.H <= 4 * static_cast<int64_t>(cus);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {

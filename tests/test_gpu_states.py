@@ -108,3 +108,23 @@ def test_token_states_empty_sequences_and_zero_state():
     z = inputs.prefill_workload(2, 0, 2, seed=6, device=DEV)
     O0, S0t = run_states(z)
     assert O0.numel() == 0 and S0t.numel() == 0
+
+
+def test_token_states_launch_forms_agree_bit_for_bit():
+    # The kernel loads a token's inputs two tokens ahead when a launch's
+    # workgroups (two per sequence and head) fit on the CUs at once, four per
+    # CU, and in the token's own iteration otherwise.  The same sequences run
+    # both ways give the same states bit for bit, and outputs within one bf16
+    # rounding of each other.
+    H = 16
+    n_small = 4 * torch.cuda.get_device_properties(0).multi_processor_count // (2 * H)
+    big = inputs.verify_workload(n_small + 8, 16, H, seed=9, device=DEV)   # packed, B = 1
+    n = n_small * 16
+    small = inputs.Workload("verify_head", *(x[:, :n] for x in (big.q, big.k, big.v, big.g, big.beta)),
+                            big.S0[:n_small], big.cu_seqlens[:n_small + 1], big.chunk, {})
+    Ob, Sb = run_states(big)
+    Os, Ss = run_states(small)
+    assert torch.equal(Ss, Sb[:, :n])
+    d = (Os.float() - Ob[:, :n].float()).abs()
+    assert d.max().item() <= 2.0 ** -8 * Ob[:, :n].float().abs().max().item()
+    say(f"[launch forms] {n} tokens: states equal, outputs differ in {(d > 0).sum().item()} elements")
