@@ -36,8 +36,12 @@
  *     GDN_ERR_HIP.
  *   - Preconditions not checked: g <= 0 and 0 <= beta <= 1 (the accuracy
  *     contract assumes them), finite inputs (NaN/Inf propagate).  For bf16
- *     io the prompt form rounds its matrix operands to fp16, so state, value
- *     and delta magnitudes must stay well inside fp16's range (< 6.5e4).
+ *     io the prompt form's matrix operands are fp16 (q and k, split pairs
+ *     where the recurrence needs them) and bf16 (v): q and k must have
+ *     entries of unit scale (|x| well below 6.5e4 / 128, as L2-normalised
+ *     rows, or up to the page's q x 1024 rescale); v and the states may have
+ *     any magnitude from about 2^-55 to 2^55 (each head's values are held at
+ *     a power-of-two scale inside the kernel).
  */
 #ifndef GDN_H
 #define GDN_H
@@ -58,7 +62,11 @@ typedef enum {
 
 typedef enum {
     GDN_F32 = 0,
-    GDN_BF16 = 1
+    GDN_BF16 = 1,
+    /* bf16 q, k, v with an fp32 O: the arithmetic of the bf16 path without the
+     * rounding of O to bf16.  Accepted by gdn_chunk_prefill and
+     * gdn_chunk_prefill_ex only (O is then [B, T, H, 128] fp32). */
+    GDN_BF16_F32_OUT = 2
 } gdn_dtype;
 
 /* How the prompt form's matrix-core kernel forms the 16 x 16 diagonal blocks of
@@ -112,8 +120,8 @@ const char *gdn_status_string(int status);
  *               on average: T <= 16 for a uniform batch, T <= 16 N for a packed
  *               one, as in a speculative verify pass) is tiled by 16 whatever
  *               the chunk, on a kernel that runs two sequence-heads per CU.
- *   O           same shape and dtype as v; rows of the call's tokens are all
- *               written.
+ *   O           same shape and dtype as v (fp32 with GDN_BF16_F32_OUT); rows of
+ *               the call's tokens are all written.
  *   S_T         [N, H, 128, 128] fp32, the state after each sequence's last
  *               token.  S_T may be exactly S0 (in-place update of a prefix
  *               state); any other overlap of S_T with S0 is GDN_ERR_ALIAS.

@@ -19,7 +19,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
 GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
-GDN_F32, GDN_BF16 = 0, 1
+GDN_F32, GDN_BF16, GDN_BF16_F32_OUT = 0, 1, 2
 EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_ex",
             "gdn_chunk_prefill_segmented", "gdn_chunk_prefill_segmented_workspace",
             "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step",
@@ -130,7 +130,7 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
-                      O=None, S_T=None, stream=None, inverse=None):
+                      O=None, S_T=None, stream=None, inverse=None, out_dtype=None):
     """Chunkwise-parallel prompt form over whole sequences.
 
     q, k, v: [B, T, H, 128] (bf16 or fp32; packed batches B = 1);
@@ -138,6 +138,8 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
     cu_seqlens: int32 [N+1] device offsets or None.
     inverse: None (gdn_chunk_prefill) or a GDN_INVERSE_* value
     (gdn_chunk_prefill_ex).
+    out_dtype: O's dtype; q's by default, or torch.float32 for bf16 inputs
+    (GDN_BF16_F32_OUT).
     Returns (O, S_T); O/S_T may be given to write in place (S_T may be S0).
     """
     B, T, H, dk = q.shape
@@ -150,15 +152,19 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
         raise ValueError("q, k, v must share shape [B, T, H, d] and dtype")
     if g.shape != (B, T, H) or beta.shape != (B, T, H):
         raise ValueError("g and beta must be [B, T, H]")
+    if out_dtype is None:
+        out_dtype = q.dtype if O is None else O.dtype
     if O is None:
-        O = torch.empty_like(v)
+        O = torch.empty(v.shape, dtype=out_dtype, device=v.device)
     if S_T is None:
         S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
-    if O.dtype != q.dtype or O.shape != v.shape:
-        raise ValueError("O must match v's shape and dtype")
+    f32_out = q.dtype == torch.bfloat16 and out_dtype == torch.float32
+    if O.shape != v.shape or O.dtype != out_dtype or not (O.dtype == q.dtype or f32_out):
+        raise ValueError("O must match v's shape, with q's dtype (or fp32 for bf16 inputs)")
     if S_T.shape != (N, H, dk, dv) or (S0 is not None and S0.shape != (N, H, dk, dv)):
         raise ValueError("S0 / S_T must be [N, H, dk, dv]")
-    args = (_ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+    args = (_ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"),
+            GDN_BF16_F32_OUT if f32_out else _io_dtype(q),
             _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
             _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
             N, T, H, dk, dv, int(chunk))

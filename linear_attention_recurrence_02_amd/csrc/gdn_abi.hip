@@ -89,17 +89,21 @@ namespace {
 
 // Validation shared by the prompt-form calls: fills `a` (and the byte spans
 // of the token buffers for further alias checks) or returns a status.
+// GDN_BF16_F32_OUT (bf16 inputs, fp32 O) only where `f32_out_ok`.
 int check_prefill(const void *q, const void *k, const void *v, int io_dtype, const float *g,
                   const float *beta, const float *S0, const int32_t *cu_seqlens,
                   int64_t B_or_N, int64_t T, int64_t H, int64_t dk, int64_t dv,
-                  int64_t chunk, void *O, float *S_T, gdn::PrefillArgs &a, int64_t &tok_bytes) {
+                  int64_t chunk, void *O, float *S_T, gdn::PrefillArgs &a, int64_t &tok_bytes,
+                  bool f32_out_ok = false) {
     if (!dims_ok(B_or_N) || !dims_ok(T) || H <= 0 || H >= 65536) return GDN_ERR_INVALID_ARG;
     const int64_t N = B_or_N;
     const int64_t rows = cu_seqlens ? T : N * T;        // token rows of H heads
     // Token buffers may be NULL only when the call has no token rows at all.
     if (rows > 0 && (!q || !k || !v || !g || !beta || !O)) return GDN_ERR_INVALID_ARG;
     if (!S_T) return GDN_ERR_INVALID_ARG;
-    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    const bool f32_out = io_dtype == GDN_BF16_F32_OUT;
+    if (io_dtype != GDN_F32 && io_dtype != GDN_BF16 && !(f32_out && f32_out_ok))
+        return GDN_ERR_UNSUPPORTED;
     if (dk != gdn::kHeadDim || dv != gdn::kHeadDim) return GDN_ERR_UNSUPPORTED;
     if (chunk != 16 && chunk != 32 && chunk != 64) return GDN_ERR_UNSUPPORTED;
     for (const void *p : {q, k, v, static_cast<const void *>(O)})
@@ -110,14 +114,15 @@ int check_prefill(const void *q, const void *k, const void *v, int io_dtype, con
 
     if (N * H >= kMaxDim) return GDN_ERR_INVALID_ARG;     // one workgroup per unit
     if (rows > (int64_t(1) << 40) / (H * gdn::kHeadDim)) return GDN_ERR_INVALID_ARG;
-    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t esz = io_dtype == GDN_F32 ? 4 : 2;
     tok_bytes = rows * H * gdn::kHeadDim * esz;
+    const int64_t out_bytes = f32_out ? 2 * tok_bytes : tok_bytes;
     const int64_t gb_bytes = rows * H * 4;
     const int64_t st_bytes = N * H * gdn::kHeadDim * gdn::kHeadDim * 4;
 
     const Range rq = span_of(q, tok_bytes), rk = span_of(k, tok_bytes),
                 rv = span_of(v, tok_bytes), rg = span_of(g, gb_bytes),
-                rb = span_of(beta, gb_bytes), rO = span_of(O, tok_bytes),
+                rb = span_of(beta, gb_bytes), rO = span_of(O, out_bytes),
                 rST = span_of(S_T, st_bytes),
                 rS0 = S0 ? span_of(S0, st_bytes) : Range{0, 0};
     for (Range r : {rq, rk, rv, rg, rb, rS0, rST})
@@ -127,7 +132,8 @@ int check_prefill(const void *q, const void *k, const void *v, int io_dtype, con
     if (S0 && overlap(rST, rS0) && rST.lo != rS0.lo) return GDN_ERR_ALIAS;
 
     a = gdn::PrefillArgs{q, k, v, g, beta, S0, cu_seqlens, N, T, H,
-                         static_cast<int>(chunk), io_dtype == GDN_BF16, O, S_T};
+                         static_cast<int>(chunk), io_dtype != GDN_F32, O, S_T};
+    a.out_f32 = f32_out;
     return GDN_OK;
 }
 
@@ -254,7 +260,7 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
     gdn::PrefillArgs a{};
     int64_t tok_bytes = 0;
     const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
-                                 dv, chunk, O, S_T, a, tok_bytes);
+                                 dv, chunk, O, S_T, a, tok_bytes, true);
     if (st != GDN_OK) return st;
     if (const int sc = check_seqlens_debug(cu_seqlens, B_or_N, T, stream)) return sc;
     return launch_prefill(a, stream);
@@ -271,7 +277,7 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
     gdn::PrefillArgs a{};
     int64_t tok_bytes = 0;
     const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
-                                 dv, chunk, O, S_T, a, tok_bytes);
+                                 dv, chunk, O, S_T, a, tok_bytes, true);
     if (st != GDN_OK) return st;
     if (const int sc = check_seqlens_debug(cu_seqlens, B_or_N, T, stream)) return sc;
     if (inverse != GDN_INVERSE_DEFAULT) {

@@ -10,6 +10,7 @@ namespace gdn {
 
 constexpr int kHeadDim = 128;   // dk == dv == 128: the page's per-head state size
 
+constexpr int kInverseDefault = 0;        // the kernel's own choice
 constexpr int kInverseSubstitution = 1;   // back substitution on the vector ALUs
 constexpr int kInverseDoubling = 2;       // block doubling on the matrix cores
 
@@ -24,9 +25,12 @@ struct PrefillArgs {
     int64_t T;                  // tokens per sequence (uniform) or total (packed)
     int64_t H;                  // heads
     int chunk;                  // 16, 32 or 64
-    bool bf16;                  // io dtype of q/k/v/O
+    bool bf16;                  // io dtype of q/k/v (and of O unless out_f32)
     void *O;
     float *S_T;
+    // bf16 inputs with an fp32 O (the matrix-core kernels' arithmetic without
+    // the rounding of O to bf16).
+    bool out_f32 = false;
     // Gated RMS norm on the output rows (null z: plain O).  O then receives
     // y = norm_w * O / sqrt(mean(O^2) + eps) * silu(z), z with the io dtype.
     const void *z = nullptr;
@@ -34,7 +38,7 @@ struct PrefillArgs {
     float eps = 0.f;
     // How the matrix-core kernel forms the diagonal 16 x 16 blocks of
     // (I + N)^-1 (the vector kernel always substitutes column by column).
-    int inverse = kInverseDoubling;
+    int inverse = kInverseDefault;
     // Whether a batch of short sequences may take the 16-token kernel (off
     // when the caller names the matrix-core kernel's inverse method).
     bool short_ok = true;

@@ -15,9 +15,14 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16;
 typedef bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+// The same product on bf16 operands (fp32's exponent range).
+__device__ __forceinline__ f32x4 mfma_bf(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ f16x4 zh4() {
@@ -29,6 +34,39 @@ __device__ __forceinline__ f16x8 cat(f16x4 a, f16x4 b) {
 }
 __device__ __forceinline__ f16x4 h4(f32x4 x) { return __builtin_convertvector(x, f16x4); }
 __device__ __forceinline__ f32x4 f4(f16x4 x) { return __builtin_convertvector(x, f32x4); }
+__device__ __forceinline__ bf16x8 catb(bf16x4 a, bf16x4 b) {
+    return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Split operands.  A product whose operand x is rounded once to fp16 carries
+// x's relative rounding error 2^-11; written as hi + lo, with hi = fp16(x) and
+// lo = fp16(x - hi), the pair holds x to about 2^-22 (relative to x, for hi
+// normal).  A product with one split operand is one K = 32 product of
+// [hi lo] with [b; b]; with both split, the lo * lo term is dropped.
+struct h4x2 {
+    f16x4 hi, lo;
+};
+__device__ __forceinline__ h4x2 split_h4(f32x4 x) {
+    const f16x4 hi = h4(x);
+    return h4x2{hi, h4(x - f4(hi))};
+}
+// The same split in bf16 (8 significant bits each, about 2^-17 together, with
+// fp32's exponent range).
+struct b4x2 {
+    bf16x4 hi, lo;
+};
+__device__ __forceinline__ b4x2 split_b4(f32x4 x) {
+    const bf16x4 hi = __builtin_convertvector(x, bf16x4);
+    return b4x2{hi, __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), bf16x4)};
+}
+
+// Exact powers of two as floats, for exponents in [-126, 127].
+__device__ __forceinline__ float pow2i(int e) { return __uint_as_float(static_cast<uint32_t>(e + 127) << 23); }
+// floor(log2 |x|) of a normal float (its unbiased exponent field); -127 for 0
+// and fp32 subnormals.
+__device__ __forceinline__ int exponent_of(float x) {
+    return static_cast<int>((__float_as_uint(x) >> 23) & 0xffu) - 127;
+}
 __device__ __forceinline__ f16x4 neg(f16x4 x) {
     typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(f16x4, __builtin_bit_cast(u32x2, x) ^ 0x80008000u);
@@ -70,11 +108,15 @@ __device__ __forceinline__ f16x8 bf_to_h8(f32x4 raw) {
     return r;
 }
 
-// The K = 16 product (one 16 x 16 tile, four k per lane group: lane l holds
+// A K = 16 product (one 16 x 16 tile, four k per lane group: lane l holds
 // A[l % 16][4 (l / 16) ..+3] and B[4 (l / 16) ..+3][l % 16]; the result lane
-// holds rows 4 (l / 16) ..+3 of column l % 16).
+// holds rows 4 (l / 16) ..+3 of column l % 16), issued as the K = 32 product
+// with zero upper halves.  The gfx950 compiler does not keep VALU writes far
+// enough behind the legacy 16x16x16 f16 instruction's read of its
+// accumulator (a result came out with half of each lane's values taken from
+// registers rewritten after the issue), so that instruction is not used.
 __device__ __forceinline__ f32x4 mfma16(f16x4 a, f16x4 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+    return mfma(cat(a, zh4()), cat(b, zh4()), c);
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave with DPP moves: shifts
@@ -95,6 +137,49 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
     return x;
 }
+// Maximum of a non-negative value over the 64 lanes of a wave (DPP moves as in
+// wave_prefix_sum, lanes without a source contributing 0), returned to every
+// lane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_max(float v) {
+    const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true);
+    return __builtin_fmaxf(v, __builtin_bit_cast(float, t));
+}
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    x = dpp_max<0x111, 0xf>(x);   // row_shr:1
+    x = dpp_max<0x112, 0xf>(x);   // row_shr:2
+    x = dpp_max<0x114, 0xf>(x);   // row_shr:4
+    x = dpp_max<0x118, 0xf>(x);   // row_shr:8
+    x = dpp_max<0x142, 0xa>(x);   // row_bcast:15 into rows 1, 3
+    x = dpp_max<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+// Largest |x| of a lane's tile values.
+__device__ __forceinline__ float absmax4(f32x4 x, float m) {
+    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
+                                           __builtin_fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3]))), m);
+}
+
+// Bound on the scale exponents, so that a change of scale is one exact
+// multiplication by a normal power of two.
+constexpr int kMaxScaleExp = 62;
+
+// Power-of-two scale of a wave's value-side quantities (the state columns it
+// owns and everything linear in them), chosen so that the largest of them
+// lands in [8, 16): fp16 operands then keep their full relative precision
+// (11 bits for a single rounding, 22 for a split pair) relative to that
+// largest value, whatever the magnitude of the values and states the caller
+// passes.  `mscaled` is the largest |x| already held at the current scale
+// 2^cur, `mtrue` the largest |x| of unscaled ones; returns the new exponent
+// (unchanged when both are zero).
+__device__ __forceinline__ int choose_scale(float mscaled, int cur, float mtrue) {
+    int e = -1000;
+    if (mscaled > 0.f) e = exponent_of(mscaled) - cur;
+    if (mtrue > 0.f) e = max(e, exponent_of(mtrue));
+    if (e == -1000) return cur;
+    return min(max(3 - e, -kMaxScaleExp), kMaxScaleExp);
+}
+
 // Inclusive prefix sum within each row of 16 lanes.
 __device__ __forceinline__ float row16_prefix_sum(float x) {
     x = dpp_add<0x111, 0xf>(x);   // row_shr:1

@@ -1,5 +1,6 @@
 // Chunkwise-parallel prompt form on the gfx950 matrix cores (bf16 inputs,
-// 64-token chunks, fp32 state and accumulation, fp16 matrix operands).
+// 64-token chunks, fp32 state and accumulation, fp16 and bf16 matrix operands,
+// split into hi + lo pairs where the recurrence needs it).
 //
 // The form (Qwen3.5-9B-npu model page, "How it works" -> "Gated DeltaNet on
 // the NPU"), per chunk of C = 64 tokens with incoming state S (dk x dv):
@@ -42,7 +43,8 @@
 //     accumulators; T_ii (one block per wave) by the page's exact block
 //     doubling on the matrix cores (or, selectable, by fp32 back
 //     substitution) and M_ij = T_ii N_ij; and the staging of chunk c+2 (rows
-//     prefetched into registers a period earlier, converted to fp16).
+//     prefetched into registers a period earlier; K and Q converted to fp16,
+//     V kept as bf16).
 //   Each chunk period has three barrier-separated phases:
 //     1: consumers D, state update (chunk c)  | producers Gram tiles (c+1),
 //                                            |   store V (c+1)
@@ -61,8 +63,22 @@
 // exchange per-row sums through LDS); kDoubling picks the T_ii method; kRank
 // walks a packed batch longest first (each workgroup ranks the sequence
 // lengths before the roles split, one barrier that both roles execute).
-// Every matrix operand is rounded once to fp16 (11 significant bits); the
-// state, the accumulators and the per-token scalars stay fp32.
+// Precision.  The state, the accumulators, U and the per-token scalars are
+// fp32.  K and Q enter the products as fp16 copies of the bf16 inputs, V as
+// the bf16 input itself (in bf16 products against P').  Correlated keys (the
+// page's own warning about real keys in reduced precision) make the chunk's
+// deltas large next to what is built from them: the terms of A D and of
+// K^T D nearly cancel, and so do those of the U chain.  An operand rounded
+// once to fp16 (2^-11) is not enough there, so A, D, the decayed D, P, P',
+// N_ij, M_ij, T_ii inside the doubling and the U chain enter their products
+// as hi + lo pairs (fp16, about 2^-22; P' as a bf16 pair against the bf16 V),
+// while S and W, whose single rounding is harmless, stay single fp16
+// operands.  Each consumer wave holds its value-side quantities (its state
+// columns and everything linear in them: U, D, O) at a power-of-two scale
+// chosen per chunk so that their largest entry lies in [8, 16), which keeps
+// fp16's relative precision for heads of any magnitude (the page's small
+// heads, 1e-3..2e-2, and far smaller or larger ones); the scale is exact and
+// is removed when O and S_T are stored.
 
 #include "gdn_mfma.hpp"
 
@@ -78,6 +94,9 @@ constexpr int AS = C + 4;         // fp16 row stride of A (token-major)
 constexpr int BS = 16 + 8;        // fp16 row stride of the 16 x 16 blocks T_ii, P_i, P'_i, M_ij
 constexpr int NS = 20;            // fp32 row stride of the diagonal blocks of N
 constexpr float kLog2e = 1.4426950408889634f;
+// How the diagonal blocks of (I + N)^-1 are formed unless the caller names a
+// method: block doubling on the matrix cores (true) or fp32 back substitution.
+constexpr bool kDefaultDoubling = true;
 
 // LDS layouts.  Each array's row stride (and, for K, V and W, an XOR of the
 // column with a few row bits) is chosen so that its main access patterns hit
@@ -87,15 +106,14 @@ constexpr float kLog2e = 1.4426950408889634f;
 // constant, so each address is a per-lane base plus a compile-time offset.
 struct __attribute__((aligned(16))) Smem {
     f16 K[2][C * KS];             // keys, double-buffered; column c of row t at c ^ ksw(t)
-    f16 V[C * KS];                // values, same layout as K
+    bf16 V[C * KS];               // values (the bf16 inputs as they are), same layout as K
     f16 Q[2][C * QS];             // queries, double-buffered
     f16 W[D * WS];                // -W, dk-major: -W_td at d * WS + (t ^ wsw(d))
-    f16 A[C * AS];                // decayed masked Q K^T, token-major
+    f16 A[2][C * AS];             // decayed masked Q K^T, token-major: hi, lo
     float NR[4][16 * NS];         // diagonal blocks of N, row-major
-    f16 Tii[4][16 * BS];          // T_ii
-    f16 P[4][16 * BS];            // T_ii diag(beta exp G)
-    f16 Pv[4][16 * BS];           // T_ii diag(beta)
-    f16 M[6][16 * BS];            // -T_ii N_ij, i > j
+    f16 P[2][4][16 * BS];         // T_ii diag(beta exp G): hi, lo
+    bf16 Pv[2][4][16 * BS];       // T_ii diag(beta): hi, lo (bf16, against the bf16 V)
+    f16 M[2][6][16 * BS];         // -T_ii N_ij, i > j: hi, lo
     float G2[2][C];               // cumsum(g) * log2(e)
     float EG[2][C];               // exp(G_t)
     float EC[2][C];               // exp(G_last - G_t)
@@ -109,28 +127,9 @@ struct __attribute__((aligned(16))) Smem {
 // bits 2..3 with row bits 2..3.
 __device__ __forceinline__ int ksw(int row) { return ((row >> 2) & 1) << 3; }
 __device__ __forceinline__ int wsw(int row) { return ((row >> 2) & 3) << 2; }
-__device__ __forceinline__ int zsw(int row) { return (row >> 1) & 3; }
 
 // index of the off-diagonal block (i, j), i > j, in Smem::M
 __device__ __forceinline__ constexpr int oblk(int i, int j) { return i * (i - 1) / 2 + j; }
-
-// Workgroup barrier for the consumer loop.  __syncthreads() is also a release
-// fence, and a release waits for every direct-to-LDS load still in flight; the
-// gated output keeps such loads (each wave's own gate rows, read only by that
-// wave) in flight across barriers, so its loop uses a barrier that waits only
-// for this wave's LDS operations and keeps the compiler from moving memory
-// accesses across it.
-template <bool kLdsOnly>
-__device__ __forceinline__ void phase_barrier() {
-    if constexpr (kLdsOnly) {
-        asm volatile("" ::: "memory");
-        __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        asm volatile("" ::: "memory");
-    } else {
-        __syncthreads();
-    }
-}
 
 // Loads are always issued, rows past the chunk reading the sequence's first row
 // instead, so that every period issues the same load sequence; the tail mask is
@@ -153,7 +152,16 @@ __device__ __forceinline__ void to_fp16_rows(f32x4 *x, int r, int nv) {
         for (int s = 0; s < 4; ++s) x[s] = ok ? x[s] : zero4();
     }
 }
-__device__ __forceinline__ void store_rows_kv(f16 *tile, const f32x4 *x, int r, int q) {
+// The same rows kept as bf16 (V): only the tail rows are zeroed.
+__device__ __forceinline__ void mask_rows(f32x4 *x, int r, int nv) {
+    if (nv < C) {
+        const bool ok = r < nv;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) x[s] = ok ? x[s] : zero4();
+    }
+}
+__device__ __forceinline__ void store_rows_kv(void *tile_, const f32x4 *x, int r, int q) {
+    f16 *tile = static_cast<f16 *>(tile_);
     const int c = (8 * q) ^ ksw(r);
 #pragma unroll
     for (int s = 0; s < 4; ++s) *reinterpret_cast<f32x4 *>(&tile[r * KS + 32 * s + c]) = x[s];
@@ -192,8 +200,8 @@ struct Producer {
     f32x4 hV[4], hQ[4];
     float pg, pb;
     float sg2, seg, sec, sbt;     // scan results of the staged chunk (wave p = 0)
-    f16x4 Ah[4];                  // A tiles of the chunk being prepared (phase 1 -> 3)
-    f16x4 Nop[3];                 // off-diagonal N blocks of the chunk (phase 1 -> 2)
+    h4x2 Ah[4];                   // A tiles of the chunk being prepared, hi/lo (phase 1 -> 3)
+    h4x2 Nop[3];                  // off-diagonal N blocks of the chunk, hi/lo (phase 1 -> 2)
 
     __device__ void prefetch(const Unit &u, int pc, int p, int l, int r16, int q) {
         const int nv = u.rows_in(pc);
@@ -204,12 +212,13 @@ struct Producer {
         pg = u.g[gi];
         pb = u.beta[gi];
     }
-    // Convert the prefetched rows (nv valid), store K in buffer set nb, keep V
-    // and Q, scan the log-decay (wave p = 0).
+    // Convert the prefetched K and Q rows to fp16 (V stays bf16; rows past nv
+    // are zeroed), store K in buffer set nb, keep V and Q, scan the log-decay
+    // (wave p = 0).
     __device__ void convert(Smem &sm, int nb, int nv, int p, int l, int r16, int q) {
         to_fp16_rows(pK, 16 * p + r16, nv);
         store_rows_kv(sm.K[nb], pK, 16 * p + r16, q);
-        to_fp16_rows(pV, 16 * p + r16, nv);
+        mask_rows(pV, 16 * p + r16, nv);
         to_fp16_rows(pQ, 16 * p + r16, nv);
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -295,7 +304,7 @@ struct Producer {
                 f32x4 x;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) x[e] = btr[e] * (__builtin_amdgcn_exp2f(g2r[e] - g2j) * kk[jb][e]);
-                Nop[jb] = h4(x);
+                Nop[jb] = split_h4(x);
             }
         }
         // qa[jb][e] = k_j . q_t, j = 16jb + 4q + e, t = 16IB + r16 -> A_tj
@@ -311,7 +320,7 @@ struct Producer {
                     const bool keep = jb < IB || 16 * jb + 4 * q + e <= t;
                     x[e] = __builtin_amdgcn_exp2f(keep ? g2t - g2j[e] : kNegInf) * qa[jb][e];
                 }
-                Ah[jb] = h4(x);
+                Ah[jb] = split_h4(x);
             }
         }
     }
@@ -326,8 +335,9 @@ struct Producer {
     // T R and its transpose R^T T^T.  T and U = T^T are both kept as result
     // tiles (lane (c = r16, q) holds T[4q+e][c] and T[c][4q+e]): a result tile
     // is a B operand as it is, and read as an A operand it is its own
-    // transpose.  Operands are rounded to fp16, sums are fp32.  Returns the U
-    // tile: columns 4q..4q+3 of row r16 of T_PP.
+    // transpose.  Operands are split into fp16 hi + lo pairs (the lo * lo term
+    // dropped), sums are fp32.  Returns the U tile: columns 4q..4q+3 of row r16
+    // of T_PP.
     template <int P>
     __device__ f32x4 invert_doubling(const Smem &sm, int r16, int q) {
         const float *Nr = sm.NR[P];
@@ -341,6 +351,10 @@ struct Producer {
             Tt[e] = (i == r16 ? 1.f : 0.f) - ((r16 & 1) == 0 && i == r16 + 1 ? nsub : 0.f);
             Ut[e] = (i == r16 ? 1.f : 0.f) - ((r16 & 1) == 1 && i == r16 - 1 ? nrow[e] : 0.f);
         }
+        // x y with both split: (x_hi + x_lo) y_hi + x_hi y_lo
+        auto prod = [](h4x2 x, h4x2 y) {
+            return mfma16(x.hi, y.lo, mfma(cat(x.hi, x.lo), cat(y.hi, y.hi), zero4()));
+        };
 #pragma unroll
         for (int b = 2; b <= 8; b *= 2) {
             f32x4 cb;   // C_b[r16][4q+e]: rows in the lower half of a 2b block, columns in its upper half
@@ -349,10 +363,10 @@ struct Producer {
                 const int j = 4 * q + e;
                 cb[e] = ((r16 / b) & 1) && j / b == r16 / b - 1 ? nrow[e] : 0.f;
             }
-            const f32x4 R = mfma(cat(h4(cb), zh4()), cat(h4(Tt), zh4()), zero4());   // C_b T
-            const f16x8 rh = cat(h4(R), zh4()), uh = cat(h4(Ut), zh4());
-            Tt -= mfma(uh, rh, zero4());                                            // T C_b T
-            Ut -= mfma(rh, uh, zero4());                                            // (T C_b T)^T
+            const h4x2 R = split_h4(prod(split_h4(cb), split_h4(Tt)));   // C_b T
+            const h4x2 uh = split_h4(Ut);
+            Tt -= prod(uh, R);                                            // T C_b T
+            Ut -= prod(R, uh);                                            // (T C_b T)^T
         }
         return Ut;
     }
@@ -427,24 +441,30 @@ struct Producer {
                 y4[e] = y[e] * m0 + y[4 + e] * m1 + y[8 + e] * m2 + y[12 + e] * m3;
         }
         }
-        // group q rounds and stores its 4 columns of the row
+        // group q splits and stores its 4 columns of the row
         {
             const f32x4 bt = *reinterpret_cast<const f32x4 *>(&Bt[16 * P + 4 * q]);
             const f32x4 eg = *reinterpret_cast<const f32x4 *>(&EG[16 * P + 4 * q]);
             const int o = r16 * BS + 4 * q;
-            *reinterpret_cast<f16x4 *>(&sm.Tii[P][o]) = h4(y4);
-            *reinterpret_cast<f16x4 *>(&sm.P[P][o]) = h4(y4 * (bt * eg));
-            *reinterpret_cast<f16x4 *>(&sm.Pv[P][o]) = h4(y4 * bt);
+            const h4x2 ph = split_h4(y4 * (bt * eg));
+            const b4x2 pv = split_b4(y4 * bt);
+            *reinterpret_cast<f16x4 *>(&sm.P[0][P][o]) = ph.hi;
+            *reinterpret_cast<f16x4 *>(&sm.P[1][P][o]) = ph.lo;
+            *reinterpret_cast<bf16x4 *>(&sm.Pv[0][P][o]) = pv.hi;
+            *reinterpret_cast<bf16x4 *>(&sm.Pv[1][P][o]) = pv.lo;
         }
         // M_Pj^T = N_Pj^T T_PP^T: A = N_Pj (lane: row j = r16, k = t = 4q..),
         // B[t'][t] = T_PP[t][t'] (lane: column t = r16, k = t' = 4q..).  The
-        // result lane holds M[t = r16][j = 4q + e]; stored negated.
+        // result lane holds M[t = r16][j = 4q + e]; stored negated, split.
         if (P > 0) {
-            const f16x8 bt = cat(h4(y4), zh4());
+            const h4x2 tb = split_h4(y4);
 #pragma unroll
             for (int jb = 0; jb < P; ++jb) {
-                const f32x4 mt = mfma(cat(Nop[jb], zh4()), bt, zero4());
-                *reinterpret_cast<f16x4 *>(&sm.M[oblk(P, jb)][r16 * BS + 4 * q]) = neg(h4(mt));
+                const f32x4 mt = mfma16(Nop[jb].hi, tb.lo,
+                                        mfma(cat(Nop[jb].hi, Nop[jb].lo), cat(tb.hi, tb.hi), zero4()));
+                const h4x2 m = split_h4(-mt);
+                *reinterpret_cast<f16x4 *>(&sm.M[0][oblk(P, jb)][r16 * BS + 4 * q]) = m.hi;
+                *reinterpret_cast<f16x4 *>(&sm.M[1][oblk(P, jb)][r16 * BS + 4 * q]) = m.lo;
             }
         }
     }
@@ -454,81 +474,109 @@ struct Producer {
     __device__ void store_a(Smem &sm, int r16, int q) {
         constexpr int IB = 3 - P;
 #pragma unroll
-        for (int jb = 0; jb <= IB; ++jb)
-            *reinterpret_cast<f16x4 *>(&sm.A[(16 * IB + r16) * AS + 16 * jb + 4 * q]) = Ah[jb];
+        for (int jb = 0; jb <= IB; ++jb) {
+            *reinterpret_cast<f16x4 *>(&sm.A[0][(16 * IB + r16) * AS + 16 * jb + 4 * q]) = Ah[jb].hi;
+            *reinterpret_cast<f16x4 *>(&sm.A[1][(16 * IB + r16) * AS + 16 * jb + 4 * q]) = Ah[jb].lo;
+        }
     }
 };
 
 // Columns [32p, 32p+32) of W and of U for the chunk in buffer set nb, block by
 // block (run by consumer wave p); stores -W (dk-major) in LDS and returns U in
-// the result-tile layout, Uo[i][cc] = U rows 16i + 4q + e, column 32p + 16cc + r16.
-__device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q, f32x4 (*Uo)[2]) {
+// the result-tile layout, Uo[i][cc] = U rows 16i + 4q + e, column 32p + 16cc + r16,
+// at the wave's scale for the chunk.  That scale is chosen here, from the
+// largest |X| of the direct terms X_i = P'_i V_i (bf16 products, unscaled) and
+// `ms`, the lane's largest |S| at the current scale 2^sc (S being the state
+// that enters the chunk); S is rescaled when the scale changes.  W's chain is
+// W_i = P_i K_i - sum_j M_ij W_j with P and M split and W single; U's chain
+// U_i = X_i - sum_j M_ij U_j with M and U split.
+__device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q, f32x4 (*Uo)[2],
+                                        f32x4 (*S)[2], int &sc, float ms) {
     r16 = opaque(r16);
     q = opaque(q);
     const int trk = (4 * q + (r16 >> 2)) * KS + ((4 * (r16 & 3)) ^ ksw(4 * q));
     const f16 *kb = sm.K[nb] + trk + 32 * p;
-    const f16 *vb = sm.V + trk + 32 * p;
+    const f16 *vb = reinterpret_cast<const f16 *>(sm.V) + trk + 32 * p;
     const int co = r16 * BS + 4 * q;
     // Everything but the previous blocks' W and U is known before the
     // substitution starts: read it all first.
-    f16x4 kx[4][2], vx[4][2], pw[4], pu[4], mm[6];
+    f16x4 kx[4][2];
+    bf16x4 vx[4][2];
+    f16x8 pw[4];
+    bf16x8 pu[4];
+    h4x2 mm[6];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             kx[i][cc] = rd_tr(kb + 16 * i * KS + 16 * cc);
-            vx[i][cc] = rd_tr(vb + 16 * i * KS + 16 * cc);
+            vx[i][cc] = __builtin_bit_cast(bf16x4, rd_tr(vb + 16 * i * KS + 16 * cc));
         }
-        pw[i] = rd4(&sm.P[i][co]);
-        pu[i] = rd4(&sm.Pv[i][co]);
+        pw[i] = cat(rd4(&sm.P[0][i][co]), rd4(&sm.P[1][i][co]));
+        pu[i] = catb(*reinterpret_cast<const bf16x4 *>(&sm.Pv[0][i][co]),
+                     *reinterpret_cast<const bf16x4 *>(&sm.Pv[1][i][co]));
     }
 #pragma unroll
-    for (int b = 0; b < 6; ++b) mm[b] = rd4(&sm.M[b][co]);
+    for (int b = 0; b < 6; ++b) mm[b] = h4x2{rd4(&sm.M[0][b][co]), rd4(&sm.M[1][b][co])};
     fence();
-    f16x4 Wr[3][2], Ur[3][2];
+    // the direct terms of U, unscaled, and the scale of the chunk
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            Uo[i][cc] = mfma_bf(pu[i], catb(vx[i][cc], vx[i][cc]), zero4());
+            mx = absmax4(Uo[i][cc], mx);
+        }
+    const int nx = choose_scale(0.f, sc, wave_max_nonneg(__builtin_fmaxf(ms * pow2i(-sc), mx)));
+    if (nx != sc) {
+        const float f = pow2i(nx - sc);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            S[i][0] *= f;
+            S[i][1] *= f;
+        }
+        sc = nx;
+    }
+    const float up = pow2i(sc);
+    f16x4 Wr[3][2];
+    h4x2 Ur[3][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        // Two K = 16 products share one K = 32 product where a pair exists;
-        // a lone one (block 0's P K, block 2's M_21 W_1) takes a K = 16
-        // product rather than a zero-padded K = 32 one
         f32x4 aw[2], au[2];
-        if (i == 0) {
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+            aw[cc] = mfma(pw[i], cat(kx[i][cc], kx[i][cc]), zero4());   // P_i K_i
+            au[cc] = Uo[i][cc] * up;
+        }
+        // - M_ij W_j and - M_ij U_j (M is stored negated): the hi products ...
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
+            const h4x2 mj = mm[oblk(i > 0 ? i : 1, j)];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                aw[cc] = mfma16(pw[0], kx[0][cc], zero4());
-                au[cc] = mfma16(pu[0], vx[0][cc], zero4());
-            }
-        } else {
-            const f16x4 m0 = mm[oblk(i > 0 ? i : 1, 0)];
-            const f16x8 a0w = cat(pw[i], m0);
-            const f16x8 a0u = cat(pu[i], m0);
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                aw[cc] = mfma(a0w, cat(kx[i][cc], Wr[0][cc]), zero4());
-                au[cc] = mfma(a0u, cat(vx[i][cc], Ur[0][cc]), zero4());
+                aw[cc] = mfma(cat(mj.hi, mj.lo), cat(Wr[j][cc], Wr[j][cc]), aw[cc]);
+                au[cc] = mfma(cat(mj.hi, mj.lo), cat(Ur[j][cc].hi, Ur[j][cc].hi), au[cc]);
             }
         }
-        if (i == 2) {
-            const f16x4 a1 = mm[oblk(2, 1)];
+        // ... and M_hi U_lo, two blocks j to a product
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                aw[cc] = mfma16(a1, Wr[1][cc], aw[cc]);
-                au[cc] = mfma16(a1, Ur[1][cc], au[cc]);
-            }
-        } else if (i == 3) {
-            const f16x8 a1 = cat(mm[oblk(3, 1)], mm[oblk(3, 2)]);
-#pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-                aw[cc] = mfma(a1, cat(Wr[1][cc], Wr[2][cc]), aw[cc]);
-                au[cc] = mfma(a1, cat(Ur[1][cc], Ur[2][cc]), au[cc]);
+        for (int cc = 0; cc < 2; ++cc) {
+            if (i == 1) {
+                au[cc] = mfma16(mm[oblk(1, 0)].hi, Ur[0][cc].lo, au[cc]);
+            } else if (i == 2) {
+                au[cc] = mfma(cat(mm[oblk(2, 0)].hi, mm[oblk(2, 1)].hi), cat(Ur[0][cc].lo, Ur[1][cc].lo), au[cc]);
+            } else if (i == 3) {
+                au[cc] = mfma(cat(mm[oblk(3, 0)].hi, mm[oblk(3, 1)].hi), cat(Ur[0][cc].lo, Ur[1][cc].lo), au[cc]);
+                au[cc] = mfma16(mm[oblk(3, 2)].hi, Ur[2][cc].lo, au[cc]);
             }
         }
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
-            const f16x4 w16 = h4(aw[cc]), u16 = h4(au[cc]);
+            const f16x4 w16 = h4(aw[cc]);
             if (i < 3) {
                 Wr[i < 3 ? i : 0][cc] = w16;
-                Ur[i < 3 ? i : 0][cc] = u16;
+                Ur[i < 3 ? i : 0][cc] = split_h4(au[cc]);
             }
             *reinterpret_cast<f16x4 *>(&sm.W[(32 * p + 16 * cc + r16) * WS + 16 * i + ((4 * q) ^ wsw(r16))]) = neg(w16);
             Uo[i][cc] = au[cc];
@@ -536,19 +584,14 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q,
     }
 }
 
-template <bool kGated, bool kDoubling, bool kRank>
+template <bool kGated, bool kDoubling, bool kRank, typename OutT>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t N, int64_t T,
-    int64_t H, bf16 *__restrict__ O, float *__restrict__ S_T, const bf16 *__restrict__ z,
+    int64_t H, OutT *__restrict__ O, float *__restrict__ S_T, const bf16 *__restrict__ z,
     const float *__restrict__ norm_w, float eps) {
     __shared__ Smem sm;
-    // Gated norm: consumer wave w's gate columns 32w..32w+31, token-major; the
-    // 16-byte slot j of row t at j ^ zsw(t).  A variable of its own, so that
-    // the compiler can tell the direct-to-LDS loads into it from the reads of
-    // the other arrays and does not wait for them before those reads.
-    __shared__ bf16 Zs[4][kGated ? C * 32 : 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6, l = tid & 63, r16 = l & 15, qd = l >> 4;
@@ -579,8 +622,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         // ======================= producer waves =======================
         if (nch == 0) return;
         // A entries above the diagonal blocks are never written.
-        for (int i = (tid - 256) * 8; i < C * AS; i += 256 * 8)
-            *reinterpret_cast<f32x4 *>(&sm.A[i]) = zero4();
+        for (int i = (tid - 256) * 8; i < C * AS; i += 256 * 8) {
+            *reinterpret_cast<f32x4 *>(&sm.A[0][i]) = zero4();
+            *reinterpret_cast<f32x4 *>(&sm.A[1][i]) = zero4();
+        }
         Producer pr;
         pr.prefetch(u, 0, w, l, r16, qd);
         pr.convert(sm, 0, u.rows_in(0), w, l, r16, qd);
@@ -629,8 +674,9 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     }
 
     // ======================= consumer waves =======================
-    // S[i][c] holds state rows 16i+4q+e, column 32w+16c+r16.
+    // S[i][c] holds state rows 16i+4q+e, column 32w+16c+r16, at scale 2^sc.
     f32x4 S[8][2];
+    int sc = 0;
     if (S0) {
         const float *S0u = S0 + unit * (D * D);
 #pragma unroll
@@ -645,16 +691,27 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         for (int i = 0; i < 8; ++i) S[i][0] = S[i][1] = zero4();
     }
     float *STu = S_T + unit * (D * D);
-    if (nch == 0) {
+    auto store_state = [&]() {
+        const float un = pow2i(-sc);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    STu[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16] = S[i][c][e];
+                    STu[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16] = S[i][c][e] * un;
+    };
+    if (nch == 0) {
+        store_state();
         return;
     }
+    // this lane's largest |S| (at the current scale), for the next scale choice
+    auto lane_max_s = [&]() {
+        float m = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) m = absmax4(S[i][1], absmax4(S[i][0], m));
+        return m;
+    };
     if (kGated && tid < D) sm.NW[tid] = norm_w[tid];
     if (kGated && tid == 0) sm.NPC = 0;
     __syncthreads();
@@ -663,28 +720,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     __syncthreads();
     __syncthreads();
     f32x4 Ur[4][2];
-    wu_step(sm, 0, w, r16, qd, Ur);
+    wu_step(sm, 0, w, r16, qd, Ur, S, sc, lane_max_s());
     __syncthreads();
 
     const uint32_t HD = static_cast<uint32_t>(H) * D;
-    // Gated norm: the gate rows of chunk cz straight into LDS (no registers):
-    // wave w fetches its 32 columns of the 64 rows, 16 rows per instruction,
-    // lane i's 16 bytes landing at slot i of the instruction's 1 KiB.  Rows
-    // past the sequence repeat the chunk's row 0 and are never used.
-    auto fetch_gate = [&](int cz) {
-        const bf16 *zc = z + (u.row0(cz) * H + u.h) * D + 32 * w;
-        const int nz = u.rows_in(cz);
-        const int lr = opaque(l);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int t = 16 * i + (lr >> 2);
-            const uint32_t off = static_cast<uint32_t>(t < nz ? t : 0) * HD + 8 * ((lr & 3) ^ zsw(t));
-            __builtin_amdgcn_global_load_lds(zc + off,
-                                             (__attribute__((address_space(3))) void *)&Zs[w][16 * 32 * i],
-                                             16, 0, 0);
-        }
-    };
-    if constexpr (kGated) fetch_gate(0);
     const int trw = (4 * qd + (r16 >> 2)) * WS + ((4 * (r16 & 3)) ^ wsw(4 * qd));
     const int trk = (4 * qd + (r16 >> 2)) * KS + ((4 * (r16 & 3)) ^ ksw(4 * qd));
     for (int c = 0; c < nch; ++c) {
@@ -692,7 +731,8 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         const int cnv = u.rows_in(c);
 
         // ======== phase 1: D = U - W S; S <- exp(G_C) S + K^T diag(exp(G_C - G)) D ========
-        f16x8 Sh[4][2], Dh[2][2];
+        // (all at the wave's scale: U and S carry it, so D does)
+        f16x8 Sh[4][2], Dh[2][2], Dl[2][2];
         {
             const f16 *Wc = sm.W + trw;
             auto ld_w = [&](int s, f16x8 *dst) {
@@ -734,7 +774,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             ld_k(0, ka[0]);
             ld_k(1, ka[0] + 2);
             fence();
-            f16x8 Dp[2][2];
+            f16x8 Dp[2][2], Dq[2][2];   // the decayed D, hi and lo
             const float *EC = sm.EC[cur];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
@@ -742,8 +782,12 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&EC[32 * s2 + 16 + 4 * qd]);
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
-                    Dh[s2][cc] = cat(h4(Dt[2 * s2][cc]), h4(Dt[2 * s2 + 1][cc]));
-                    Dp[s2][cc] = cat(h4(Dt[2 * s2][cc] * e0), h4(Dt[2 * s2 + 1][cc] * e1));
+                    const h4x2 d0 = split_h4(Dt[2 * s2][cc]), d1 = split_h4(Dt[2 * s2 + 1][cc]);
+                    Dh[s2][cc] = cat(d0.hi, d1.hi);
+                    Dl[s2][cc] = cat(d0.lo, d1.lo);
+                    const h4x2 p0 = split_h4(Dt[2 * s2][cc] * e0), p1 = split_h4(Dt[2 * s2 + 1][cc] * e1);
+                    Dp[s2][cc] = cat(p0.hi, p1.hi);
+                    Dq[s2][cc] = cat(p0.lo, p1.lo);
                 }
             }
             const float eC = sm.EG[cur][C - 1];
@@ -763,24 +807,40 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                        for (int cc = 0; cc < 2; ++cc)
+                        for (int cc = 0; cc < 2; ++cc) {
                             S[2 * ib + ii][cc] = mfma(ka[ib & 1][2 * ii + s2], Dp[s2][cc], S[2 * ib + ii][cc]);
+                            S[2 * ib + ii][cc] = mfma(ka[ib & 1][2 * ii + s2], Dq[s2][cc], S[2 * ib + ii][cc]);
+                        }
             }
         }
-        phase_barrier<kGated>();
+        __syncthreads();
 
         // ======== phase 2: O = diag(exp G) Q S + A D (S as it entered the chunk) ========
         // Computed transposed, O^T = S^T Q^T diag(exp G) + D^T A^T: the fp16
         // tiles of S and D serve as A operands as they are, a lane's column is
         // one token (one decay factor), and each lane ends up with four
-        // consecutive columns of one token row (one 8-byte store).
-        // With the gated norm, the gate rows z are loaded before the products,
-        // O is multiplied by w silu(z) after them, and each wave leaves its
-        // partial sums of O^2 per token row in LDS; the rows are scaled by
-        // 1/sqrt(mean(O^2) + eps) and stored after the barrier.
-        bf16 *obase = O + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
+        // consecutive columns of one token row (one 8-byte store).  A D takes
+        // both split: (D_hi + D_lo) A_hi + D_hi A_lo.  O is unscaled before it
+        // is stored (or normed).
+        // With the gated norm, the gate rows z are loaded into registers before
+        // the products, O is multiplied by w silu(z) after them, and each wave
+        // leaves its partial sums of O^2 per token row in LDS; the four waves
+        // meet on an LDS counter and the rows are scaled by
+        // 1/sqrt(mean(O^2) + eps) and stored.
+        OutT *obase = O + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
         f32x4 Ot[4][2];           // Ot[m][cc]: O[16m + r16][32w + 16cc + 4q + e]
         {
+            bf16x4 zr[4][2];
+            if constexpr (kGated) {
+                const bf16 *zc = z + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const int t = 16 * m + r16;
+                    const uint32_t off = static_cast<uint32_t>(t < cnv ? t : 0) * HD;
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) zr[m][cc] = *reinterpret_cast<const bf16x4 *>(zc + off + 16 * cc);
+                }
+            }
 #pragma unroll
             for (int m = 0; m < 4; ++m) Ot[m][0] = Ot[m][1] = zero4();
             const f16 *Qc = sm.Q[cur] + r16 * QS + 4 * qd;
@@ -791,22 +851,11 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     dst[m] = cat(rd4(qp), rd4(qp + 16));
                 }
             };
-            const f16 *Ac = sm.A + r16 * AS + 4 * qd;
-            f16x8 qb[2][4], ab[6];
+            f16x8 qb[2][4];
             ld_q(0, qb[0]);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (s < 3) ld_q(s + 1, qb[(s + 1) & 1]);
-                if (s == 3) {
-                    int n = 0;
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-#pragma unroll
-                        for (int s2 = 0; s2 <= m / 2; ++s2) {
-                            const f16 *ap = Ac + 16 * m * AS + 32 * s2;
-                            ab[n++] = cat(rd4(ap), rd4(ap + 16));
-                        }
-                }
                 fence();
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
@@ -820,30 +869,32 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 Ot[m][1] *= eg;
             }
             {
-                int n = 0;
+                const f16 *Ah = sm.A[0] + r16 * AS + 4 * qd, *Al = sm.A[1] + r16 * AS + 4 * qd;
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
                     for (int s2 = 0; s2 <= m / 2; ++s2) {
+                        const f16x8 ah = cat(rd4(Ah + 16 * m * AS + 32 * s2), rd4(Ah + 16 * m * AS + 32 * s2 + 16));
+                        const f16x8 al = cat(rd4(Al + 16 * m * AS + 32 * s2), rd4(Al + 16 * m * AS + 32 * s2 + 16));
 #pragma unroll
-                        for (int cc = 0; cc < 2; ++cc) Ot[m][cc] = mfma(Dh[s2][cc], ab[n], Ot[m][cc]);
-                        ++n;
+                        for (int cc = 0; cc < 2; ++cc) {
+                            Ot[m][cc] = mfma(Dh[s2][cc], ah, Ot[m][cc]);
+                            Ot[m][cc] = mfma(Dl[s2][cc], ah, Ot[m][cc]);
+                            Ot[m][cc] = mfma(Dh[s2][cc], al, Ot[m][cc]);
+                        }
                     }
+            }
+            {
+                const float un = pow2i(-sc);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    Ot[m][0] *= un;
+                    Ot[m][1] *= un;
+                }
             }
             if constexpr (kGated) {
                 const f32x4 nw0 = *reinterpret_cast<const f32x4 *>(&sm.NW[32 * w + 4 * qd]);
                 const f32x4 nw1 = *reinterpret_cast<const f32x4 *>(&sm.NW[32 * w + 16 + 4 * qd]);
-                // this wave's gate rows, fetched into LDS a period ago
-                __builtin_amdgcn_s_waitcnt(0x0f70);      // vmcnt(0)
-                bf16x4 zr[4][2];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const int t = 16 * m + r16;
-#pragma unroll
-                    for (int cc = 0; cc < 2; ++cc)
-                        zr[m][cc] = *reinterpret_cast<const bf16x4 *>(
-                            &Zs[w][t * 32 + 8 * ((2 * cc + (qd >> 1)) ^ zsw(t)) + 4 * (qd & 1)]);
-                }
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     float ss = 0.f;
@@ -869,11 +920,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 // The four consumer waves meet on an LDS counter (the producers
                 // are still solving): each posts its partial sums, then waits
                 // until all four sets of this chunk are there.  Rows are then
-                // normed and stored here, in the part of the period where the
-                // CU has no other memory traffic.  Every consumer wave posts
-                // once per chunk and no wave can run a chunk ahead (the phase
-                // barriers), so the count reaches 4 (c + 1); the spin is
-                // bounded all the same.
+                // normed and stored here.  Every consumer wave posts once per
+                // chunk and no wave can run a chunk ahead (the phase barriers),
+                // so the count reaches 4 (c + 1); the spin is bounded all the
+                // same.
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): partials landed
                 if (l == 0) __hip_atomic_fetch_add(&sm.NPC, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
@@ -887,7 +937,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 asm volatile("" ::: "memory");
                 const int rr = opaque(r16);
                 const float *np = &sm.NP[rr][0];
-                bf16 *orow = obase + static_cast<uint32_t>(rr) * HD;
+                OutT *orow = obase + static_cast<uint32_t>(rr) * HD;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f32x4 ps = *reinterpret_cast<const f32x4 *>(np + 64 * m);
@@ -900,9 +950,6 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                                 __builtin_convertvector(Ot[m][cc] * rs, bf16x4);
                     }
                 }
-                // this wave's reads of its gate slice are done: refill it with
-                // the next chunk's rows, a period ahead of their use
-                if (c + 1 < nch) fetch_gate(c + 1);
             } else {
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
@@ -910,25 +957,23 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     if (t < cnv) {
                         const uint32_t off = static_cast<uint32_t>(t) * HD;
 #pragma unroll
-                        for (int cc = 0; cc < 2; ++cc)
-                            *reinterpret_cast<bf16x4 *>(obase + off + 16 * cc) = __builtin_convertvector(Ot[m][cc], bf16x4);
+                        for (int cc = 0; cc < 2; ++cc) {
+                            if constexpr (sizeof(OutT) == 4)
+                                *reinterpret_cast<f32x4 *>(obase + off + 16 * cc) = Ot[m][cc];
+                            else
+                                *reinterpret_cast<bf16x4 *>(obase + off + 16 * cc) = __builtin_convertvector(Ot[m][cc], bf16x4);
+                        }
                     }
                 }
             }
         }
-        phase_barrier<kGated>();
+        const float msl = lane_max_s();   // the state entering chunk c + 1
+        __syncthreads();
         // ======== phase 3: W and U of the next chunk ========
-        if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, r16, qd, Ur);
-        phase_barrier<kGated>();
+        if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, r16, qd, Ur, S, sc, msl);
+        __syncthreads();
     }
-
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                STu[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16] = S[i][c][e];
+    store_state();
 }
 
 }  // namespace
@@ -946,18 +991,35 @@ bool rank_longest_first_pays(const PrefillArgs &a) {
     return cus > 0 && a.N * a.H <= 4 * static_cast<int64_t>(cus);
 }
 
-hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
+template <typename OutT>
+void launch_typed(void (*kern)(const bf16 *, const bf16 *, const bf16 *, const float *, const float *,
+                               const float *, const int32_t *, int64_t, int64_t, int64_t, OutT *,
+                               float *, const bf16 *, const float *, float),
+                  const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(512);
-    const bool rank = rank_longest_first_pays(a);
-    // (the longest-first order is compiled into the default form only)
-    const bool dbl = a.inverse == kInverseDoubling;
-    auto kern = a.z ? (dbl ? prefill_mfma_kernel<true, true, false> : prefill_mfma_kernel<true, false, false>)
-                    : (dbl ? (rank ? prefill_mfma_kernel<false, true, true> : prefill_mfma_kernel<false, true, false>)
-                           : prefill_mfma_kernel<false, false, false>);
     kern<<<grid, block, 0, stream>>>(
         static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
         static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.N, a.T, a.H,
-        static_cast<bf16 *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps);
+        static_cast<OutT *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps);
+}
+
+hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
+    const bool rank = rank_longest_first_pays(a);
+    // (the longest-first order is compiled into the default form only; the
+    // gated norm and the fp32 O are offered in the two inverse methods)
+    const bool dbl = a.inverse == kInverseDoubling || (a.inverse == kInverseDefault && kDefaultDoubling);
+    if (a.out_f32)
+        launch_typed<float>(dbl ? prefill_mfma_kernel<false, true, false, float>
+                                : prefill_mfma_kernel<false, false, false, float>, a, stream);
+    else if (a.z)
+        launch_typed<bf16>(dbl ? prefill_mfma_kernel<true, true, false, bf16>
+                               : prefill_mfma_kernel<true, false, false, bf16>, a, stream);
+    else if (a.inverse == kInverseDefault)
+        launch_typed<bf16>(rank ? prefill_mfma_kernel<false, kDefaultDoubling, true, bf16>
+                                : prefill_mfma_kernel<false, kDefaultDoubling, false, bf16>, a, stream);
+    else
+        launch_typed<bf16>(dbl ? prefill_mfma_kernel<false, true, false, bf16>
+                               : prefill_mfma_kernel<false, false, false, bf16>, a, stream);
     return hipGetLastError();
 }
 

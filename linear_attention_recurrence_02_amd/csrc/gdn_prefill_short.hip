@@ -19,7 +19,8 @@
 // Wave w owns dv columns [32w, 32w+32) of S, U, D and O, its share of S held
 // in 8 x 2 result tiles of v_mfma_f32_16x16x32_f16 for the whole walk (lane
 // l: rows 4(l/16)..+3 of column l%16 of each 16 x 16 tile).  Per chunk:
-//   1. all waves stage K, Q, V (fp16) in LDS; wave 0 scans the log-decay;
+//   1. all waves stage K, Q (fp16) and V (bf16) in LDS; wave 0 scans the
+//      log-decay;
 //   2. wave 0 forms K K^T -> N and T = (I + N)^-1 by forward substitution in
 //      fp32 (one column per lane), scaled to P = T diag(beta exp G) and
 //      P' = T diag(beta); wave 1 forms Q K^T -> A;
@@ -29,8 +30,21 @@
 //      lane ends with four adjacent columns of one token row), and the state
 //      update.
 // The state is loaded before the first chunk is staged and first used in
-// step 4, so its load overlaps steps 1 to 3.  Matrix operands are rounded
-// once to fp16, sums are fp32.
+// step 4, so its load overlaps steps 1 to 3.
+//
+// Precision.  Sums are fp32; the state, D and U are fp32 between products.
+// K and Q enter the products as fp16 copies of the bf16 inputs (exact for
+// unit-scale keys and queries), V as the bf16 input itself.  Correlated keys
+// make the chunk's deltas D large next to the quantities built from them (the
+// terms of A D and of K^T D nearly cancel), so an operand rounded once to fp16
+// (2^-11 relative) is not enough where it multiplies D or enters D: P, A, D and
+// the decayed D are split into fp16 hi + lo pairs, and P' into a bf16 pair
+// (against the bf16 V).  S and W stay single fp16 operands.  Each wave holds
+// its value-side quantities (its state columns, U, D, O) at a power-of-two
+// scale chosen per chunk so that their largest entry lies in [8, 16): the fp16
+// operands then have their full precision relative to it, whatever the
+// magnitude of the values and states passed in.  Scaling by a power of two is
+// exact; O and S_T are unscaled when stored.
 
 #include "gdn_mfma.hpp"
 
@@ -47,11 +61,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct __attribute__((aligned(16))) ShortSmem {
     f16 K[CS * RS];
     f16 Q[CS * RS];
-    f16 V[CS * RS];
+    bf16 V[CS * RS];              // the bf16 inputs as they are
     f16 W[CS * RS];               // -W, token-major
-    f16 A[CS * TS];               // decayed masked Q K^T, token-major
-    f16 P[CS * TS];               // T diag(beta exp G)
-    f16 Pv[CS * TS];              // T diag(beta)
+    f16 A[2][CS * TS];            // decayed masked Q K^T, token-major: hi, lo
+    f16 P[2][CS * TS];            // T diag(beta exp G): hi, lo
+    bf16 Pv[2][CS * TS];          // T diag(beta): hi, lo
     float N[CS * NS];             // strictly lower N
     float G2[CS];                 // cumsum(g) * log2(e)
     float Bt[CS];                 // beta
@@ -59,10 +73,11 @@ struct __attribute__((aligned(16))) ShortSmem {
     float EC[CS];                 // exp(G_last - G_t)
 };
 
+template <typename OutT>
 __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta, const float *__restrict__ S0,
-    const int32_t *__restrict__ cu_seqlens, int64_t T, int64_t H, bf16 *__restrict__ O,
+    const int32_t *__restrict__ cu_seqlens, int64_t T, int64_t H, OutT *__restrict__ O,
     float *__restrict__ S_T) {
     __shared__ ShortSmem sm;
     const int tid = threadIdx.x;
@@ -87,15 +102,18 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) S[i][0] = S[i][1] = zero4();
     }
+    // S holds the state at scale 2^sc_exp (wave-uniform)
+    int sc_exp = 0;
     float *STu = S_T + unit * (D * D);
     auto store_state = [&]() {
+        const float un = pow2i(-sc_exp);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
             for (int c = 0; c < 2; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    STu[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16] = S[i][c][e];
+                    STu[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16] = S[i][c][e] * un;
     };
     if (nch == 0) {
         store_state();
@@ -134,7 +152,7 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
             const bool ok = sr < nv;
             const f32x4 hk = ok ? __builtin_bit_cast(f32x4, bf_to_h8(xk)) : zero4();
             const f32x4 hq = ok ? __builtin_bit_cast(f32x4, bf_to_h8(xq)) : zero4();
-            const f32x4 hv = ok ? __builtin_bit_cast(f32x4, bf_to_h8(xv)) : zero4();
+            const f32x4 hv = ok ? xv : zero4();
             *reinterpret_cast<f32x4 *>(&sm.K[sr * RS + sc]) = hk;
             *reinterpret_cast<f32x4 *>(&sm.Q[sr * RS + sc]) = hq;
             *reinterpret_cast<f32x4 *>(&sm.V[sr * RS + sc]) = hv;
@@ -195,16 +213,23 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
                     const float sp = bt * eg;
 #pragma unroll
                     for (int i = 0; i < CS; ++i) {
-                        sm.P[i * TS + r16] = static_cast<f16>(tc[i] * sp);
-                        sm.Pv[i * TS + r16] = static_cast<f16>(tc[i] * bt);
+                        const float p = tc[i] * sp, pv = tc[i] * bt;
+                        const f16 ph = static_cast<f16>(p);
+                        const bf16 pvh = static_cast<bf16>(pv);
+                        sm.P[0][i * TS + r16] = ph;
+                        sm.P[1][i * TS + r16] = static_cast<f16>(p - static_cast<float>(ph));
+                        sm.Pv[0][i * TS + r16] = pvh;
+                        sm.Pv[1][i * TS + r16] = static_cast<bf16>(pv - static_cast<float>(pvh));
                     }
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int t = 4 * qd + e;
-                    sm.A[t * TS + r16] = static_cast<f16>(
-                        __builtin_amdgcn_exp2f(r16 <= t ? g2t[e] - g2j : kNegInf) * acc[e]);
+                    const float a = __builtin_amdgcn_exp2f(r16 <= t ? g2t[e] - g2j : kNegInf) * acc[e];
+                    const f16 ah = static_cast<f16>(a);
+                    sm.A[0][t * TS + r16] = ah;
+                    sm.A[1][t * TS + r16] = static_cast<f16>(a - static_cast<float>(ah));
                 }
             }
         }
@@ -215,21 +240,45 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
         const int trow = (4 * qd + (r16 >> 2)) * RS + 4 * (r16 & 3);
         f32x4 U[2];
         {
-            const f16x4 pa = rd4(sm.P + r16 * TS + 4 * qd);
-            const f16x4 pva = rd4(sm.Pv + r16 * TS + 4 * qd);
+            const f16x8 pa = cat(rd4(sm.P[0] + r16 * TS + 4 * qd), rd4(sm.P[1] + r16 * TS + 4 * qd));
+            const bf16x8 pva = catb(*reinterpret_cast<const bf16x4 *>(sm.Pv[0] + r16 * TS + 4 * qd),
+                                    *reinterpret_cast<const bf16x4 *>(sm.Pv[1] + r16 * TS + 4 * qd));
 #pragma unroll
             for (int bb = 0; bb < 2; ++bb) {
                 const int b = 2 * w + bb;
-                const f32x4 wt = mfma16(pa, rd_tr(sm.K + trow + 16 * b), zero4());
+                const f16x4 kt = rd_tr(sm.K + trow + 16 * b);
+                const f32x4 wt = mfma(pa, cat(kt, kt), zero4());
 #pragma unroll
                 for (int e = 0; e < 4; ++e) sm.W[(4 * qd + e) * RS + 16 * b + r16] = static_cast<f16>(-wt[e]);
-                U[bb] = mfma16(pva, rd_tr(sm.V + trow + 16 * b), zero4());
+                const bf16x4 vt = __builtin_bit_cast(bf16x4, rd_tr(reinterpret_cast<const f16 *>(sm.V) + trow + 16 * b));
+                U[bb] = mfma_bf(pva, catb(vt, vt), zero4());
             }
         }
         __syncthreads();
 
+        // ---- the wave's scale for this chunk: its state columns (held at
+        // 2^sc_exp) and U (unscaled) ----
+        {
+            float ms = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ms = absmax4(S[i][1], absmax4(S[i][0], ms));
+            const float mu = absmax4(U[1], absmax4(U[0], 0.f));
+            const float m = wave_max_nonneg(__builtin_fmaxf(ms * pow2i(-sc_exp), mu));
+            const int nx = choose_scale(0.f, sc_exp, m);
+            if (nx != sc_exp) {
+                const float f = pow2i(nx - sc_exp);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    S[i][0] *= f;
+                    S[i][1] *= f;
+                }
+                sc_exp = nx;
+            }
+        }
+
         // ---- 4. D = U - W S; O = diag(exp G) Q S + A D; state update ----
-        f32x4 Dt[2] = {U[0], U[1]};
+        const float up = pow2i(sc_exp);
+        f32x4 Dt[2] = {U[0] * up, U[1] * up};
         f32x4 Ot[2] = {zero4(), zero4()};
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
@@ -246,28 +295,41 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
             }
         }
         {
+            // A D with both split: (D_hi + D_lo) A_hi + D_hi A_lo
             const float egt = sm.EG[r16];
-            const f16x4 ab = rd4(sm.A + r16 * TS + 4 * qd);
+            const f16x4 ah = rd4(sm.A[0] + r16 * TS + 4 * qd), al = rd4(sm.A[1] + r16 * TS + 4 * qd);
+            const float un = pow2i(-sc_exp);
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) Ot[cc] = mfma16(h4(Dt[cc]), ab, Ot[cc] * egt);
+            for (int cc = 0; cc < 2; ++cc) {
+                const h4x2 d = split_h4(Dt[cc]);
+                Ot[cc] = mfma(cat(d.hi, d.lo), cat(ah, ah), Ot[cc] * egt);
+                Ot[cc] = mfma16(d.hi, al, Ot[cc]) * un;
+            }
             if (r16 < nv) {
-                bf16 *orow = O + ((start + int64_t(c) * CS + r16) * H + h) * D + 32 * w + 4 * qd;
+                OutT *orow = O + ((start + int64_t(c) * CS + r16) * H + h) * D + 32 * w + 4 * qd;
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc)
-                    *reinterpret_cast<bf16x4 *>(orow + 16 * cc) = __builtin_convertvector(Ot[cc], bf16x4);
+                for (int cc = 0; cc < 2; ++cc) {
+                    if constexpr (sizeof(OutT) == 4)
+                        *reinterpret_cast<f32x4 *>(orow + 16 * cc) = Ot[cc];
+                    else
+                        *reinterpret_cast<bf16x4 *>(orow + 16 * cc) = __builtin_convertvector(Ot[cc], bf16x4);
+                }
             }
         }
         {
             const f32x4 ect = *reinterpret_cast<const f32x4 *>(&sm.EC[4 * qd]);
             const float eC = sm.EG[CS - 1];
-            f16x4 Dp[2];
+            f16x8 Dp[2];
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) Dp[cc] = h4(Dt[cc] * ect);
+            for (int cc = 0; cc < 2; ++cc) {
+                const h4x2 d = split_h4(Dt[cc] * ect);
+                Dp[cc] = cat(d.hi, d.lo);
+            }
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const f16x4 ka = rd_tr(sm.K + trow + 16 * i);
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) S[i][cc] = mfma16(ka, Dp[cc], S[i][cc] * eC);
+                for (int cc = 0; cc < 2; ++cc) S[i][cc] = mfma(cat(ka, ka), Dp[cc], S[i][cc] * eC);
             }
         }
         __syncthreads();
@@ -288,10 +350,15 @@ bool prefill_short_pays(const PrefillArgs &a) {
 }
 
 hipError_t launch_prefill_short(const PrefillArgs &a, hipStream_t stream) {
-    prefill_short_kernel<<<dim3(static_cast<unsigned>(a.N * a.H)), dim3(256), 0, stream>>>(
-        static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
-        static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
-        static_cast<bf16 *>(a.O), a.S_T);
+    const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(256);
+    const bf16 *q = static_cast<const bf16 *>(a.q), *k = static_cast<const bf16 *>(a.k),
+               *v = static_cast<const bf16 *>(a.v);
+    if (a.out_f32)
+        prefill_short_kernel<float><<<grid, block, 0, stream>>>(q, k, v, a.g, a.beta, a.S0, a.cu_seqlens,
+                                                                a.T, a.H, static_cast<float *>(a.O), a.S_T);
+    else
+        prefill_short_kernel<bf16><<<grid, block, 0, stream>>>(q, k, v, a.g, a.beta, a.S0, a.cu_seqlens,
+                                                               a.T, a.H, static_cast<bf16 *>(a.O), a.S_T);
     return hipGetLastError();
 }
 

@@ -35,12 +35,12 @@ namespace {
 constexpr int kThreads = 128;
 constexpr int kRow = kHeadDim + 1;   // padded LDS row stride for K and Q
 
-template <typename IO, int C, bool kGated>
+template <typename IO, typename OutT, int C, bool kGated>
 __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const IO *__restrict__ q, const IO *__restrict__ k, const IO *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t T,
-    int64_t H, IO *__restrict__ O, float *__restrict__ S_T, const IO *__restrict__ z,
+    int64_t H, OutT *__restrict__ O, float *__restrict__ S_T, const IO *__restrict__ z,
     const float *__restrict__ norm_w, float eps) {
     __shared__ float sK[C * kRow], sQ[C * kRow];
     __shared__ float sD[C * kHeadDim];
@@ -141,10 +141,10 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
                 if (t < nv) {
                     const float zf = to_f32(z[oi]);
                     const float silu = zf / (1.f + expf(-zf));
-                    O[oi] = from_f32<IO>(nw * (o / sqrtf(ms + eps)) * silu);
+                    O[oi] = from_f32<OutT>(nw * (o / sqrtf(ms + eps)) * silu);
                 }
             } else {
-                if (t < nv) O[oi] = from_f32<IO>(o);
+                if (t < nv) O[oi] = from_f32<OutT>(o);
             }
         }
 
@@ -166,30 +166,33 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     for (int i = 0; i < kHeadDim; ++i) STu[i * kHeadDim + j] = S[i];
 }
 
-template <typename IO, int C>
+template <typename IO, typename OutT, int C>
 hipError_t launch_typed(const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(kThreads);
-    auto kern = a.z ? prefill_valu_kernel<IO, C, true> : prefill_valu_kernel<IO, C, false>;
+    // (the gated output is only offered with O in the io dtype)
+    auto kern = a.z ? prefill_valu_kernel<IO, OutT, C, true> : prefill_valu_kernel<IO, OutT, C, false>;
     kern<<<grid, block, 0, stream>>>(
         static_cast<const IO *>(a.q), static_cast<const IO *>(a.k),
         static_cast<const IO *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.T, a.H,
-        static_cast<IO *>(a.O), a.S_T, static_cast<const IO *>(a.z), a.norm_w, a.eps);
+        static_cast<OutT *>(a.O), a.S_T, static_cast<const IO *>(a.z), a.norm_w, a.eps);
     return hipGetLastError();
 }
 
-template <typename IO>
+template <typename IO, typename OutT>
 hipError_t launch_chunk(const PrefillArgs &a, hipStream_t stream) {
     switch (a.chunk) {
-    case 16: return launch_typed<IO, 16>(a, stream);
-    case 32: return launch_typed<IO, 32>(a, stream);
-    default: return launch_typed<IO, 64>(a, stream);
+    case 16: return launch_typed<IO, OutT, 16>(a, stream);
+    case 32: return launch_typed<IO, OutT, 32>(a, stream);
+    default: return launch_typed<IO, OutT, 64>(a, stream);
     }
 }
 
 }  // namespace
 
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream) {
-    return a.bf16 ? launch_chunk<__hip_bfloat16>(a, stream) : launch_chunk<float>(a, stream);
+    if (!a.bf16) return launch_chunk<float, float>(a, stream);
+    return a.out_f32 ? launch_chunk<__hip_bfloat16, float>(a, stream)
+                     : launch_chunk<__hip_bfloat16, __hip_bfloat16>(a, stream);
 }
 
 }  // namespace gdn

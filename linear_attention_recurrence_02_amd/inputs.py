@@ -214,3 +214,89 @@ def preop_inputs(B: int, T: int, H: int, *, lengths=None, io_dtype=torch.bfloat1
     conv_w = 0.5 * rn(3, H, DK, 4)
     state = rn(N, 3, H, 3, DK).to(io_dtype)
     return PreopInputs(xq, xk, xv, a, b, conv_w, state, cu)
+
+
+# --- inputs at the edges of the method's numerics ------------------------------
+#
+# The Qwen3.5-9B-npu model page ("How it works" -> "Gated DeltaNet on the NPU"
+# and "fp16 precision of the DeltaNet output") names two hazards for reduced
+# precision: real keys are highly correlated, and some heads carry outputs far
+# smaller than others.  These draws reproduce both, plus the special cases of
+# the recurrence (no write, a full read-back, full decay), at any size.
+
+KEYS = ("iid", "corr", "exact")
+DECAYS = ("normal", "slow", "none", "full")
+WRITES = ("sigmoid", "one", "zero")
+
+
+def edge_workload(B: int, T: int, H: int, *, keys: str = "iid", sigma: float = 0.1,
+                  decay: str = "normal", write: str = "sigmoid", value_scale: float = 1.0,
+                  q_is_k: bool = False, lengths=None, chunk: int = 64,
+                  io_dtype=torch.bfloat16, s0: bool = True, seed: int = 0,
+                  device="cpu") -> Workload:
+    """A prompt-form workload at an edge of the numerics.
+
+    keys: "iid" draws unit keys as the other workloads do; "corr" draws
+      k = normalize(b + sigma n / sqrt(dk)) around one unit direction b per
+      (sequence, head), n ~ N(0, I), so that neighbouring keys have cosine
+      about 1 / sqrt(1 + sigma^2) (0.958, 0.995, 0.9996 at sigma 0.3, 0.1, 0.03);
+      "exact" draws keys whose norm is exactly 1 in bf16: +-1/8 on 64 of the
+      128 coordinates (random signs and coordinates), zero elsewhere.
+    decay: "normal" g = -softplus(x), "slow" 0.02 times that, "none" g = 0,
+      "full" g = -1e4 (exp(g) underflows to zero in fp32).
+    write: "sigmoid" beta = sigmoid(x), "one" beta = 1, "zero" beta = 0.
+    value_scale: v and S0 are multiplied by it (the page's small heads have an
+      output RMS of 1e-3..2e-2).
+    q_is_k: queries equal to the keys.
+    lengths: a packed batch of these lengths (B must then be 1 and T their sum).
+    Draw order from one generator seeded with ``seed`` on ``device``: q, k (or
+    the key directions and the spread), v, g_raw, beta_raw, S0.
+    """
+    if keys not in KEYS or decay not in DECAYS or write not in WRITES:
+        raise ValueError("unknown edge workload option")
+    gen = _generator(seed, device)
+    dev = gen.device
+    rn = lambda *shape: torch.randn(*shape, generator=gen, device=dev)
+    cu = None
+    n_states = B
+    if lengths is not None:
+        lengths = torch.as_tensor(lengths, dtype=torch.int64)
+        c = torch.zeros(lengths.numel() + 1, dtype=torch.int64)
+        c[1:] = torch.cumsum(lengths, 0)
+        if B != 1 or int(c[-1]) != T:
+            raise ValueError("a packed batch needs B == 1 and T == sum(lengths)")
+        cu = c.to(torch.int32).to(device)
+        n_states = lengths.numel()
+    lead = (B, T, H)
+    q = _unit(rn(*lead, DK))
+    if keys == "corr":
+        base = _unit(rn(B, 1, H, DK))
+        k = _unit(base + sigma * rn(*lead, DK) / DK ** 0.5)
+    elif keys == "exact":
+        x = rn(*lead, DK)
+        rank = x.abs().argsort(dim=-1).argsort(dim=-1)      # a random half of the coordinates
+        k = torch.where(rank >= DK // 2, torch.sign(x) / 8, torch.zeros_like(x))
+    else:
+        k = _unit(rn(*lead, DK))
+    if q_is_k:
+        q = k
+    v = rn(*lead, DV) * value_scale
+    g = -F.softplus(rn(*lead))
+    if decay == "slow":
+        g = 0.02 * g
+    elif decay == "none":
+        g = torch.zeros_like(g)
+    elif decay == "full":
+        g = torch.full_like(g, -1e4)
+    beta = torch.sigmoid(rn(*lead))
+    if write == "one":
+        beta = torch.ones_like(beta)
+    elif write == "zero":
+        beta = torch.zeros_like(beta)
+    S0 = 0.1 * value_scale * rn(n_states, H, DK, DV) if s0 else None
+    name = f"edge[{keys}{'' if keys == 'iid' else f' s={sigma}'} g={decay} b={write} x{value_scale:g}]"
+    meta = dict(B=B, T=T, H=H, seed=seed, tokens=T if lengths is not None else B * T)
+    if lengths is not None:
+        meta.update(N=n_states, lengths=lengths.tolist())
+    return Workload(name, q.to(io_dtype), k.to(io_dtype), v.to(io_dtype), g, beta, S0,
+                    cu, chunk, meta)

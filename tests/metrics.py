@@ -73,3 +73,29 @@ def bf16_output_ok(x, r, tol, spans, H):
         ratio = np.max(np.abs(a - b) / np.where(bound > 0, bound, 1e-300))
         worst = max(worst, float(ratio))
     return worst <= 1.0, worst
+
+
+def gated_output_ok(Y, Yr, Or, z, w, eps, tol, spans, H):
+    """Bound for the gated RMS norm's output y = w o / rho silu(z),
+    rho = sqrt(mean(o^2) + eps) per (token, head) row, derived from the bar on
+    O: if each element of O is within D = tol * max_slice|O_ref| of the
+    reference, then to first order
+        |y_j - r_j| <= |w_j silu(z_j)| (D / rho) (1 + |o_j| / rho)
+    (the Jacobian of the norm is (w silu(z) / rho)(I - o o^T / (n rho^2)), and
+    sum_i |o_i| <= n rho).  A bf16 output may also differ by half an ulp.
+    Returns (ok, worst ratio of |y - r| to the bound)."""
+    Y, Yr, Or, z = f64(Y), f64(Yr), f64(Or), f64(z)
+    w = f64(w)
+    worst = 0.0
+    for yy, rr, oo, zz in zip(slices_tokens(Y, spans, H), slices_tokens(Yr, spans, H),
+                              slices_tokens(Or, spans, H), slices_tokens(z, spans, H)):
+        if oo.size == 0:
+            continue
+        d = tol * np.max(np.abs(oo))
+        rho = np.sqrt(np.mean(oo * oo, axis=-1, keepdims=True) + eps)
+        gate = np.abs(w * zz / (1.0 + np.exp(-zz)))
+        bound = gate * (d / rho) * (1.0 + np.abs(oo) / rho) \
+            + bf16_half_ulp(np.maximum(np.abs(yy), np.abs(rr)))
+        ratio = np.max(np.abs(yy - rr) / np.where(bound > 0, bound, 1e-300))
+        worst = max(worst, float(ratio))
+    return worst <= 1.0, worst
