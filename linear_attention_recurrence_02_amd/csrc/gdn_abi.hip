@@ -147,19 +147,18 @@ int launch_prefill(const gdn::PrefillArgs &a, void *stream) {
 }
 
 // Workspace of the segmented prompt form: the segments' offsets, each
-// sequence's first segment, a zero copy of v, and three arrays of one state per
-// (segment, head).  A uniform batch has N ceil(T / L) segments (at least N); a
-// packed one at most N + ceil(T / L), each sequence rounding up once.  Parts are
-// 256-byte aligned; false for sizes it cannot hold.
+// sequence's first segment, and three arrays of one state per (segment,
+// head).  A uniform batch has N ceil(T / L) segments (at least N); a packed one
+// at most N + ceil(T / L), each sequence rounding up once.  Parts are 256-byte
+// aligned; false for sizes it cannot hold.
 struct SegLayout {
-    int64_t Ns, rows, cu, seg, vzero, vzero_bytes, s1, m, b, total;
+    int64_t Ns, rows, cu, seg, s1, m, b, total;
 };
 
 bool seg_layout(int io_dtype, bool packed, int64_t N, int64_t T, int64_t H, int64_t L,
                 SegLayout &w) {
     if (!dims_ok(N) || !dims_ok(T) || H <= 0 || H >= 65536 || L <= 0) return false;
     if (io_dtype != GDN_F32 && io_dtype != GDN_BF16) return false;
-    const int64_t esz = io_dtype == GDN_BF16 ? 2 : 4;
     const int64_t per = (T + L - 1) / L;
     w.rows = packed ? T : N * T;
     if (w.rows >= kMaxDim) return false;           // the segments' offsets are int32
@@ -171,13 +170,82 @@ bool seg_layout(int io_dtype, bool packed, int64_t N, int64_t T, int64_t H, int6
     const int64_t state = gdn::kHeadDim * gdn::kHeadDim * 4;
     w.cu = 0;
     w.seg = up((w.Ns + 1) * 4);
-    w.vzero = w.seg + up((N + 1) * 4);
-    w.vzero_bytes = up(w.rows * H * gdn::kHeadDim * esz);
-    w.s1 = w.vzero + w.vzero_bytes;
+    w.s1 = w.seg + up((N + 1) * 4);
     w.m = w.s1 + up(units * state);
     w.b = w.m + up(units * state);
     w.total = w.b + up(units * state);
     return true;
+}
+
+// The segmented form on a validated call, with its workspace at `ws` (at
+// least w.total bytes, 256-byte aligned, disjoint from the call's buffers).
+int run_segmented(const gdn::PrefillArgs &a, const SegLayout &w, char *ws, int64_t segment_len,
+                  void *stream) {
+    const int64_t N = a.N, H = a.H;
+    int32_t *cu = reinterpret_cast<int32_t *>(ws + w.cu);    // the segments' offsets
+    int32_t *seg = reinterpret_cast<int32_t *>(ws + w.seg);  // each sequence's first segment
+    float *s1 = reinterpret_cast<float *>(ws + w.s1);   // identity states, then S_in
+    float *m = reinterpret_cast<float *>(ws + w.m);     // state maps
+    float *b = reinterpret_cast<float *>(ws + w.b);     // zero-start states, then end states
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    auto run = [&](const void *vv, const float *s0, void *O, float *st_out) {
+        gdn::PrefillArgs r = a;
+        r.v = vv;
+        r.S0 = s0;
+        r.O = O;
+        r.S_T = st_out;
+        r.cu_seqlens = cu;
+        r.N = w.Ns;
+        r.T = w.rows;
+        return launch_prefill(r, stream);
+    };
+    if (gdn::launch_segment_prep(a.cu_seqlens, N, a.T, segment_len, w.Ns, seg, cu, s1, w.Ns * H, s) !=
+        hipSuccess)
+        return GDN_ERR_HIP;
+    int rc = run(a.v, nullptr, nullptr, b);            // B: each segment from zero, no O
+    if (rc == GDN_OK) rc = run(nullptr, s1, nullptr, m);   // M: no values, from the identity
+    if (rc != GDN_OK) return rc;
+    if (gdn::launch_segment_scan(m, b, a.S0, s1, seg, N, H, s) != hipSuccess) return GDN_ERR_HIP;
+    rc = run(a.v, s1, a.O, b);                         // O and the end states from S_in
+    if (rc != GDN_OK) return rc;
+    return gdn::launch_segment_gather(b, a.S0, seg, a.S_T, N, H, s) == hipSuccess ? GDN_OK
+                                                                                   : GDN_ERR_HIP;
+}
+
+// Validation shared by the two segmented entry points: fills `a` and `w`;
+// GDN_OK with w.total == 0 means the call is the plain form (launched here).
+int check_segmented(const void *q, const void *k, const void *v, int io_dtype, const float *g,
+                    const float *beta, const float *S0, const int32_t *cu_seqlens, int64_t B_or_N,
+                    int64_t T, int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                    int64_t segment_len, void *O, float *S_T, void *stream, gdn::PrefillArgs &a,
+                    SegLayout &w, int64_t &tok_bytes, bool &done) {
+    done = false;
+    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
+                                 dv, chunk, O, S_T, a, tok_bytes);
+    if (st != GDN_OK) return st;
+    if (segment_len <= 0 || segment_len % chunk != 0) return GDN_ERR_INVALID_ARG;
+    if (!seg_layout(io_dtype, cu_seqlens != nullptr, B_or_N, T, H, segment_len, w))
+        return GDN_ERR_INVALID_ARG;
+    if (const int sc = check_seqlens_debug(cu_seqlens, B_or_N, T, stream)) return sc;
+    // a uniform batch of one segment per sequence is the plain form
+    if (B_or_N == 0 || (!cu_seqlens && T <= segment_len)) {
+        done = true;
+        return launch_prefill(a, stream);
+    }
+    return GDN_OK;
+}
+
+// Whether the byte range [p, p + bytes) overlaps any buffer of the call.
+bool overlaps_call(const void *p, int64_t bytes, const gdn::PrefillArgs &a, int64_t tok_bytes) {
+    const int64_t gb = (a.cu_seqlens ? a.T : a.N * a.T) * a.H * 4,
+                  st_bytes = a.N * a.H * gdn::kHeadDim * gdn::kHeadDim * 4;
+    const Range rw = span_of(p, bytes);
+    for (Range r : {span_of(a.q, tok_bytes), span_of(a.k, tok_bytes), span_of(a.v, tok_bytes),
+                    span_of(a.g, gb), span_of(a.beta, gb), span_of(a.O, tok_bytes),
+                    span_of(a.S_T, st_bytes), a.S0 ? span_of(a.S0, st_bytes) : Range{0, 0},
+                    a.cu_seqlens ? span_of(a.cu_seqlens, (a.N + 1) * 4) : Range{0, 0}})
+        if (overlap(rw, r)) return true;
+    return false;
 }
 
 }  // namespace
@@ -199,57 +267,16 @@ int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int
                                 void *workspace, int64_t workspace_bytes, void *O, float *S_T,
                                 void *stream) {
     gdn::PrefillArgs a{};
+    SegLayout w{};
     int64_t tok_bytes = 0;
-    const int st = check_prefill(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
-                                 dv, chunk, O, S_T, a, tok_bytes);
-    if (st != GDN_OK) return st;
-    if (segment_len <= 0 || segment_len % chunk != 0) return GDN_ERR_INVALID_ARG;
-    const int64_t N = B_or_N;
-    SegLayout w;
-    if (!seg_layout(io_dtype, cu_seqlens != nullptr, N, T, H, segment_len, w))
-        return GDN_ERR_INVALID_ARG;
-    if (const int sc = check_seqlens_debug(cu_seqlens, N, T, stream)) return sc;
-    // a uniform batch of one segment per sequence is the plain form
-    if (N == 0 || (!cu_seqlens && T <= segment_len)) return launch_prefill(a, stream);
+    bool done = false;
+    const int st = check_segmented(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
+                                   dv, chunk, segment_len, O, S_T, stream, a, w, tok_bytes, done);
+    if (st != GDN_OK || done) return st;
     if (!workspace || workspace_bytes < w.total || !aligned(workspace, 256))
         return GDN_ERR_INVALID_ARG;
-    const int64_t gb = w.rows * H * 4, st_bytes = N * H * gdn::kHeadDim * gdn::kHeadDim * 4;
-    const Range rw = span_of(workspace, w.total);
-    for (Range r : {span_of(q, tok_bytes), span_of(k, tok_bytes), span_of(v, tok_bytes),
-                    span_of(g, gb), span_of(beta, gb), span_of(O, tok_bytes),
-                    span_of(S_T, st_bytes), S0 ? span_of(S0, st_bytes) : Range{0, 0},
-                    cu_seqlens ? span_of(cu_seqlens, (N + 1) * 4) : Range{0, 0}})
-        if (overlap(rw, r)) return GDN_ERR_ALIAS;
-
-    char *ws = static_cast<char *>(workspace);
-    int32_t *cu = reinterpret_cast<int32_t *>(ws + w.cu);    // the segments' offsets
-    int32_t *seg = reinterpret_cast<int32_t *>(ws + w.seg);  // each sequence's first segment
-    void *vzero = ws + w.vzero;
-    float *s1 = reinterpret_cast<float *>(ws + w.s1);   // identity states, then S_in
-    float *m = reinterpret_cast<float *>(ws + w.m);     // state maps
-    float *b = reinterpret_cast<float *>(ws + w.b);     // zero-start states, then end states
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    auto run = [&](const void *vv, const float *s0, float *st_out) {
-        gdn::PrefillArgs r = a;
-        r.v = vv;
-        r.S0 = s0;
-        r.S_T = st_out;
-        r.cu_seqlens = cu;
-        r.N = w.Ns;
-        r.T = w.rows;
-        return launch_prefill(r, stream);
-    };
-    if (gdn::launch_segment_prep(cu_seqlens, N, T, segment_len, w.Ns, seg, cu, vzero, w.vzero_bytes,
-                                 s1, w.Ns * H, s) != hipSuccess)
-        return GDN_ERR_HIP;
-    int rc = run(v, nullptr, b);                       // B: each segment from zero
-    if (rc == GDN_OK) rc = run(vzero, s1, m);          // M: V = 0 from the identity
-    if (rc != GDN_OK) return rc;
-    if (gdn::launch_segment_scan(m, b, S0, s1, seg, N, H, s) != hipSuccess) return GDN_ERR_HIP;
-    rc = run(v, s1, b);                                // O and the end states from S_in
-    if (rc != GDN_OK) return rc;
-    return gdn::launch_segment_gather(b, S0, seg, S_T, N, H, s) == hipSuccess ? GDN_OK
-                                                                               : GDN_ERR_HIP;
+    if (overlaps_call(workspace, w.total, a, tok_bytes)) return GDN_ERR_ALIAS;
+    return run_segmented(a, w, static_cast<char *>(workspace), segment_len, stream);
 }
 
 int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,

@@ -95,8 +95,8 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
 hipError_t launch_decode_preop(const DecodePreopArgs &a, hipStream_t stream);
 // Helpers of the segmented prompt form (see gdn_segmented.hip).
 hipError_t launch_segment_prep(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
-                               int32_t *seg, int32_t *cu_out, void *vzero, int64_t vzero_bytes,
-                               float *sid, int64_t units, hipStream_t stream);
+                               int32_t *seg, int32_t *cu_out, float *sid, int64_t units,
+                               hipStream_t stream);
 hipError_t launch_segment_scan(const float *M, const float *B, const float *S0, float *Sin,
                                const int32_t *seg, int64_t N, int64_t H, hipStream_t stream);
 hipError_t launch_segment_gather(const float *Sout, const float *S0, const int32_t *seg,

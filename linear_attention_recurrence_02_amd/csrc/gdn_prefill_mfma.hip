@@ -58,6 +58,8 @@
 //   The two roles run as two separate loops under a wave-uniform branch and
 //   execute the same number of barriers (1 + 3 (nch + 1)).  Phase 2 is the
 //   producers' critical phase, so they take wave priority in it.
+// A null v stands for zero values and a null O for no output rows (the
+// segmented form's state-map runs).
 // Template variants: kGated fuses the block's gated RMS norm into the output
 // step (the gate rows fetched into LDS a period ahead; the consumer waves
 // exchange per-row sums through LDS); kDoubling picks the T_ii method; kRank
@@ -206,7 +208,12 @@ struct Producer {
     __device__ void prefetch(const Unit &u, int pc, int p, int l, int r16, int q) {
         const int nv = u.rows_in(pc);
         load_rows(pK, u.k, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
-        load_rows(pV, u.v, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
+        if (u.v) {
+            load_rows(pV, u.v, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) pV[s] = zero4();
+        }
         load_rows(pQ, u.q, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
         const int64_t gi = (l < nv ? u.row0(pc) + l : u.start) * u.H + u.h;
         pg = u.g[gi];
@@ -954,7 +961,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int t = 16 * m + r16;
-                    if (t < cnv) {
+                    if (O && t < cnv) {
                         const uint32_t off = static_cast<uint32_t>(t) * HD;
 #pragma unroll
                         for (int cc = 0; cc < 2; ++cc) {

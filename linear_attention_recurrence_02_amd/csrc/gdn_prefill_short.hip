@@ -30,7 +30,8 @@
 //      lane ends with four adjacent columns of one token row), and the state
 //      update.
 // The state is loaded before the first chunk is staged and first used in
-// step 4, so its load overlaps steps 1 to 3.
+// step 4, so its load overlaps steps 1 to 3.  A null v stands for zero values
+// and a null O for no output rows.
 //
 // Precision.  Sums are fp32; the state, D and U are fp32 between products.
 // K and Q enter the products as fp16 copies of the bf16 inputs (exact for
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
         const int64_t off = (row * H + h) * D + sc;
         xk = *reinterpret_cast<const f32x4 *>(k + off);
         xq = *reinterpret_cast<const f32x4 *>(q + off);
-        xv = *reinterpret_cast<const f32x4 *>(v + off);
+        xv = v ? *reinterpret_cast<const f32x4 *>(v + off) : zero4();
         if (w == 0) {
             const int64_t gi = (r16 < nv ? start + int64_t(c) * CS + r16 : start) * H + h;
             xg = g[gi];
@@ -305,7 +306,7 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
                 Ot[cc] = mfma(cat(d.hi, d.lo), cat(ah, ah), Ot[cc] * egt);
                 Ot[cc] = mfma16(d.hi, al, Ot[cc]) * un;
             }
-            if (r16 < nv) {
+            if (O && r16 < nv) {
                 OutT *orow = O + ((start + int64_t(c) * CS + r16) * H + h) * D + 32 * w + 4 * qd;
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {

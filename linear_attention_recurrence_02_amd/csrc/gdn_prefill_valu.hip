@@ -21,6 +21,8 @@
 // row-strided reads hit distinct LDS banks), D, N and the masked decayed
 // QK^T live in LDS.
 //
+// A null v stands for zero values and a null O for no output rows.
+//
 // With the gated RMS norm on the output (the norm a Gated DeltaNet block
 // applies after the recurrence), each output row is reduced across the
 // workgroup as it is produced (one barrier per row, partial sums
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
                 ks += kt[i] * S[i];
                 qs += qt[i] * S[i];
             }
-            const float vt = t < nv ? to_f32(v[((row0 + t) * H + h) * kHeadDim + j]) : 0.f;
+            const float vt = v && t < nv ? to_f32(v[((row0 + t) * H + h) * kHeadDim + j]) : 0.f;
             float r = sB[t] * (vt - sEG[t] * ks);
             for (int s = 0; s < t; ++s) r -= sN[t * C + s] * sD[s * kHeadDim + j];
             sD[t * kHeadDim + j] = r;
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
                     O[oi] = from_f32<OutT>(nw * (o / sqrtf(ms + eps)) * silu);
                 }
             } else {
-                if (t < nv) O[oi] = from_f32<OutT>(o);
+                if (O && t < nv) O[oi] = from_f32<OutT>(o);
             }
         }
 

@@ -14,8 +14,8 @@
 //
 // This file holds the small kernels around those runs: the plan (each
 // sequence's first segment and the segments' offsets, for a uniform or a
-// packed batch), the zero values and identity states the map run needs, the
-// scan, and the gather of each sequence's final state.
+// packed batch), the identity states the map run starts from (it runs with no
+// values: a null v), the scan, and the gather of each sequence's final state.
 
 #include "gdn_internal.hpp"
 
@@ -33,13 +33,13 @@ constexpr int64_t kState = int64_t(D) * D;
 // starts at row start + j L.  The numbering is capped at Ns, the workspace's
 // segment count (reached only by offsets that overlap, which give wrong
 // results but stay in bounds); the segments past the last sequence start, and
-// end, at the last row.  The other workgroups write the zero values and one
-// identity state per segment unit.
+// end, at the last row.  The other workgroups write one identity state per
+// segment unit.
 constexpr int kPrepThreads = 256;
 __global__ __launch_bounds__(kPrepThreads) void segment_prep_kernel(
     const int32_t *__restrict__ cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
-    int32_t *__restrict__ seg, int32_t *__restrict__ cu_out, uint4 *__restrict__ vzero,
-    int64_t vzero16, float *__restrict__ sid, int64_t units) {
+    int32_t *__restrict__ seg, int32_t *__restrict__ cu_out, float *__restrict__ sid,
+    int64_t units) {
     const int tid = threadIdx.x;
     if (blockIdx.x == 0) {
         __shared__ int64_t sc[kPrepThreads];
@@ -77,7 +77,6 @@ __global__ __launch_bounds__(kPrepThreads) void segment_prep_kernel(
     }
     const int64_t stride = static_cast<int64_t>(gridDim.x - 1) * kPrepThreads;
     const int64_t i0 = static_cast<int64_t>(blockIdx.x - 1) * kPrepThreads + tid;
-    for (int64_t i = i0; i < vzero16; i += stride) vzero[i] = make_uint4(0u, 0u, 0u, 0u);
     static_assert(kState / 4 == 4096 && D == 128, "index bits below");
     for (int64_t i = i0; i < units * (kState / 4); i += stride) {
         const int e = 4 * static_cast<int>(i & 4095);          // first of 4 elements
@@ -251,11 +250,10 @@ __global__ __launch_bounds__(256) void segment_gather_kernel(const float *__rest
 }  // namespace
 
 hipError_t launch_segment_prep(const int32_t *cu_in, int64_t N, int64_t T, int64_t L, int64_t Ns,
-                               int32_t *seg, int32_t *cu_out, void *vzero, int64_t vzero_bytes,
-                               float *sid, int64_t units, hipStream_t stream) {
-    segment_prep_kernel<<<1025, kPrepThreads, 0, stream>>>(cu_in, N, T, L, Ns, seg, cu_out,
-                                                          static_cast<uint4 *>(vzero),
-                                                          vzero_bytes / 16, sid, units);
+                               int32_t *seg, int32_t *cu_out, float *sid, int64_t units,
+                               hipStream_t stream) {
+    segment_prep_kernel<<<1025, kPrepThreads, 0, stream>>>(cu_in, N, T, L, Ns, seg, cu_out, sid,
+                                                          units);
     return hipGetLastError();
 }
 

@@ -134,13 +134,14 @@ def test_prefill_segmented_validation(lib):
     W = A + 2048 * MB
     ws = lib.gdn_chunk_prefill_segmented_workspace
     need = ws(1, None, 2, 1000, 2, 256)
-    # 2 x 4 segments x 2 heads x 64 KiB three times, a zero copy of v, the offsets
-    assert need >= 3 * 16 * 65536 + 2 * 1000 * 2 * 256
+    # 2 x 4 segments x 2 heads x 64 KiB three times, plus the segments' offsets
+    # and each sequence's first segment (256-byte aligned parts)
+    assert need == 3 * 16 * 65536 + 256 + 256
     assert ws(1, None, 2, 1000, 2, 0) == -1
     assert ws(7, None, 2, 1000, 2, 256) == -1
     # a packed batch of N sequences and T rows is sized for N + ceil(T / L) segments
     packed = ws(1, A, 3, 2000, 2, 256)
-    assert packed >= 3 * (3 + 8) * 2 * 65536 + 2000 * 2 * 256
+    assert packed == 3 * (3 + 8) * 2 * 65536 + 256 + 256
     # the rows (B * T, or T when packed) must fit the int32 segment offsets
     assert ws(1, None, 2, 1 << 30, 1, 1 << 20) == -1
     assert ws(1, None, 1, (1 << 30) - 1, 1, 1 << 20) > 0
