@@ -57,7 +57,8 @@ typedef enum {
     GDN_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, misalignment */
     GDN_ERR_UNSUPPORTED = 2,   /* dk/dv != 128, chunk not in {16,32,64}, dtype */
     GDN_ERR_ALIAS = 3,         /* buffers overlap in a way the call forbids */
-    GDN_ERR_HIP = 4            /* the HIP runtime refused the launch */
+    GDN_ERR_HIP = 4,           /* the HIP runtime refused the launch */
+    GDN_ERR_SCRATCH = 5        /* more scratch than gdn_chunk_prefill_segmented_noalloc holds */
 } gdn_status;
 
 typedef enum {
@@ -195,6 +196,35 @@ int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int
                                 int64_t dk, int64_t dv, int64_t chunk, int64_t segment_len,
                                 void *workspace, int64_t workspace_bytes, void *O, float *S_T,
                                 void *stream);
+
+/*
+ * gdn_chunk_prefill_segmented_noalloc -- gdn_chunk_prefill_segmented without a
+ * workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that must not allocate, harnesses
+ * that forbid it).  The scratch is a file-scope device array in libgdn,
+ * gdn_noalloc_scratch_bytes() bytes (48 MiB + 64 KiB), one copy per GPU,
+ * held while the library is loaded; its address is looked up once per device
+ * on that device's first call.  The call allocates nothing.
+ *
+ *   Arguments, layouts and results as gdn_chunk_prefill_segmented.  A call
+ *   whose workspace (gdn_chunk_prefill_segmented_workspace) would exceed the
+ *   scratch returns GDN_ERR_SCRATCH with nothing enqueued; that is about
+ *   256 (segment, head) pairs, e.g. 16 heads of a 4096-token sequence in
+ *   256-token segments.
+ *   Every call on one GPU uses the same scratch: calls that overlap in time
+ *   on one GPU (on different streams, or from different host threads without
+ *   ordering) race and give wrong results.  Calls in one stream are ordered
+ *   and safe.  Nothing in the scratch needs to start at zero (each call
+ *   writes every part it reads).
+ */
+int gdn_chunk_prefill_segmented_noalloc(const void *q, const void *k, const void *v, int io_dtype,
+                                        const float *g, const float *beta, const float *S0,
+                                        const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                                        int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                                        int64_t segment_len, void *O, float *S_T, void *stream);
+
+/* Bytes of device scratch gdn_chunk_prefill_segmented_noalloc holds per GPU. */
+int64_t gdn_noalloc_scratch_bytes(void);
 
 /* Bytes of workspace gdn_chunk_prefill_segmented needs for these sizes, or -1
  * if they are invalid: per segment and head, three states of 64 KiB (a

@@ -18,10 +18,11 @@ import torch  # imported first so that libgdn binds to torch's HIP runtime
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgdn.so")
 
-GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP = range(5)
+GDN_OK, GDN_ERR_INVALID_ARG, GDN_ERR_UNSUPPORTED, GDN_ERR_ALIAS, GDN_ERR_HIP, GDN_ERR_SCRATCH = range(6)
 GDN_F32, GDN_BF16, GDN_BF16_F32_OUT = 0, 1, 2
 EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_prefill_ex",
             "gdn_chunk_prefill_segmented", "gdn_chunk_prefill_segmented_workspace",
+            "gdn_chunk_prefill_segmented_noalloc", "gdn_noalloc_scratch_bytes",
             "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step",
             "gdn_decode_step_ex", "gdn_decode_step_preop")
 GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
@@ -66,6 +67,12 @@ def load_library(path: Optional[str] = None):
                                                 i64, i64, i64, i64, i64, i64, vp, i64, vp, vp,
                                                 vp]
     lib.gdn_chunk_prefill_segmented.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_segmented_noalloc.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp,
+                                                        i64, i64, i64, i64, i64, i64, i64, vp,
+                                                        vp, vp]
+    lib.gdn_chunk_prefill_segmented_noalloc.restype = ctypes.c_int
+    lib.gdn_noalloc_scratch_bytes.argtypes = []
+    lib.gdn_noalloc_scratch_bytes.restype = i64
     lib.gdn_chunk_prefill_segmented_workspace.argtypes = [ctypes.c_int, vp, i64, i64, i64, i64]
     lib.gdn_chunk_prefill_segmented_workspace.restype = i64
     lib.gdn_chunk_prefill_gated.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64,
@@ -228,6 +235,44 @@ def gdn_chunk_prefill_segmented(q, k, v, g, beta, S0=None, chunk=64, segment_len
         _ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
     _check(st)
     return O, S_T
+
+
+def gdn_chunk_prefill_segmented_noalloc(q, k, v, g, beta, S0=None, chunk=64, segment_len=256, *,
+                                        cu_seqlens=None, O=None, S_T=None, stream=None):
+    """gdn_chunk_prefill_segmented with the library's own per-GPU scratch instead
+    of a workspace (see include/gdn.h): nothing is allocated by the call except
+    O / S_T here when they are not given.  Returns (O, S_T)."""
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed batches (cu_seqlens) need B == 1")
+    if k.shape != q.shape or v.shape[:3] != q.shape[:3] or k.dtype != q.dtype \
+            or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share shape [B, T, H, d] and dtype")
+    if g.shape != (B, T, H) or beta.shape != (B, T, H):
+        raise ValueError("g and beta must be [B, T, H]")
+    if O is None:
+        O = torch.empty_like(v)
+    if S_T is None:
+        S_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+    if O.dtype != q.dtype or O.shape != v.shape:
+        raise ValueError("O must match v's shape and dtype")
+    if S_T.shape != (N, H, dk, dv) or (S0 is not None and S0.shape != (N, H, dk, dv)):
+        raise ValueError("S0 / S_T must be [N, H, dk, dv]")
+    st = load_library().gdn_chunk_prefill_segmented_noalloc(
+        _ptr(q, name="q"), _ptr(k, name="k"), _ptr(v, name="v"), _io_dtype(q),
+        _ptr(g, torch.float32, "g"), _ptr(beta, torch.float32, "beta"),
+        _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
+        N, T, H, dk, dv, int(chunk), int(segment_len), _ptr(O, name="O"),
+        _ptr(S_T, torch.float32, "S_T"), _stream(stream))
+    _check(st)
+    return O, S_T
+
+
+def noalloc_scratch_bytes() -> int:
+    """Bytes of the per-GPU scratch gdn_chunk_prefill_segmented_noalloc holds."""
+    return load_library().gdn_noalloc_scratch_bytes()
 
 
 def gdn_chunk_prefill_gated(q, k, v, g, beta, z, norm_w, eps, S0=None, cu_seqlens=None,

@@ -10,6 +10,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 namespace {
@@ -66,6 +67,7 @@ const char *gdn_status_string(int status) {
     case GDN_ERR_UNSUPPORTED: return "unsupported configuration (dk/dv must be 128, chunk 16/32/64, dtype f32/bf16)";
     case GDN_ERR_ALIAS: return "buffers overlap in a way the call forbids";
     case GDN_ERR_HIP: return "HIP runtime error while enqueuing a kernel";
+    case GDN_ERR_SCRATCH: return "the call needs more scratch than the no-allocation entry point holds";
     default: return "unknown status";
     }
 }
@@ -248,6 +250,28 @@ bool overlaps_call(const void *p, int64_t bytes, const gdn::PrefillArgs &a, int6
     return false;
 }
 
+// Scratch of the no-allocation segmented form: a file-scope device array,
+// one copy per GPU, held while the library is loaded.  Host code uses the
+// address hipGetSymbolAddress returns for the current device, never the
+// array's name (which on the host is only a stand-in).
+constexpr int64_t kNoAllocScratchBytes = (int64_t(48) << 20) + (int64_t(64) << 10);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+// The current device's address of `scratch`, looked up once per device.
+char *scratch_address() {
+    static std::mutex mu;
+    static char *addr[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = static_cast<char *>(p);
+    }
+    return addr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -278,6 +302,26 @@ int gdn_chunk_prefill_segmented(const void *q, const void *k, const void *v, int
     if (overlaps_call(workspace, w.total, a, tok_bytes)) return GDN_ERR_ALIAS;
     return run_segmented(a, w, static_cast<char *>(workspace), segment_len, stream);
 }
+
+int gdn_chunk_prefill_segmented_noalloc(const void *q, const void *k, const void *v, int io_dtype,
+                                        const float *g, const float *beta, const float *S0,
+                                        const int32_t *cu_seqlens, int64_t B_or_N, int64_t T,
+                                        int64_t H, int64_t dk, int64_t dv, int64_t chunk,
+                                        int64_t segment_len, void *O, float *S_T, void *stream) {
+    gdn::PrefillArgs a{};
+    SegLayout w{};
+    int64_t tok_bytes = 0;
+    bool done = false;
+    const int st = check_segmented(q, k, v, io_dtype, g, beta, S0, cu_seqlens, B_or_N, T, H, dk,
+                                   dv, chunk, segment_len, O, S_T, stream, a, w, tok_bytes, done);
+    if (st != GDN_OK || done) return st;
+    if (w.total > kNoAllocScratchBytes) return GDN_ERR_SCRATCH;
+    char *ws = scratch_address();
+    if (!ws) return GDN_ERR_HIP;
+    return run_segmented(a, w, ws, segment_len, stream);
+}
+
+int64_t gdn_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
 
 int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
                       const float *g, const float *beta, const float *S0,

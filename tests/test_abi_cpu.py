@@ -169,6 +169,34 @@ def test_prefill_segmented_validation(lib):
     assert seg(cu=cu, B=3, T=2000, wsb=packed, ws=cu - 256) == binding.GDN_ERR_ALIAS
 
 
+def test_prefill_segmented_noalloc_validation(lib):
+    """The no-allocation segmented form checks its arguments like the workspace
+    form and refuses, before any device work, a call whose workspace would not
+    fit its scratch."""
+    scratch = lib.gdn_noalloc_scratch_bytes()
+    assert scratch == 48 * MB + 64 * 1024
+
+    def seg(**kw):
+        a = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB, beta=A + 200 * MB,
+                 S0=A + 256 * MB, cu=None, B=2, T=1000, H=2, chunk=64, L=256,
+                 O=A + 512 * MB, S_T=A + 768 * MB)
+        a.update(kw)
+        return lib.gdn_chunk_prefill_segmented_noalloc(
+            a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"], a["S0"], a["cu"], a["B"],
+            a["T"], a["H"], 128, 128, a["chunk"], a["L"], a["O"], a["S_T"], None)
+    assert seg(L=100) == binding.GDN_ERR_INVALID_ARG               # not a multiple of chunk
+    assert seg(q=None) == binding.GDN_ERR_INVALID_ARG
+    assert seg(chunk=48) == binding.GDN_ERR_UNSUPPORTED
+    assert seg(B=0) == binding.GDN_OK
+    # 16 heads of 4096 tokens in 256-token segments fit (256 segment-heads) ...
+    fits = lib.gdn_chunk_prefill_segmented_workspace(1, None, 1, 4096, 16, 256)
+    assert 0 < fits <= scratch
+    # ... 32 heads do not: refused with its own status, nothing enqueued
+    assert lib.gdn_chunk_prefill_segmented_workspace(1, None, 1, 4096, 32, 256) > scratch
+    assert seg(B=1, T=4096, H=32) == binding.GDN_ERR_SCRATCH
+    assert b"scratch" in lib.gdn_status_string(binding.GDN_ERR_SCRATCH)
+
+
 def gated(lib, q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB,
           beta=A + 200 * MB, S0=A + 256 * MB, cu=None, N=2, T=64, H=2, dk=128,
           dv=128, chunk=64, z=A + 1024 * MB, w=A + 1100 * MB, eps=1e-6, Y=A + 512 * MB,
