@@ -6,10 +6,15 @@
 A step is one gdn_decode_step call over the batched-decode workload (B = 64
 sequences x H = 16 heads, bf16 q/k/v, fp32 g/beta, fp32 state [64,16,128,128]
 updated in place), each step with its own freshly drawn token.  W untimed
-steps run first; then exactly K steps are timed between two device
-synchronisations, launched as one captured HIP graph so that host launch cost
-does not pace the GPU.  `value` is the state traffic those K steps move
-(2 x 64 KiB per head-step) per second.
+steps run first; the K steps are captured as one HIP graph (so that host
+launch cost does not pace the GPU), replayed once untimed, and then replayed
+once more between two device synchronisations, timed by device events on the
+replay's stream.  `value` is the state traffic those K steps move (2 x 64 KiB
+per head-step) per second, `ms_per_step` their time over K and
+`roofline.achieved` their algorithmic bytes per launch over the same time.
+With one state batch updated in place, the 64 MiB state stays in the 256 MB
+last-level cache; the same steps over eight batches in turn (512 MiB), with
+the non-temporal state form, give `roofline_state_from_hbm`.
 
 The same run times the prompt form (gdn_chunk_prefill) on the large prefill
 (B=8, H=32, T=16384, chunk 64, bf16, zero S0) and on the long, packed
@@ -41,6 +46,13 @@ HBM_PEAK = 8.0e12            # B/s, MI355X HBM3E
 BF16_PEAK = 2.5166e15        # flop/s, dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 DK = DV = 128
 STATE_BYTES = DK * DV * 4    # one fp32 head state
+
+
+# What the bf16 prompt-form legs compute in: matrix-core products on fp16
+# operands (hi + lo pairs where the recurrence needs them) and bf16 values,
+# fp32 accumulation, fp32 state.
+PREFILL_ARITH = ("bf16 io; matrix-core products on fp16 operands (split into hi + lo "
+                 "pairs where needed) and bf16 values, fp32 accumulation and state")
 
 
 def log(*a):
@@ -125,10 +137,11 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold, streaming=False):
             gdn.gdn_decode_step(w.q[s], w.k[s], w.v[s], w.g[s], w.beta[s],
                                 states[s % nbuf], o=outs[s], streaming=streaming)
     torch.cuda.synchronize()
-    graph.replay()          # untimed replay (first-replay setup cost)
-    torch.cuda.synchronize()
-    for st in states:
-        st.copy_(w.S0)
+    # one untimed replay (first-replay setup cost); the timed replay follows it
+    # directly, so each state batch starts where that replay left it, as in a
+    # steady stream of steps (with one batch, the 64 MiB state then sits in the
+    # 256 MB last-level cache)
+    graph.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -151,22 +164,25 @@ def bench_decode(torch, gdn, inputs, steps, warmup, cold, streaming=False):
     return dict(units=units, wall_s=wall, gpu_ms=gpu_ms, eager_s=eager, workload=w)
 
 
-def state_traffic_ceiling(torch, S0, steps):
+def state_traffic_ceiling(torch, S0, steps, nbuf=1):
     """Microseconds per launch for torch's in-place elementwise pass over a
     tensor of the decode state's size (read once, written once) and for a
     device copy of it, each captured ``steps`` times in a graph like the decode
-    steps: what moving the same bytes costs without any arithmetic."""
-    x = S0.clone()
-    y = torch.empty_like(x)
+    steps, over ``nbuf`` such tensors in turn: what moving the same bytes
+    costs without any arithmetic (nbuf = 8 puts 512 MiB in play, more than the
+    last-level cache holds)."""
+    xs = [S0.clone() for _ in range(nbuf)]
+    ys = [torch.empty_like(S0) for _ in range(nbuf)]
     out = {}
-    for tag, op in (("state_rmw_ceiling_us", lambda: x.mul_(1.0)),
-                    ("state_copy_ceiling_us", lambda: y.copy_(x))):
-        op()
+    pre = "" if nbuf == 1 else "cold_"
+    for tag, op in ((pre + "state_rmw_ceiling_us", lambda i: xs[i % nbuf].mul_(1.0)),
+                    (pre + "state_copy_ceiling_us", lambda i: ys[i % nbuf].copy_(xs[i % nbuf]))):
+        op(0)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph, stream=torch.cuda.Stream()):
-            for _ in range(steps):
-                op()
+            for i in range(steps):
+                op(i)
         graph.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -176,7 +192,7 @@ def state_traffic_ceiling(torch, S0, steps):
         torch.cuda.synchronize()
         out[tag] = e0.elapsed_time(e1) * 1e3 / steps
         del graph
-    del x, y
+    del xs, ys
     torch.cuda.empty_cache()
     return out
 
@@ -294,6 +310,7 @@ def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
     return {
         "workload": w.name + ("_gated_norm" if gate is not None else "")
                     + (f"_segmented_{segment_len}" if segment_len is not None else ""),
+        "arith": PREFILL_ARITH if esz == 2 else "fp32 arithmetic (vector kernel)",
         "tokens": tokens, "heads": H, "chunk": w.chunk,
         "seconds": t, "tokens_per_s": tokens / t,
         "mfma_frac": flops / t / BF16_PEAK, "hbm_frac": nbytes / t / HBM_PEAK,
@@ -439,7 +456,10 @@ def main():
                     help="time the decode with non-temporal state loads and stores "
                          "(gdn_decode_step_ex, GDN_STATE_STREAMING)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None)
+    ap.add_argument("--only", choices=["decode", "decode-step", "prefill"], default=None,
+                    help="decode: the decode legs; decode-step: only the headline decode "
+                         "steps (the command the kernel trace in profiles/ is taken on); "
+                         "prefill: the prompt-form legs")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run a plain device-to-device copy of this many MiB "
                          "(5 times), to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -473,7 +493,8 @@ def main():
         "metric": "prefill tokens/s (MFMA %) and decode state GB/s (HBM %) on 1 MI355X",
         "value": None, "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 io, fp32 state/math",
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 io; decode step in fp32 arithmetic, fp32 state",
         "data": "synthetic (seeded device draws; q,k unit-norm, g=-softplus(N(0,1)), "
                 "beta=sigmoid(N(0,1)), S0~0.1*N(0,1))",
         "config": {"workload": "batched decode step: B=64 sequences x H=16 heads, "
@@ -483,30 +504,41 @@ def main():
     }
 
     dec = None
-    if args.only in (None, "decode"):
+    if args.only in (None, "decode", "decode-step"):
         log("decode: generating inputs and capturing the step graph ...")
         dec = bench_decode(torch, gdn, inputs, args.steps, args.warmup, args.cold,
                            args.streaming)
         K = args.steps
         units = dec["units"]
-        state_gbs = K * units * 2 * STATE_BYTES / dec["wall_s"] / 1e9
-        avg_launch = dec["gpu_ms"] / 1e3 / K
+        # one timer for the value, ms_per_step and the roofline: the device
+        # events around the timed replay of the K steps (the host clock around
+        # the same replay is reported beside it)
+        gpu_s = dec["gpu_ms"] / 1e3
+        state_gbs = K * units * 2 * STATE_BYTES / gpu_s / 1e9
+        avg_launch = gpu_s / K
         alg = decode_bytes(units)
-        traffic = read_traffic("decode_bf16_b64h16", source_digest("gdn_decode.hip"))
-        result.update(value=state_gbs, ms_per_step=dec["wall_s"] * 1e3 / K)
+        traffic = read_traffic(
+            "decode_bf16_b64h16" + ("_streaming" if args.streaming else ""),
+            source_digest("gdn_decode.hip"))
+        result.update(value=state_gbs, ms_per_step=avg_launch * 1e3)
         result["roofline"] = roofline("hbm", alg / avg_launch / 1e9, HBM_PEAK / 1e9, "GB/s",
                                       traffic)
         result["decode"] = {
-            "steps_per_s": K / dec["wall_s"],
+            "steps_per_s": K / gpu_s,
             "avg_launch_us": avg_launch * 1e6,
+            "wall_us_per_step": dec["wall_s"] * 1e6 / K,
             "alg_bytes_per_launch": alg,
             "eager_launch_state_gbs": K * units * 2 * STATE_BYTES / dec["eager_s"] / 1e9,
             "cold_rotating_8_batches": bool(args.cold),
             "streaming_state": bool(args.streaming),
+            "state_residency": ("8 state batches of 64 MiB in turn (512 MiB): read from HBM"
+                                if args.cold else
+                                "one 64 MiB batch updated in place: after the first step it "
+                                "sits in the 256 MB last-level cache"),
         }
         log(f"decode: {state_gbs:.1f} GB/s state, {avg_launch*1e6:.2f} us/step "
-            f"(eager {dec['eager_s']*1e6/K:.2f} us/step)")
-        if not args.cold and not args.streaming:
+            f"(host clock {dec['wall_s']*1e6/K:.2f} us/step, eager {dec['eager_s']*1e6/K:.2f} us/step)")
+        if not args.cold and not args.streaming and args.only != "decode-step":
             # the same steps over eight state batches in turn (512 MiB, twice the
             # last-level cache), so that every step reads its state from HBM;
             # with plain and with non-temporal state access, and the latter on
@@ -517,8 +549,17 @@ def main():
                 r_ = bench_decode(torch, gdn, inputs, K, args.warmup, cold_, streaming_)
                 launch = r_["gpu_ms"] / 1e3 / K
                 result["decode"][f"{tag}_avg_launch_us"] = launch * 1e6
-                result["decode"][f"{tag}_state_gbs"] = K * units * 2 * STATE_BYTES / r_["wall_s"] / 1e9
+                result["decode"][f"{tag}_state_gbs"] = K * units * 2 * STATE_BYTES / (r_["gpu_ms"] / 1e3) / 1e9
                 result["decode"][f"{tag}_hbm_frac"] = alg / launch / HBM_PEAK
+                if tag == "cold_streaming":
+                    # the state read from HBM on every step: the roofline of the
+                    # decode step when the cache cannot hold the state
+                    result["roofline_state_from_hbm"] = dict(
+                        roofline("hbm", alg / launch / 1e9, HBM_PEAK / 1e9, "GB/s",
+                                 read_traffic("decode_bf16_b64h16_streaming",
+                                              source_digest("gdn_decode.hip"))),
+                        call="gdn_decode_step_ex (GDN_STATE_STREAMING)",
+                        workload="the same steps over 8 state batches of 64 MiB in turn")
                 log(f"decode, {'8 rotating state batches' if cold_ else 'one batch'}"
                     f"{', non-temporal state' if streaming_ else ''}: {launch*1e6:.2f} us/step, "
                     f"HBM {100*alg/launch/HBM_PEAK:.1f}%")
@@ -529,9 +570,12 @@ def main():
             # elementwise pass, and a device copy into a second buffer), captured
             # and replayed like the decode steps
             ceil = state_traffic_ceiling(torch, dec["workload"].S0, K)
+            ceil.update(state_traffic_ceiling(torch, dec["workload"].S0, K, nbuf=8))
             result["decode"].update(ceil)
-            log(f"same state bytes by torch: in-place pass {ceil['state_rmw_ceiling_us']:.2f} us, "
-                f"copy {ceil['state_copy_ceiling_us']:.2f} us per launch")
+            log(f"same state bytes by torch, one batch: in-place pass "
+                f"{ceil['state_rmw_ceiling_us']:.2f} us, copy {ceil['state_copy_ceiling_us']:.2f} us; "
+                f"8 batches in turn: {ceil['cold_state_rmw_ceiling_us']:.2f} us, "
+                f"{ceil['cold_state_copy_ceiling_us']:.2f} us per launch")
 
     if args.only in (None, "decode") and not args.cold and not args.streaming:
         dp = bench_decode_preop(torch, gdn, inputs, min(args.steps, 200))
