@@ -380,6 +380,43 @@ def bench_preop(torch, gdn, p, iters):
     }
 
 
+def bench_prefill_preop(torch, gdn, p, iters):
+    """The prompt form from the raw projections, gdn_chunk_prefill_preop (the
+    pre-operations inside the prompt kernel's chunk load), against the two
+    calls gdn_preop then gdn_chunk_prefill on the same inputs."""
+    B, T, H = p.xq.shape[:3]
+    st = p.state.clone()
+    S0 = torch.zeros(B, H, DK, DK, device="cuda")
+    O = torch.empty_like(p.xq)
+    S_T = torch.empty_like(S0)
+    pre = (torch.empty_like(p.xq), torch.empty_like(p.xk), torch.empty_like(p.xv),
+           torch.empty_like(p.a), torch.empty_like(p.b))
+
+    def fused():
+        gdn.gdn_chunk_prefill_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st, S0, O=O, S_T=S_T)
+
+    def separate():
+        q, k, v, g, b = gdn.gdn_preop(p.xq, p.xk, p.xv, p.a, p.b, p.conv_w, st, out=pre)
+        gdn.gdn_chunk_prefill(q, k, v, g, b, S0, None, 64, O=O, S_T=S_T)
+
+    for call in (fused, separate):
+        for _ in range(2):
+            call()
+        torch.cuda.synchronize()
+    t_sep = time_calls(torch, separate, iters)
+    t = time_calls(torch, fused, iters)
+    rows = B * T
+    esz = p.xq.element_size()
+    # projections and gate inputs in, O out, the states in and out, the FIFO
+    nbytes = rows * H * (4 * DK * esz + 8) + 2 * B * H * DK * DK * 4 + 2 * p.state.numel() * esz
+    return {
+        "workload": f"prefill_preop_{B}x{T}x{H}", "tokens": rows, "heads": H, "seconds": t,
+        "tokens_per_s": rows / t, "two_call_seconds": t_sep, "hbm_frac": nbytes / t / HBM_PEAK,
+        "alg_bytes": nbytes, "arith": PREFILL_ARITH + "; pre-operations in fp32",
+        "roofline": roofline("hbm", nbytes / t / 1e9, HBM_PEAK / 1e9, "GB/s"),
+    }
+
+
 def cpu_model():
     """The host CPU's model name, from /proc/cpuinfo (None if unreadable)."""
     try:
@@ -640,6 +677,10 @@ def main():
         r["roofline"]["traffic"] = read_traffic("preop_large", source_digest("gdn_preop.hip"))
         log(f"pre-operations {r['workload']}: {r['seconds']*1e3:.3f} ms, "
             f"{r['roofline']['achieved']:.0f} GB/s, HBM {100*r['hbm_frac']:.1f}%")
+        pre[r["workload"]] = r
+        r = bench_prefill_preop(torch, gdn, p, args.prefill_iters)
+        log(f"prompt form from the projections {r['workload']}: {r['seconds']*1e3:.3f} ms fused, "
+            f"{r['two_call_seconds']*1e3:.3f} ms as two calls")
         pre[r["workload"]] = r
         del p
         torch.cuda.empty_cache()

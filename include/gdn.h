@@ -330,6 +330,33 @@ int gdn_preop(const void *xq, const void *xk, const void *xv, int io_dtype, cons
               float *beta, void *stream);
 
 /*
+ * gdn_chunk_prefill_preop -- gdn_preop and gdn_chunk_prefill (chunk 64) as one
+ * prompt-form call from the raw projections: the pre-operations (gdn_preop's
+ * formulas and page citations: the causal conv over the FIFO window, silu,
+ * q and k divided by sqrt(sum y^2 + eps), g = -softplus(a), beta = sigmoid(b))
+ * run inside the 64-token matrix-core kernel as it loads each chunk, so q, k,
+ * v, g and beta never go to memory.  q and k enter the recurrence's products
+ * rounded from fp32 to fp16, v rounded to bf16 (the prompt form's own operand
+ * types), instead of all three rounded to bf16 in between as with two calls.
+ * The FIFO state is then advanced as by gdn_preop.
+ *
+ *   xq, xk, xv, a, b, conv_w, state_in, state_out, eps, kernel_size: as for
+ *               gdn_preop, with io_dtype GDN_BF16 only
+ *   S0, cu_seqlens, B_or_N, T, H, dk, dv, O, S_T: as for gdn_chunk_prefill
+ *               (O bf16), with chunk 64 only
+ *   Other io dtypes, chunks or kernel sizes: GDN_ERR_UNSUPPORTED.  O and S_T
+ *   must not overlap the inputs (gdn_chunk_prefill's rule, conv_w and state_in
+ *   included); state_out is exactly state_in (advanced in place) or overlaps
+ *   nothing (GDN_ERR_ALIAS).
+ */
+int gdn_chunk_prefill_preop(const void *xq, const void *xk, const void *xv, int io_dtype,
+                            const float *a, const float *b, const float *conv_w,
+                            const void *state_in, void *state_out, float eps, const float *S0,
+                            const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
+                            int64_t dk, int64_t dv, int64_t kernel_size, int64_t chunk, void *O,
+                            float *S_T, void *stream);
+
+/*
  * gdn_decode_step -- one token per (sequence, head) with the page's one-token
  * matrix form: with d = exp(g), a = S^T k and b = S^T q read in one pass over
  * S, delta = beta (v - d a), o = d b + (q.k) delta and S' = d S + k delta^T,

@@ -24,7 +24,7 @@ EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_
             "gdn_chunk_prefill_segmented", "gdn_chunk_prefill_segmented_workspace",
             "gdn_chunk_prefill_segmented_noalloc", "gdn_noalloc_scratch_bytes",
             "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step",
-            "gdn_decode_step_ex", "gdn_decode_step_preop")
+            "gdn_decode_step_ex", "gdn_decode_step_preop", "gdn_chunk_prefill_preop")
 GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
 GDN_STATE_CACHED, GDN_STATE_STREAMING = 0, 1
 
@@ -92,6 +92,10 @@ def load_library(path: Optional[str] = None):
                                           ctypes.c_float, vp, vp, ctypes.c_float, vp, i64, i64,
                                           i64, i64, ctypes.c_int, vp, vp]
     lib.gdn_decode_step_preop.restype = ctypes.c_int
+    lib.gdn_chunk_prefill_preop.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, vp,
+                                            ctypes.c_float, vp, vp, i64, i64, i64, i64, i64,
+                                            i64, i64, vp, vp, vp]
+    lib.gdn_chunk_prefill_preop.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -353,6 +357,44 @@ def gdn_preop(xq, xk, xv, a, b, conv_w, state, cu_seqlens=None, eps=1e-6, *, sta
         _stream(stream))
     _check(st)
     return q, k, v, g, beta
+
+
+def gdn_chunk_prefill_preop(xq, xk, xv, a, b, conv_w, state, S0=None, cu_seqlens=None,
+                            eps=1e-6, *, state_out=None, O=None, S_T=None, stream=None):
+    """The prompt form from the raw projections: gdn_preop's pre-operations
+    inside the 64-token kernel's chunk load (bf16 only).
+
+    xq, xk, xv, a, b, conv_w, state, cu_seqlens, eps: as for gdn_preop (the
+    FIFO ``state`` is advanced in place unless ``state_out`` is given);
+    S0: optional [N, H, 128, 128] fp32.  Returns (O, S_T) as gdn_chunk_prefill.
+    """
+    B, T, H, dk = xq.shape
+    dv = xv.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    if cu_seqlens is not None and B != 1:
+        raise ValueError("packed batches (cu_seqlens) need B == 1")
+    if xk.shape != xq.shape or xv.shape[:3] != xq.shape[:3] or xk.dtype != xq.dtype \
+            or xv.dtype != xq.dtype:
+        raise ValueError("xq, xk, xv must share shape [B, T, H, d] and dtype")
+    if a.shape != (B, T, H) or b.shape != (B, T, H):
+        raise ValueError("a and b must be [B, T, H]")
+    if state.shape != (N, 3, H, 3, max(dk, dv)) or state.dtype != xq.dtype:
+        raise ValueError("state must be [N, 3, H, 3, d] with the projections' dtype")
+    if state_out is None:
+        state_out = state
+    if O is None:
+        O = torch.empty(B, T, H, dv, dtype=xq.dtype, device=xq.device)
+    if S_T is None:
+        S_T = torch.empty(N, H, dk, dv, dtype=torch.float32, device=xq.device)
+    st = load_library().gdn_chunk_prefill_preop(
+        _ptr(xq, name="xq"), _ptr(xk, name="xk"), _ptr(xv, name="xv"), _io_dtype(xq),
+        _ptr(a, torch.float32, "a"), _ptr(b, torch.float32, "b"),
+        _ptr(conv_w, torch.float32, "conv_w"), _ptr(state, name="state"),
+        _ptr(state_out, name="state_out"), float(eps), _ptr(S0, torch.float32, "S0"),
+        _ptr(cu_seqlens, torch.int32, "cu_seqlens"), N, T, H, dk, dv, conv_w.shape[-1], 64,
+        _ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
+    _check(st)
+    return O, S_T
 
 
 def gdn_prefill_states(q, k, v, g, beta, S0=None, cu_seqlens=None, *, O=None, S_tok=None,

@@ -484,6 +484,53 @@ int gdn_preop(const void *xq, const void *xk, const void *xv, int io_dtype, cons
     return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
+int gdn_chunk_prefill_preop(const void *xq, const void *xk, const void *xv, int io_dtype,
+                            const float *a, const float *b, const float *conv_w,
+                            const void *state_in, void *state_out, float eps, const float *S0,
+                            const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
+                            int64_t dk, int64_t dv, int64_t kernel_size, int64_t chunk, void *O,
+                            float *S_T, void *stream) {
+    gdn::PrefillArgs pa{};
+    int64_t tok_bytes = 0;
+    const int st = check_prefill(xq, xk, xv, io_dtype, a, b, S0, cu_seqlens, B_or_N, T, H, dk,
+                                 dv, chunk, O, S_T, pa, tok_bytes);
+    if (st != GDN_OK) return st;
+    if (io_dtype != GDN_BF16 || chunk != 64 || kernel_size != 4) return GDN_ERR_UNSUPPORTED;
+    const int64_t N = B_or_N;
+    if (N > 0 && (!conv_w || !state_in || !state_out)) return GDN_ERR_INVALID_ARG;
+    if (!(eps >= 0.f && eps <= FLT_MAX)) return GDN_ERR_INVALID_ARG;
+    for (const void *p : {static_cast<const void *>(conv_w), state_in,
+                          static_cast<const void *>(state_out)})
+        if (!aligned(p, 16)) return GDN_ERR_INVALID_ARG;
+    const int64_t rows = cu_seqlens ? T : N * T;
+    const int64_t gb = rows * H * 4, fifo = N * 3 * H * 3 * gdn::kHeadDim * 2,
+                  wb = 3 * H * gdn::kHeadDim * 4 * 4,
+                  sb = N * H * gdn::kHeadDim * gdn::kHeadDim * 4;
+    const Range rxq = span_of(xq, tok_bytes), rxk = span_of(xk, tok_bytes),
+                rxv = span_of(xv, tok_bytes), ra = span_of(a, gb), rb = span_of(b, gb),
+                rw = span_of(conv_w, wb), rsi = span_of(state_in, fifo),
+                rso = span_of(state_out, fifo), rO = span_of(O, tok_bytes),
+                rST = span_of(S_T, sb), rS0 = S0 ? span_of(S0, sb) : Range{0, 0};
+    // the FIFO out is exactly the FIFO in, or apart from every other buffer
+    for (Range r : {rxq, rxk, rxv, ra, rb, rw, rO, rST, rS0})
+        if (overlap(rso, r)) return GDN_ERR_ALIAS;
+    if (overlap(rso, rsi) && rso.lo != rsi.lo) return GDN_ERR_ALIAS;
+    // the outputs O and S_T are apart from the weights and the FIFO in
+    for (Range r : {rw, rsi})
+        if (overlap(rO, r) || overlap(rST, r)) return GDN_ERR_ALIAS;
+    if (N == 0) return GDN_OK;
+    if (const int sc = check_seqlens_debug(cu_seqlens, N, T, stream)) return sc;
+    pa.conv_w = conv_w;
+    pa.fifo = state_in;
+    pa.ceps = eps;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (gdn::launch_prefill_mfma(pa, s) != hipSuccess) return GDN_ERR_HIP;
+    // the FIFO update after the prompt kernel, which read state_in
+    gdn::PreopArgs p{xq, xk, xv, a, b, conv_w, state_in, state_out, cu_seqlens, N, T, rows, H,
+                     eps, true, nullptr, nullptr, nullptr, nullptr, nullptr};
+    return gdn::launch_preop_state(p, s) == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
 namespace {
 int decode_step(const void *q, const void *k, const void *v, int io_dtype, const float *g,
                 const float *beta, float *S, int64_t B, int64_t H, int64_t dk, int64_t dv,

@@ -42,6 +42,13 @@ struct PrefillArgs {
     // Whether a batch of short sequences may take the 16-token kernel (off
     // when the caller names the matrix-core kernel's inverse method).
     bool short_ok = true;
+    // The pre-operations fused into the 64-token kernel's chunk load (non-null
+    // conv_w): q, k, v, g, beta are then the raw projections xq, xk, xv and the
+    // gate inputs a, b; fifo is the conv FIFO state [N, 3, H, 3, 128] (bf16)
+    // read for the rows before each sequence, and ceps the norm's eps.
+    const float *conv_w = nullptr;
+    const void *fifo = nullptr;
+    float ceps = 0.f;
 };
 
 struct DecodeArgs {
@@ -102,6 +109,9 @@ hipError_t launch_segment_scan(const float *M, const float *B, const float *S0, 
 hipError_t launch_segment_gather(const float *Sout, const float *S0, const int32_t *seg,
                                  float *S_T, int64_t N, int64_t H, hipStream_t stream);
 hipError_t launch_preop(const PreopArgs &p, hipStream_t stream);
+// The FIFO update of a pre-operation call alone (state_out from state_in and
+// the raw rows), after every read of state_in on the same stream.
+hipError_t launch_preop_state(const PreopArgs &p, hipStream_t stream);
 hipError_t launch_prefill_valu(const PrefillArgs &a, hipStream_t stream);
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream);
 bool prefill_mfma_supports(const PrefillArgs &a);

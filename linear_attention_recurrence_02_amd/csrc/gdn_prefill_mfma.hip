@@ -64,7 +64,15 @@
 // step (the gate rows fetched into LDS a period ahead; the consumer waves
 // exchange per-row sums through LDS); kDoubling picks the T_ii method; kRank
 // walks a packed batch longest first (each workgroup ranks the sequence
-// lengths before the roles split, one barrier that both roles execute).
+// lengths before the roles split, one barrier that both roles execute);
+// kPreop runs the block's pre-operations (causal conv over the FIFO window,
+// silu, L2 norm of q and k, g = -softplus(a), beta = sigmoid(b); the
+// Qwen3.5-4B -- Hexagon NPU (QHexRT) -- v81 page's text decoder description
+// and the QCS6490 page's port notes) in the producers' staging step, from the
+// raw projections: each producer lane holds two channels of its block's rows
+// and of the three rows before them, so the conv window stays in the lane; K's
+// pre-operations run in phase 2 after the inverse chain, q's and v's in
+// phase 3 beside the consumers' W/U step.
 // Precision.  The state, the accumulators, U and the per-token scalars are
 // fp32.  K and Q enter the products as fp16 copies of the bf16 inputs, V as
 // the bf16 input itself (in bf16 products against P').  Correlated keys (the
@@ -179,10 +187,48 @@ __device__ __forceinline__ void store_rows_q(f16 *tile, const f32x4 *x, int r, i
     }
 }
 
+// A DPP move within rows of 16 lanes (every lane has a source for the
+// controls used here).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+
+// Sums over the 64 lanes of a wave of 16 values per lane (x[r] for block row
+// r), by halving exchanges: at each step a lane keeps the rows of one half,
+// adds its partner's values of those rows and hands over the other half in
+// exchange.  Lane bits 5, 4, 3 and 2 pick the halves (partners l ^ 32, l ^ 16,
+// l ^ 8, then l ^ 7 within each eight lanes), and the last two steps add the
+// four lanes of a quad, so lane l returns the sum of row
+// 8 (l >> 5 & 1) + 4 (l >> 4 & 1) + 2 (l >> 3 & 1) + (l >> 2 & 1).
+__device__ __forceinline__ float rows16_wave_sum(const float *x, int l) {
+    const bool b5 = (l >> 5) & 1, b4 = (l >> 4) & 1, b3 = (l >> 3) & 1, b2 = (l >> 2) & 1;
+    float y[8], z[4], w[2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        y[i] = (b5 ? x[i + 8] : x[i]) + __shfl_xor(b5 ? x[i] : x[i + 8], 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        z[i] = (b4 ? y[i + 4] : y[i]) + __shfl_xor(b4 ? y[i] : y[i + 4], 16);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        w[i] = (b3 ? z[i + 2] : z[i]) + dpp_mov<0x128>(b3 ? z[i] : z[i + 2]);   // row_ror:8
+    float t = (b2 ? w[1] : w[0]) + dpp_mov<0x141>(b2 ? w[0] : w[1]);         // row_half_mirror
+    t += dpp_mov<0xb1>(t);                                                    // quad_perm [1,0,3,2]
+    t += dpp_mov<0x4e>(t);                                                    // quad_perm [2,3,0,1]
+    return t;
+}
+
 struct Unit {
     const bf16 *q, *k, *v;
     const float *g, *beta;
     int64_t start, len, H, h;
+    // fused pre-operations: q, k, v, g, beta are then the raw projections and
+    // gate inputs; the conv FIFO state of the sequence and the conv weights
+    const bf16 *fifo;
+    const float *conv_w;
+    int64_t seq;
+    float ceps;
     __device__ int rows_in(int pc) const {
         const int64_t rem = len - int64_t(pc) * C;
         return static_cast<int>(rem < 0 ? 0 : (rem < C ? rem : C));
@@ -232,24 +278,172 @@ struct Producer {
             hV[s] = pV[s];
             hQ[s] = pQ[s];
         }
-        if (p == 0) {
-            const bool okl = l < nv;
-            sbt = okl ? pb : 0.f;
-            sg2 = wave_prefix_sum(okl ? pg : 0.f) * kLog2e;
-            const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sg2), 63));
-            seg = __builtin_amdgcn_exp2f(sg2);
-            sec = __builtin_amdgcn_exp2f(last - sg2);
+        if (p == 0) scan(nv, l);
+    }
+    // The per-token scalars of the staged chunk from g and beta (wave p = 0,
+    // lane l = token l; rows past nv take g = 0, beta = 0).
+    __device__ void scan(int nv, int l) {
+        const bool okl = l < nv;
+        sbt = okl ? pb : 0.f;
+        sg2 = wave_prefix_sum(okl ? pg : 0.f) * kLog2e;
+        const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sg2), 63));
+        seg = __builtin_amdgcn_exp2f(sg2);
+        sec = __builtin_amdgcn_exp2f(last - sg2);
+    }
+
+    // ---- staging with the pre-operations fused in (kPreop) ----
+    // Producer wave p holds, in lane l, channels 2l and 2l+1 of the chunk rows
+    // 16p-3 .. 16p+15 of each stream: its block's 16 rows and the three
+    // before them, which the causal conv of its first rows reads.  The window
+    // then lies within the lane, and each 4-byte load of a wave covers one
+    // whole 256-byte token row.  Rows before the sequence's first token come
+    // from its FIFO state; rows past its end read its first row (their
+    // outputs are zeroed).
+    uint32_t raw[3][19];          // bf16 pairs, streams q, k, v
+    uint32_t xQ[16], xV[16];      // the block's q (fp16 pairs) and v (bf16 pairs)
+    float cw[3][2][4];            // conv weights of channels 2l, 2l+1, taps oldest first
+
+    __device__ void load_weights(const Unit &u, int l) {
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+            const float *wp = u.conv_w + ((s * u.H + u.h) * D + 2 * l) * 4;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const f32x4 t = *reinterpret_cast<const f32x4 *>(wp + 4 * c);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) cw[s][c][j] = t[j];
+            }
         }
     }
-    __device__ void store_v(Smem &sm, int p, int r16, int q) { store_rows_kv(sm.V, hV, 16 * p + r16, q); }
-    __device__ void store_q(Smem &sm, int nb, int p, int l, int r16, int q) {
-        store_rows_q(sm.Q[nb], hQ, 16 * p + r16, q);
+    // Prefetch of stream s (0 q, 1 k, 2 v) of chunk pc, and of the raw gate
+    // inputs a, b of token l.
+    __device__ void prefetch_pre(const Unit &u, int pc, int p, int l, int s) {
+        const int64_t base = int64_t(pc) * C + 16 * p - 3;   // sequence row of raw[s][0]
+        const int64_t HD = u.H * D;
+        const uint32_t lo = static_cast<uint32_t>(u.h * D + 2 * l);
+        const bf16 *x = s == 0 ? u.q : (s == 1 ? u.k : u.v);
+        // the three window rows before the block: FIFO rows at a sequence start
+        const bf16 *fifo = u.fifo + ((u.seq * 3 + s) * u.H + u.h) * 3 * D + 2 * l;
+#pragma unroll
+        for (int j = 0; j < 19; ++j) {
+            const int64_t r = base + j;
+            const bf16 *ptr;
+            if (j < 3 && r < 0)
+                ptr = fifo + (3 + r) * D;
+            else
+                ptr = x + (u.start + (r < u.len ? r : 0)) * HD + lo;
+            raw[s][j] = *reinterpret_cast<const uint32_t *>(ptr);
+        }
+    }
+    __device__ void prefetch_gates(const Unit &u, int pc, int l) {
+        const int nv = u.rows_in(pc);
+        const int64_t gi = (l < nv ? u.row0(pc) + l : u.start) * u.H + u.h;
+        pg = u.g[gi];       // raw gate inputs a and b
+        pb = u.beta[gi];
+    }
+    __device__ void prefetch_pre(const Unit &u, int pc, int p, int l) {
+#pragma unroll
+        for (int s = 0; s < 3; ++s) prefetch_pre(u, pc, p, l, s);
+        prefetch_gates(u, pc, l);
+    }
+    // conv, silu and (for q and k) the row's L2 norm of the stream s rows held
+    // in raw[s]; y[r] holds channels 2l, 2l+1 of block row r.
+    __device__ void conv_rows(int s, float ceps, float (*y)[2], int l) {
+        float x[19][2];
+#pragma unroll
+        for (int j = 0; j < 19; ++j) {
+            x[j][0] = __uint_as_float(raw[s][j] << 16);
+            x[j][1] = __uint_as_float(raw[s][j] & 0xffff0000u);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float u = cw[s][c][0] * x[r][c] + cw[s][c][1] * x[r + 1][c] +
+                                cw[s][c][2] * x[r + 2][c] + cw[s][c][3] * x[r + 3][c];
+                y[r][c] = u * __builtin_amdgcn_rcpf(1.f + __expf(-u));
+            }
+        if (s < 2) {
+            float ss[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ss[r] = y[r][0] * y[r][0] + y[r][1] * y[r][1];
+            // lane 32 (r >> 3) + 16 ((r >> 2) & 1) + 8 ((r >> 1) & 1) + 4 (r & 1)
+            // ends with row r's sum
+            const float inv = rsqrtf(rows16_wave_sum(ss, l) + ceps);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int src = 32 * (r >> 3) + 16 * ((r >> 2) & 1) + 8 * ((r >> 1) & 1) + 4 * (r & 1);
+                const float f = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, inv), src));
+                y[r][0] *= f;
+                y[r][1] *= f;
+            }
+        }
+    }
+    // The pre-operations on the prefetched rows of a chunk with nv rows:
+    // convert_pre_k stores K (fp16) in buffer set nb; convert_pre_qv keeps Q
+    // (fp16) and V (bf16) for their stores, and wave p = 0 turns the raw gate
+    // inputs into g = -softplus(a), beta = sigmoid(b) and scans them.  Rows
+    // past nv are zero.
+    __device__ void convert_pre_k(Smem &sm, int nb, int nv, int p, int l, float ceps) {
+        typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        float y[16][2];
+        auto live = [&](int r) { return nv >= C || 16 * p + r < nv; };
+        conv_rows(1, ceps, y, l);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = 16 * p + r;
+            const f16x2 h = live(r) ? __builtin_convertvector(f32x2{y[r][0], y[r][1]}, f16x2) : f16x2{0, 0};
+            *reinterpret_cast<f16x2 *>(&sm.K[nb][t * KS + ((2 * l) ^ ksw(t))]) = h;
+        }
+    }
+    __device__ void convert_pre_qv(int nv, int p, int l, float ceps) {
+        typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+        typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        typedef float f32x2 __attribute__((ext_vector_type(2)));
+        float y[16][2];
+        auto live = [&](int r) { return nv >= C || 16 * p + r < nv; };
+        conv_rows(0, ceps, y, l);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            xQ[r] = live(r) ? __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y[r][0], y[r][1]}, f16x2)) : 0u;
+        conv_rows(2, ceps, y, l);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            xV[r] = live(r) ? __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{y[r][0], y[r][1]}, bf16x2)) : 0u;
+        if (p == 0) {
+            // softplus(a) = max(a, 0) + log1p(exp(-|a|)), without overflow
+            pg = -(fmaxf(pg, 0.f) + log1pf(__expf(-fabsf(pg))));
+            pb = 1.f / (1.f + __expf(-pb));
+            scan(nv, l);
+        }
+    }
+    __device__ void store_v_pre(Smem &sm, int p, int l) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int t = 16 * p + r;
+            *reinterpret_cast<uint32_t *>(&sm.V[t * KS + ((2 * l) ^ ksw(t))]) = xV[r];
+        }
+    }
+    __device__ void store_q_pre(Smem &sm, int nb, int p, int l) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            *reinterpret_cast<uint32_t *>(&sm.Q[nb][(16 * p + r) * QS + 2 * l]) = xQ[r];
+        store_scalars(sm, nb, p, l);
+    }
+    __device__ void store_scalars(Smem &sm, int nb, int p, int l) {
         if (p == 0) {
             sm.G2[nb][l] = sg2;
             sm.EG[nb][l] = seg;
             sm.EC[nb][l] = sec;
             sm.Bt[nb][l] = sbt;
         }
+    }
+
+    __device__ void store_v(Smem &sm, int p, int r16, int q) { store_rows_kv(sm.V, hV, 16 * p + r16, q); }
+    __device__ void store_q(Smem &sm, int nb, int p, int l, int r16, int q) {
+        store_rows_q(sm.Q[nb], hQ, 16 * p + r16, q);
+        store_scalars(sm, nb, p, l);
     }
 
     // Phase 1 for the chunk in buffer set nb: the Gram tiles of row block P of
@@ -591,13 +785,14 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q,
     }
 }
 
-template <bool kGated, bool kDoubling, bool kRank, typename OutT>
+template <bool kGated, bool kDoubling, bool kRank, typename OutT, bool kPreop = false>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t N, int64_t T,
     int64_t H, OutT *__restrict__ O, float *__restrict__ S_T, const bf16 *__restrict__ z,
-    const float *__restrict__ norm_w, float eps) {
+    const float *__restrict__ norm_w, float eps, const float *__restrict__ conv_w,
+    const bf16 *__restrict__ fifo, float ceps) {
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
@@ -622,6 +817,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     u.q = q; u.k = k; u.v = v; u.g = g; u.beta = beta;
     u.H = H;
     u.h = unit % H;
+    u.fifo = fifo;
+    u.conv_w = conv_w;
+    u.seq = seq;
+    u.ceps = ceps;
     sequence_span(cu_seqlens, seq, T, u.start, u.len);
     const int nch = static_cast<int>((u.len + C - 1) / C);
 
@@ -634,16 +833,28 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             *reinterpret_cast<f32x4 *>(&sm.A[1][i]) = zero4();
         }
         Producer pr;
-        pr.prefetch(u, 0, w, l, r16, qd);
-        pr.convert(sm, 0, u.rows_in(0), w, l, r16, qd);
-        pr.store_q(sm, 0, w, l, r16, qd);
-        pr.prefetch(u, 1, w, l, r16, qd);
+        if constexpr (kPreop) {
+            pr.load_weights(u, l);
+            pr.prefetch_pre(u, 0, w, l);
+            pr.convert_pre_k(sm, 0, u.rows_in(0), w, l, u.ceps);
+            pr.convert_pre_qv(u.rows_in(0), w, l, u.ceps);
+            pr.store_q_pre(sm, 0, w, l);
+            pr.prefetch_pre(u, 1, w, l);
+        } else {
+            pr.prefetch(u, 0, w, l, r16, qd);
+            pr.convert(sm, 0, u.rows_in(0), w, l, r16, qd);
+            pr.store_q(sm, 0, w, l, r16, qd);
+            pr.prefetch(u, 1, w, l, r16, qd);
+        }
         __syncthreads();
         // Period c (c = -1 .. nch-1) prepares chunk c+1 and stages chunk c+2;
         // the last period's work is on empty chunks and is never read.
         for (int c = -1; c < nch; ++c) {
             const int nb = (c + 1) & 1;
-            pr.store_v(sm, w, r16, qd);                // V of chunk c+1
+            if constexpr (kPreop)                      // V of chunk c+1
+                pr.store_v_pre(sm, w, l);
+            else
+                pr.store_v(sm, w, r16, qd);
             switch (w) {
             case 0: pr.gram<0>(sm, nb, r16, qd); break;
             case 1: pr.gram<1>(sm, nb, r16, qd); break;
@@ -664,8 +875,13 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             default: pr.solve<3, kDoubling>(sm, nb, r16, qd); break;
             }
             // K of chunk c+2 goes to the buffer nobody reads in phases 2 and 3
-            pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
-            pr.prefetch(u, c + 3, w, l, r16, qd);
+            if constexpr (kPreop) {
+                pr.convert_pre_k(sm, nb ^ 1, u.rows_in(c + 2), w, l, u.ceps);
+                pr.prefetch_pre(u, c + 3, w, l, 1);
+            } else {
+                pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
+                pr.prefetch(u, c + 3, w, l, r16, qd);
+            }
             if constexpr (!kGated) __builtin_amdgcn_s_setprio(0);
             __syncthreads();
             switch (w) {
@@ -674,7 +890,19 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             case 2: pr.store_a<2>(sm, r16, qd); break;
             default: pr.store_a<3>(sm, r16, qd); break;
             }
-            pr.store_q(sm, nb ^ 1, w, l, r16, qd);
+            if constexpr (kPreop) {
+                // the pre-operations of chunk c+2's q and v beside the
+                // consumers' W/U step, at a raised priority: Q goes to the
+                // buffer nobody reads in phase 3, V waits for phase 1
+                __builtin_amdgcn_s_setprio(1);
+                pr.convert_pre_qv(u.rows_in(c + 2), w, l, u.ceps);
+                pr.store_q_pre(sm, nb ^ 1, w, l);
+                pr.prefetch_pre(u, c + 3, w, l, 0);
+                pr.prefetch_pre(u, c + 3, w, l, 2);
+                pr.prefetch_gates(u, c + 3, l);
+                __builtin_amdgcn_s_setprio(0);
+            } else
+                pr.store_q(sm, nb ^ 1, w, l, r16, qd);
             __syncthreads();
         }
         return;
@@ -1001,13 +1229,15 @@ bool rank_longest_first_pays(const PrefillArgs &a) {
 template <typename OutT>
 void launch_typed(void (*kern)(const bf16 *, const bf16 *, const bf16 *, const float *, const float *,
                                const float *, const int32_t *, int64_t, int64_t, int64_t, OutT *,
-                               float *, const bf16 *, const float *, float),
+                               float *, const bf16 *, const float *, float, const float *,
+                               const bf16 *, float),
                   const PrefillArgs &a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(512);
     kern<<<grid, block, 0, stream>>>(
         static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
         static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.N, a.T, a.H,
-        static_cast<OutT *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps);
+        static_cast<OutT *>(a.O), a.S_T, static_cast<const bf16 *>(a.z), a.norm_w, a.eps,
+        a.conv_w, static_cast<const bf16 *>(a.fifo), a.ceps);
 }
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
@@ -1015,7 +1245,10 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     // (the longest-first order is compiled into the default form only; the
     // gated norm and the fp32 O are offered in the two inverse methods)
     const bool dbl = a.inverse == kInverseDoubling || (a.inverse == kInverseDefault && kDefaultDoubling);
-    if (a.out_f32)
+    if (a.conv_w)   // the pre-operations fused into the chunk load
+        launch_typed<bf16>(rank ? prefill_mfma_kernel<false, kDefaultDoubling, true, bf16, true>
+                                : prefill_mfma_kernel<false, kDefaultDoubling, false, bf16, true>, a, stream);
+    else if (a.out_f32)
         launch_typed<float>(dbl ? prefill_mfma_kernel<false, true, false, float>
                                 : prefill_mfma_kernel<false, false, false, float>, a, stream);
     else if (a.z)

@@ -280,6 +280,15 @@ __global__ __launch_bounds__(128) void preop_state_kernel(
 }
 
 template <typename IO>
+hipError_t launch_state(const PreopArgs &p, hipStream_t stream) {
+    const dim3 sgrid(static_cast<unsigned>(p.N), 3, static_cast<unsigned>(p.H));
+    preop_state_kernel<IO><<<sgrid, kHeadDim, 0, stream>>>(
+        static_cast<const IO *>(p.xq), static_cast<const IO *>(p.xk), static_cast<const IO *>(p.xv),
+        static_cast<const IO *>(p.state_in), p.cu_seqlens, p.T, p.H, static_cast<IO *>(p.state_out));
+    return hipGetLastError();
+}
+
+template <typename IO>
 hipError_t launch_typed(const PreopArgs &p, hipStream_t stream) {
     const int64_t rows = p.rows;
     if (rows > 0) {
@@ -295,17 +304,17 @@ hipError_t launch_typed(const PreopArgs &p, hipStream_t stream) {
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const dim3 sgrid(static_cast<unsigned>(p.N), 3, static_cast<unsigned>(p.H));
-    preop_state_kernel<IO><<<sgrid, kHeadDim, 0, stream>>>(
-        static_cast<const IO *>(p.xq), static_cast<const IO *>(p.xk), static_cast<const IO *>(p.xv),
-        static_cast<const IO *>(p.state_in), p.cu_seqlens, p.T, p.H, static_cast<IO *>(p.state_out));
-    return hipGetLastError();
+    return launch_state<IO>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_preop(const PreopArgs &p, hipStream_t stream) {
     return p.bf16 ? launch_typed<__hip_bfloat16>(p, stream) : launch_typed<float>(p, stream);
+}
+
+hipError_t launch_preop_state(const PreopArgs &p, hipStream_t stream) {
+    return p.bf16 ? launch_state<__hip_bfloat16>(p, stream) : launch_state<float>(p, stream);
 }
 
 }  // namespace gdn

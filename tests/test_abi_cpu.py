@@ -256,6 +256,43 @@ def test_preop_validation(lib):
                  so=None, q=None, k=None, v=None, g=None, beta=None) == binding.GDN_OK
 
 
+def test_prefill_preop_validation(lib):
+    def pp(**kw):
+        a = dict(xq=A, xk=A + 8 * MB, xv=A + 16 * MB, dtype=1, a=A + 24 * MB, b=A + 25 * MB,
+                 w=A + 26 * MB, si=A + 27 * MB, so=A + 27 * MB, eps=1e-6, S0=A + 28 * MB,
+                 cu=None, N=2, T=64, H=2, dk=128, dv=128, K=4, chunk=64, O=A + 32 * MB,
+                 S_T=A + 40 * MB)
+        a.update(kw)
+        return lib.gdn_chunk_prefill_preop(a["xq"], a["xk"], a["xv"], a["dtype"], a["a"],
+                                           a["b"], a["w"], a["si"], a["so"], a["eps"], a["S0"],
+                                           a["cu"], a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                           a["K"], a["chunk"], a["O"], a["S_T"], None)
+    assert pp(xq=None) == binding.GDN_ERR_INVALID_ARG
+    assert pp(w=None) == binding.GDN_ERR_INVALID_ARG
+    assert pp(si=None) == binding.GDN_ERR_INVALID_ARG
+    assert pp(S_T=None) == binding.GDN_ERR_INVALID_ARG
+    assert pp(dtype=0) == binding.GDN_ERR_UNSUPPORTED                   # fp32: bf16 only
+    assert pp(dtype=2) == binding.GDN_ERR_UNSUPPORTED                   # no fp32 O here
+    assert pp(chunk=32) == binding.GDN_ERR_UNSUPPORTED
+    assert pp(K=3) == binding.GDN_ERR_UNSUPPORTED
+    assert pp(dk=64) == binding.GDN_ERR_UNSUPPORTED
+    assert pp(eps=-1.0) == binding.GDN_ERR_INVALID_ARG
+    assert pp(eps=float("nan")) == binding.GDN_ERR_INVALID_ARG
+    assert pp(w=A + 26 * MB + 4) == binding.GDN_ERR_INVALID_ARG         # misaligned
+    assert pp(si=A + 27 * MB + 8, so=A + 27 * MB + 8) == binding.GDN_ERR_INVALID_ARG
+    # 2 x 64 rows x 2 heads x 256 B = 64 KiB per token tensor
+    assert pp(O=A + 4096) == binding.GDN_ERR_ALIAS                      # O over xq
+    assert pp(O=A + 26 * MB) == binding.GDN_ERR_ALIAS                   # O over conv_w
+    assert pp(S_T=A + 27 * MB) == binding.GDN_ERR_ALIAS                 # S_T over the FIFO
+    assert pp(so=A + 27 * MB + 256) == binding.GDN_ERR_ALIAS            # FIFO partly in place
+    assert pp(so=A + 24 * MB) == binding.GDN_ERR_ALIAS                  # new FIFO over a
+    assert pp(so=A + 40 * MB) == binding.GDN_ERR_ALIAS                  # new FIFO over S_T
+    assert pp(N=0) == binding.GDN_OK
+    assert pp(N=0, so=A + 29 * MB) == binding.GDN_OK                    # out of place
+    assert pp(N=0, T=0, xq=None, xk=None, xv=None, a=None, b=None, w=None, si=None,
+              so=None, O=None) == binding.GDN_OK
+
+
 def test_decode_rejects_bad_calls(lib):
     assert decode(lib, S=None) == binding.GDN_ERR_INVALID_ARG
     assert decode(lib, B=-1) == binding.GDN_ERR_INVALID_ARG
