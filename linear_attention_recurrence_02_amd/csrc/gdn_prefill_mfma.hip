@@ -48,16 +48,16 @@
 //   Each chunk period has three barrier-separated phases:
 //     1: consumers D, state update (chunk c)  | producers Gram tiles (c+1),
 //                                            |   store V (c+1)
-//     2: consumers O (chunk c)               | producers T_ii, P_i, M_ij (c+1);
-//                                            |   convert c+2, store its K;
-//                                            |   prefetch c+3
-//     3: consumers W, U (chunk c+1)          | producers store A (c+1), Q and
-//                                            |   scalars (c+2)
+//     2: consumers O (chunk c)               | producers T_ii, P_i, M_ij (c+1)
+//     3: consumers W, U (chunk c+1)          | producers store A (c+1); convert
+//                                            |   c+2, store its K, Q and
+//                                            |   scalars; prefetch c+3
 //   Each array is written in a phase in which nobody reads it: K, Q and the
 //   per-token scalars are double-buffered, everything else is single.
 //   The two roles run as two separate loops under a wave-uniform branch and
-//   execute the same number of barriers (1 + 3 (nch + 1)).  Phase 2 is the
-//   producers' critical phase, so they take wave priority in it.
+//   execute the same number of barriers (1 + 3 (nch + 1)).  The consumers'
+//   work sets phases 1 to 3 of the plain form; with the pre-operations fused
+//   in, the producers set phases 2 and 3 and take wave priority in them.
 // A null v stands for zero values and a null O for no output rows (the
 // segmented form's state-map runs).
 // Template variants: kGated fuses the block's gated RMS norm into the output
@@ -238,11 +238,10 @@ struct Unit {
 
 // Producer wave p = 4..7 - 4 (lane r16 + 16 q).  Rows 16p + r16 of chunk c+2
 // (and token l's g and beta) are loaded into pK, pV, pQ (pg, pb) a period
-// ahead; in phase 2 of period c they are converted to fp16 and K is stored;
-// Q and the per-token scalars wait in hQ (sg2, ...) for phase 3, after the
-// consumers' output step has read the previous ones, and V waits in hV for
-// phase 1 of the next period, after the consumers' W/U step has read the
-// previous V.
+// ahead; in phase 3 of period c they are converted to fp16 and K, Q and the
+// per-token scalars are stored (the consumers' W/U step reads neither buffer),
+// while V waits in hV for phase 1 of the next period, after the consumers'
+// W/U step has read the previous V.
 struct Producer {
     f32x4 pK[4], pV[4], pQ[4];
     f32x4 hV[4], hQ[4];
@@ -862,12 +861,17 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             default: pr.gram<3>(sm, nb, r16, qd); break;
             }
             __syncthreads();
-            // Phase 2 is the producers' critical phase, while the consumers'
-            // output step there has slack: the producers take precedence on
-            // their SIMDs (matrix core and vector ALU) until it ends.  Not
-            // with the gated norm, whose consumers norm and store the rows in
-            // this phase.
-            if constexpr (!kGated) __builtin_amdgcn_s_setprio(2);
+            // Phase 2's longest work: with the pre-operations the producers'
+            // (the inverse chain, then K's conv), which take precedence on
+            // their SIMDs (matrix core and vector ALU) until it ends; in the
+            // plain form the consumers' output step and the producer of block
+            // 3 (its inverse chain and the three M_3j), which alone raises its
+            // priority.
+            if constexpr (kPreop) {
+                __builtin_amdgcn_s_setprio(2);
+            } else if constexpr (!kGated) {
+                if (w == 3) __builtin_amdgcn_s_setprio(1);
+            }
             switch (w) {
             case 0: pr.solve<0, kDoubling>(sm, nb, r16, qd); break;
             case 1: pr.solve<1, kDoubling>(sm, nb, r16, qd); break;
@@ -878,9 +882,6 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             if constexpr (kPreop) {
                 pr.convert_pre_k(sm, nb ^ 1, u.rows_in(c + 2), w, l, u.ceps);
                 pr.prefetch_pre(u, c + 3, w, l, 1);
-            } else {
-                pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
-                pr.prefetch(u, c + 3, w, l, r16, qd);
             }
             if constexpr (!kGated) __builtin_amdgcn_s_setprio(0);
             __syncthreads();
@@ -901,8 +902,14 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 pr.prefetch_pre(u, c + 3, w, l, 2);
                 pr.prefetch_gates(u, c + 3, l);
                 __builtin_amdgcn_s_setprio(0);
-            } else
+            } else {
+                // the rows of chunk c+2 converted beside the consumers' W/U
+                // step, this phase's longer work: K and Q go to the buffers
+                // nobody reads in phase 3, V waits for phase 1
+                pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
                 pr.store_q(sm, nb ^ 1, w, l, r16, qd);
+                pr.prefetch(u, c + 3, w, l, r16, qd);
+            }
             __syncthreads();
         }
         return;
