@@ -679,6 +679,8 @@ def main():
             f"{r['roofline']['achieved']:.0f} GB/s, HBM {100*r['hbm_frac']:.1f}%")
         pre[r["workload"]] = r
         r = bench_prefill_preop(torch, gdn, p, args.prefill_iters)
+        r["roofline"]["traffic"] = read_traffic(
+            "prefill_preop_large", source_digest("gdn_prefill_mfma.hip", "gdn_mfma.hpp"))
         log(f"prompt form from the projections {r['workload']}: {r['seconds']*1e3:.3f} ms fused, "
             f"{r['two_call_seconds']*1e3:.3f} ms as two calls")
         pre[r["workload"]] = r
