@@ -180,6 +180,18 @@ __device__ __forceinline__ int choose_scale(float mscaled, int cur, float mtrue)
     return min(max(3 - e, -kMaxScaleExp), kMaxScaleExp);
 }
 
+// Lower bound on each token's log-decay g before the in-chunk prefix sums.
+// exp(-64) ~ 1.6e-28 is below anything an fp32 result resolves, so the bound
+// changes no result, while it keeps the prefix sums of a chunk small (|G| <=
+// 64 per token): the decay factor between two tokens is exp of a difference
+// of prefix sums, and after a token that clears the state (g of -1e4, say)
+// unbounded sums would carry that difference with an error of ~1e-3.
+constexpr float kMinLogDecay = -64.f;
+__device__ __forceinline__ float bounded_log_decay(float g) { return __builtin_fmaxf(g, kMinLogDecay); }
+// log2(e) x, rounded once and kept out of any later fused multiply-add, so
+// that exp2(G_last - G_t) is exactly 1 for the last row.
+__device__ __forceinline__ float log2e_times(float x) { return __fmul_rn(x, 1.4426950408889634f); }
+
 // Inclusive prefix sum within each row of 16 lanes.
 __device__ __forceinline__ float row16_prefix_sum(float x) {
     x = dpp_add<0x111, 0xf>(x);   // row_shr:1

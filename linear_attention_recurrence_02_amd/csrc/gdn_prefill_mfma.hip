@@ -103,7 +103,6 @@ constexpr int WS = C + 16;        // fp16 row stride of W (dk-major)
 constexpr int AS = C + 4;         // fp16 row stride of A (token-major)
 constexpr int BS = 16 + 8;        // fp16 row stride of the 16 x 16 blocks T_ii, P_i, P'_i, M_ij
 constexpr int NS = 20;            // fp32 row stride of the diagonal blocks of N
-constexpr float kLog2e = 1.4426950408889634f;
 // How the diagonal blocks of (I + N)^-1 are formed unless the caller names a
 // method: block doubling on the matrix cores (true) or fp32 back substitution.
 constexpr bool kDefaultDoubling = true;
@@ -284,7 +283,7 @@ struct Producer {
     __device__ void scan(int nv, int l) {
         const bool okl = l < nv;
         sbt = okl ? pb : 0.f;
-        sg2 = wave_prefix_sum(okl ? pg : 0.f) * kLog2e;
+        sg2 = log2e_times(wave_prefix_sum(okl ? bounded_log_decay(pg) : 0.f));
         const float last = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, sg2), 63));
         seg = __builtin_amdgcn_exp2f(sg2);
         sec = __builtin_amdgcn_exp2f(last - sg2);

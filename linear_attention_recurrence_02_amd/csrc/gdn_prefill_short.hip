@@ -57,7 +57,6 @@ constexpr int D = kHeadDim;       // 128
 constexpr int RS = D + 8;         // fp16 row stride of the token-major K, Q, V, W tiles
 constexpr int TS = CS + 4;        // fp16 row stride of the 16 x 16 tiles A, P, P'
 constexpr int NS = CS + 4;        // fp32 row stride of N (16-byte aligned rows)
-constexpr float kLog2e = 1.4426950408889634f;
 
 struct __attribute__((aligned(16))) ShortSmem {
     f16 K[CS * RS];
@@ -162,7 +161,7 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
         if (w == 0) {
             const bool ok = r16 < nv;
             bt = ok ? xb : 0.f;
-            const float g2 = row16_prefix_sum(ok ? xg : 0.f) * kLog2e;
+            const float g2 = log2e_times(row16_prefix_sum(ok ? bounded_log_decay(xg) : 0.f));
             const float last = __builtin_bit_cast(
                 float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, g2), CS - 1));
             eg = __builtin_amdgcn_exp2f(g2);

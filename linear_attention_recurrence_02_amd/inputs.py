@@ -225,7 +225,7 @@ def preop_inputs(B: int, T: int, H: int, *, lengths=None, io_dtype=torch.bfloat1
 # the recurrence (no write, a full read-back, full decay), at any size.
 
 KEYS = ("iid", "corr", "exact")
-DECAYS = ("normal", "slow", "none", "full")
+DECAYS = ("normal", "slow", "none", "full", "reset")
 WRITES = ("sigmoid", "one", "zero")
 
 
@@ -243,7 +243,9 @@ def edge_workload(B: int, T: int, H: int, *, keys: str = "iid", sigma: float = 0
       "exact" draws keys whose norm is exactly 1 in bf16: +-1/8 on 64 of the
       128 coordinates (random signs and coordinates), zero elsewhere.
     decay: "normal" g = -softplus(x), "slow" 0.02 times that, "none" g = 0,
-      "full" g = -1e4 (exp(g) underflows to zero in fp32).
+      "full" g = -1e4 (exp(g) underflows to zero in fp32), "reset" the normal
+      draws with g = -1e4 at every 97th token (a token that clears the state,
+      at varying positions within 64- and 16-token chunks).
     write: "sigmoid" beta = sigmoid(x), "one" beta = 1, "zero" beta = 0.
     value_scale: v and S0 are multiplied by it (the page's small heads have an
       output RMS of 1e-3..2e-2).
@@ -288,6 +290,8 @@ def edge_workload(B: int, T: int, H: int, *, keys: str = "iid", sigma: float = 0
         g = torch.zeros_like(g)
     elif decay == "full":
         g = torch.full_like(g, -1e4)
+    elif decay == "reset":
+        g[:, 96::97] = -1e4
     beta = torch.sigmoid(rn(*lead))
     if write == "one":
         beta = torch.ones_like(beta)

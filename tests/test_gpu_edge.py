@@ -12,7 +12,9 @@ outputs are orders of magnitude smaller than others.  Every path is run on:
   * the recurrence's special cases: no write (beta = 0: pure decay), the
     read-back of a projection (g = 0, beta = 1, q = k: o_t = v_t, with keys of
     norm exactly 1 in bf16) and full
-    decay (exp(g) = 0: o_t = beta_t (q_t . k_t) v_t).
+    decay (exp(g) = 0: o_t = beta_t (q_t . k_t) v_t);
+  * tokens that clear the state (g = -1e4) among normal decays, at varying
+    positions within the chunks.
 A packed batch of 512 and 384 tokens (several chunks, a ragged tail) with
 4 heads and a nonzero initial state.  The bar is the one of every other
 parity test: per (sequence, head) slice, 2e-3 of the slice's largest
@@ -55,6 +57,8 @@ for _x in (1e-3, 1e-5, 1e2):
 CASES["nowrite"] = dict(decay="slow", write="zero")
 CASES["readback"] = dict(keys="exact", decay="none", write="one", q_is_k=True)
 CASES["fulldecay"] = dict(decay="full")
+CASES["reset"] = dict(decay="reset")
+CASES["corr0.1-reset"] = dict(keys="corr", sigma=0.1, decay="reset")
 
 
 @functools.lru_cache(maxsize=None)
@@ -207,3 +211,19 @@ def test_edge_decode(case):
     es = worst_slice_error(S, Sr[:1])
     say(f"[decode {case}] o bound ratio {ratio:.3f}  S {es:.3e}")
     assert ok and es <= TOL_BF16, (ratio, es)
+
+
+@pytest.mark.parametrize("path", ["chunk64_doubling_f32out", "short16_f32out", "segmented"])
+def test_full_decay_leaves_the_last_outer_product(path):
+    """With exp(g) = 0 the state after a sequence is beta k v^T of its last
+    token, which the prompt kernels reach through products of exact copies
+    (k) and split operands (beta v, to about 2^-17): held to 1e-4, well under
+    the bar, so that an error in the chunk's decay factors (the last row's
+    exp(G_last - G_t) must be exactly 1) shows."""
+    w, Or, Sr = workload("fulldecay")
+    O, S_T = run_path(path, w)
+    torch.cuda.synchronize()
+    _, Sc = closed_form("fulldecay", w)
+    es = worst_slice_error(S_T, Sc)
+    say(f"[{path} full decay] S_T against beta k v^T: {es:.3e}")
+    assert es <= 1e-4, es
