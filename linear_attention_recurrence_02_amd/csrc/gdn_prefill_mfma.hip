@@ -104,7 +104,8 @@ constexpr int AS = C + 4;         // fp16 row stride of A (token-major)
 constexpr int BS = 16 + 8;        // fp16 row stride of the 16 x 16 blocks T_ii, P_i, P'_i, M_ij
 constexpr int NS = 20;            // fp32 row stride of the diagonal blocks of N
 // How the diagonal blocks of (I + N)^-1 are formed unless the caller names a
-// method: block doubling on the matrix cores (true) or fp32 back substitution.
+// method: block doubling on the matrix cores (true) or fp32 back substitution
+// (launches that leave most CUs idle take substitution, substitution_pays).
 constexpr bool kDefaultDoubling = true;
 
 // LDS layouts.  Each array's row stride (and, for K, V and W, an XOR of the
@@ -1232,6 +1233,16 @@ bool rank_longest_first_pays(const PrefillArgs &a) {
     return cus > 0 && a.N * a.H <= 4 * static_cast<int64_t>(cus);
 }
 
+// Whether the default form of a launch should find the diagonal blocks by
+// fp32 back substitution instead of block doubling: a uniform batch of at
+// most one unit per two CUs, which leaves most of the chip idle.  Measured at
+// 4096 tokens: substitution takes 0.92, 0.94, 0.95, 0.97 and 0.99 of the
+// doubling time with 4, 16, 32, 64 and 128 units, and 1.01 with 256 and 512.
+bool substitution_pays(const PrefillArgs &a) {
+    const int cus = compute_units();
+    return !a.cu_seqlens && cus > 0 && 2 * a.N * a.H <= static_cast<int64_t>(cus);
+}
+
 template <typename OutT>
 void launch_typed(void (*kern)(const bf16 *, const bf16 *, const bf16 *, const float *, const float *,
                                const float *, const int32_t *, int64_t, int64_t, int64_t, OutT *,
@@ -1248,21 +1259,26 @@ void launch_typed(void (*kern)(const bf16 *, const bf16 *, const bf16 *, const f
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     const bool rank = rank_longest_first_pays(a);
-    // (the longest-first order is compiled into the default form only; the
-    // gated norm and the fp32 O are offered in the two inverse methods)
-    const bool dbl = a.inverse == kInverseDoubling || (a.inverse == kInverseDefault && kDefaultDoubling);
+    // The inverse method: the caller's, else doubling, save where substitution
+    // pays; the plain, gated and fp32-O forms of one launch take the same one,
+    // so that they share their arithmetic.  (The longest-first order is
+    // compiled into the default doubling form only; the pre-operations always
+    // use doubling: their producers set the period, and substitution there
+    // measured 4.0 ms against 2.2 ms on 8 x 16384 x 32.)
+    const bool dbl = a.inverse == kInverseDoubling ||
+                     (a.inverse == kInverseDefault && kDefaultDoubling && !substitution_pays(a));
     if (a.conv_w)   // the pre-operations fused into the chunk load
-        launch_typed<bf16>(rank ? prefill_mfma_kernel<false, kDefaultDoubling, true, bf16, true>
-                                : prefill_mfma_kernel<false, kDefaultDoubling, false, bf16, true>, a, stream);
+        launch_typed<bf16>(rank ? prefill_mfma_kernel<false, true, true, bf16, true>
+                                : prefill_mfma_kernel<false, true, false, bf16, true>, a, stream);
     else if (a.out_f32)
         launch_typed<float>(dbl ? prefill_mfma_kernel<false, true, false, float>
                                 : prefill_mfma_kernel<false, false, false, float>, a, stream);
     else if (a.z)
         launch_typed<bf16>(dbl ? prefill_mfma_kernel<true, true, false, bf16>
                                : prefill_mfma_kernel<true, false, false, bf16>, a, stream);
-    else if (a.inverse == kInverseDefault)
-        launch_typed<bf16>(rank ? prefill_mfma_kernel<false, kDefaultDoubling, true, bf16>
-                                : prefill_mfma_kernel<false, kDefaultDoubling, false, bf16>, a, stream);
+    else if (a.inverse == kInverseDefault && dbl)
+        launch_typed<bf16>(rank ? prefill_mfma_kernel<false, true, true, bf16>
+                                : prefill_mfma_kernel<false, true, false, bf16>, a, stream);
     else
         launch_typed<bf16>(dbl ? prefill_mfma_kernel<false, true, false, bf16>
                                : prefill_mfma_kernel<false, false, false, bf16>, a, stream);
