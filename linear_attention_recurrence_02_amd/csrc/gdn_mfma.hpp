@@ -46,9 +46,25 @@ __device__ __forceinline__ bf16x8 catb(bf16x4 a, bf16x4 b) {
 struct h4x2 {
     f16x4 hi, lo;
 };
+// -1 in a scalar register that the compiler cannot see through: x + hi * (-1)
+// then stays one mixed-precision fused multiply-add per value (v_fma_mixlo_f16
+// and v_fma_mixhi_f16 read hi as fp16 straight from its packed register and
+// round to fp16 into either half of the lo register), where a visible -1 lets
+// the compiler fold it into a convert, a subtract and a second convert.
+__device__ __forceinline__ float opaque_minus_one() {
+    float m = -1.f;
+    asm volatile("" : "+s"(m));
+    return m;
+}
+// x - hi is exact in fp32 (hi is x rounded to the nearest fp16, or x's
+// residual is below fp16's subnormal step), so lo is x - hi rounded once.
 __device__ __forceinline__ h4x2 split_h4(f32x4 x) {
     const f16x4 hi = h4(x);
-    return h4x2{hi, h4(x - f4(hi))};
+    const float m1 = opaque_minus_one();
+    f16x4 lo;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lo[i] = static_cast<f16>(__builtin_fmaf(static_cast<float>(hi[i]), m1, x[i]));
+    return h4x2{hi, lo};
 }
 // The same split in bf16 (8 significant bits each, about 2^-17 together, with
 // fp32's exponent range).
@@ -79,6 +95,22 @@ __device__ __forceinline__ f16x8 rd8(const f16 *p) { return *reinterpret_cast<co
 // the whole chunk loop.
 __device__ __forceinline__ int opaque(int x) {
     asm volatile("" : "+v"(x));
+    return x;
+}
+
+// s_waitcnt operands (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4, lgkmcnt in 11:8; a field at its maximum waits for nothing).  The
+// vector-memory counter counts stores as well as loads.
+constexpr int kVmcnt0 = 0x0f70;     // vmcnt(0)
+constexpr int kLgkmcnt0 = 0xc07f;   // lgkmcnt(0)
+
+// The lane's index in its wave, recomputed where it is called (two vector ALU
+// instructions; volatile, so it is neither hoisted nor merged with another
+// call): a kernel that needs lane-derived indices in every period then keeps
+// no register for them across the loop, and never reloads one from scratch.
+__device__ __forceinline__ int fresh_lane_id() {
+    int x;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(x));
     return x;
 }
 

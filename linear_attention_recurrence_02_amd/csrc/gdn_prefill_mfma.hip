@@ -690,10 +690,9 @@ struct Producer {
 // that enters the chunk); S is rescaled when the scale changes.  W's chain is
 // W_i = P_i K_i - sum_j M_ij W_j with P and M split and W single; U's chain
 // U_i = X_i - sum_j M_ij U_j with M and U split.
-__device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int r16, int q, f32x4 (*Uo)[2],
-                                        f32x4 (*S)[2], int &sc, float ms) {
-    r16 = opaque(r16);
-    q = opaque(q);
+__device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2], f32x4 (*S)[2], int &sc,
+                                        float ms) {
+    const int lane = fresh_lane_id(), r16 = lane & 15, q = lane >> 4;
     const int trk = (4 * q + (r16 >> 2)) * KS + ((4 * (r16 & 3)) ^ ksw(4 * q));
     const f16 *kb = sm.K[nb] + trk + 32 * p;
     const f16 *vb = reinterpret_cast<const f16 *>(sm.V) + trk + 32 * p;
@@ -795,7 +794,11 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, l = tid & 63, r16 = l & 15, qd = l >> 4;
+    // the wave index is the same in every lane: read it once into a scalar
+    // register, so that everything derived from it (roles, column groups, row
+    // blocks, LDS offsets) stays scalar instead of taking vector registers
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int l = tid & 63, r16 = l & 15, qd = l >> 4;
     const int w = wave & 3;                 // consumer column group / producer row block
     // A packed batch of sequences of mixed lengths is walked longest first
     // (in the instantiation the launch picks for it), so that the long ones do
@@ -908,6 +911,11 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 // nobody reads in phase 3, V waits for phase 1
                 pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
                 pr.store_q(sm, nb ^ 1, w, l, r16, qd);
+                // Every load in flight has been consumed by now; saying so
+                // here keeps the compiler from placing a wait after the new
+                // loads (the counter drains in order, so such a wait would
+                // hold the wave for their full latency).
+                __builtin_amdgcn_s_waitcnt(kVmcnt0);
                 pr.prefetch(u, c + 3, w, l, r16, qd);
             }
             __syncthreads();
@@ -962,7 +970,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     __syncthreads();
     __syncthreads();
     f32x4 Ur[4][2];
-    wu_step(sm, 0, w, r16, qd, Ur, S, sc, lane_max_s());
+    wu_step(sm, 0, w, Ur, S, sc, lane_max_s());
     __syncthreads();
 
     const uint32_t HD = static_cast<uint32_t>(H) * D;
@@ -1069,18 +1077,29 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         // leaves its partial sums of O^2 per token row in LDS; the four waves
         // meet on an LDS counter and the rows are scaled by
         // 1/sqrt(mean(O^2) + eps) and stored.
-        OutT *obase = O + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
+        // O rows of the chunk: a base common to the wave (kept in scalar
+        // registers) plus one 32-bit byte offset per lane.  No per-lane 64-bit
+        // address then has to survive the products, so none is spilled: a
+        // reload from scratch would wait for every store the wave has in
+        // flight, the output stores included.
+        char *const obase = reinterpret_cast<char *>(O + (u.row0(c) * H + u.h) * D);
+        const uint32_t olane = (static_cast<uint32_t>(r16) * HD + 32 * w + 4 * qd) * sizeof(OutT);
+        auto orow = [&](int m, int cc) {
+            return obase + static_cast<uint32_t>(16 * m) * HD * sizeof(OutT) + olane + 16 * cc * sizeof(OutT);
+        };
         f32x4 Ot[4][2];           // Ot[m][cc]: O[16m + r16][32w + 16cc + 4q + e]
         {
             bf16x4 zr[4][2];
             if constexpr (kGated) {
-                const bf16 *zc = z + (u.row0(c) * H + u.h) * D + 32 * w + 4 * qd;
+                const char *zc = reinterpret_cast<const char *>(z + (u.row0(c) * H + u.h) * D);
+                const uint32_t zlane = (32 * w + 4 * qd) * sizeof(bf16);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int t = 16 * m + r16;
-                    const uint32_t off = static_cast<uint32_t>(t < cnv ? t : 0) * HD;
+                    const uint32_t off = static_cast<uint32_t>(t < cnv ? t : 0) * HD * sizeof(bf16) + zlane;
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) zr[m][cc] = *reinterpret_cast<const bf16x4 *>(zc + off + 16 * cc);
+                    for (int cc = 0; cc < 2; ++cc)
+                        zr[m][cc] = *reinterpret_cast<const bf16x4 *>(zc + off + 16 * cc * sizeof(bf16));
                 }
             }
 #pragma unroll
@@ -1167,7 +1186,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 // so the count reaches 4 (c + 1); the spin is bounded all the
                 // same.
                 asm volatile("" ::: "memory");
-                __builtin_amdgcn_s_waitcnt(0xc07f);       // lgkmcnt(0): partials landed
+                __builtin_amdgcn_s_waitcnt(kLgkmcnt0);    // partials landed
                 if (l == 0) __hip_atomic_fetch_add(&sm.NPC, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
                 const uint32_t target = 4u * static_cast<uint32_t>(c + 1);
                 for (int spin = 0; spin < (1 << 22); ++spin) {
@@ -1179,7 +1198,6 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 asm volatile("" ::: "memory");
                 const int rr = opaque(r16);
                 const float *np = &sm.NP[rr][0];
-                OutT *orow = obase + static_cast<uint32_t>(rr) * HD;
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const f32x4 ps = *reinterpret_cast<const f32x4 *>(np + 64 * m);
@@ -1188,8 +1206,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     if (rr < cnv - 16 * m) {
 #pragma unroll
                         for (int cc = 0; cc < 2; ++cc)
-                            *reinterpret_cast<bf16x4 *>(orow + 16 * m * HD + 16 * cc) =
-                                __builtin_convertvector(Ot[m][cc] * rs, bf16x4);
+                            *reinterpret_cast<bf16x4 *>(orow(m, cc)) = __builtin_convertvector(Ot[m][cc] * rs, bf16x4);
                     }
                 }
             } else {
@@ -1197,13 +1214,12 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 for (int m = 0; m < 4; ++m) {
                     const int t = 16 * m + r16;
                     if (O && t < cnv) {
-                        const uint32_t off = static_cast<uint32_t>(t) * HD;
 #pragma unroll
                         for (int cc = 0; cc < 2; ++cc) {
                             if constexpr (sizeof(OutT) == 4)
-                                *reinterpret_cast<f32x4 *>(obase + off + 16 * cc) = Ot[m][cc];
+                                *reinterpret_cast<f32x4 *>(orow(m, cc)) = Ot[m][cc];
                             else
-                                *reinterpret_cast<bf16x4 *>(obase + off + 16 * cc) = __builtin_convertvector(Ot[m][cc], bf16x4);
+                                *reinterpret_cast<bf16x4 *>(orow(m, cc)) = __builtin_convertvector(Ot[m][cc], bf16x4);
                         }
                     }
                 }
@@ -1212,7 +1228,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         const float msl = lane_max_s();   // the state entering chunk c + 1
         __syncthreads();
         // ======== phase 3: W and U of the next chunk ========
-        if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, r16, qd, Ur, S, sc, msl);
+        if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, Ur, S, sc, msl);
         __syncthreads();
     }
     store_state();
