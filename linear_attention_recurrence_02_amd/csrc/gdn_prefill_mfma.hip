@@ -236,48 +236,63 @@ struct Unit {
     __device__ int64_t row0(int pc) const { return start + int64_t(pc) * C; }
 };
 
-// Producer wave p = 4..7 - 4 (lane r16 + 16 q).  Rows 16p + r16 of chunk c+2
-// (and token l's g and beta) are loaded into pK, pV, pQ (pg, pb) a period
-// ahead; in phase 3 of period c they are converted to fp16 and K, Q and the
-// per-token scalars are stored (the consumers' W/U step reads neither buffer),
-// while V waits in hV for phase 1 of the next period, after the consumers'
-// W/U step has read the previous V.
+// Producer wave p = 4..7 - 4 (lane r16 + 16 q) stages rows 16p + r16 of each
+// chunk from registers loaded a period ahead.  K and Q (and token l's g and
+// beta, for wave p = 0, which scans them) of chunk c+2 are converted and
+// stored in phase 3 of period c, into the buffers the consumers' W/U step does
+// not read, and each stream's loads for chunk c+3 go out as soon as its
+// registers are free.  V is single-buffered (the W/U step of phase 3 reads
+// it): V of chunk c+1 is stored in phase 1 of period c, and the loads of V of
+// chunk c+2 follow at once into the same registers.
 struct Producer {
     f32x4 pK[4], pV[4], pQ[4];
-    f32x4 hV[4], hQ[4];
     float pg, pb;
     float sg2, seg, sec, sbt;     // scan results of the staged chunk (wave p = 0)
     h4x2 Ah[4];                   // A tiles of the chunk being prepared, hi/lo (phase 1 -> 3)
     h4x2 Nop[3];                  // off-diagonal N blocks of the chunk, hi/lo (phase 1 -> 2)
 
-    __device__ void prefetch(const Unit &u, int pc, int p, int l, int r16, int q) {
-        const int nv = u.rows_in(pc);
-        load_rows(pK, u.k, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
+    __device__ void load_v(const Unit &u, int pc, int p, int r16, int q) {
         if (u.v) {
-            load_rows(pV, u.v, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
+            load_rows(pV, u.v, u.start, u.row0(pc), 16 * p + r16, u.rows_in(pc), u.H, u.h, q);
         } else {
 #pragma unroll
             for (int s = 0; s < 4; ++s) pV[s] = zero4();
         }
-        load_rows(pQ, u.q, u.start, u.row0(pc), 16 * p + r16, nv, u.H, u.h, q);
-        const int64_t gi = (l < nv ? u.row0(pc) + l : u.start) * u.H + u.h;
+    }
+    __device__ void load_k(const Unit &u, int pc, int p, int r16, int q) {
+        load_rows(pK, u.k, u.start, u.row0(pc), 16 * p + r16, u.rows_in(pc), u.H, u.h, q);
+    }
+    __device__ void load_q(const Unit &u, int pc, int p, int r16, int q) {
+        load_rows(pQ, u.q, u.start, u.row0(pc), 16 * p + r16, u.rows_in(pc), u.H, u.h, q);
+    }
+    __device__ void load_gates(const Unit &u, int pc, int l) {
+        const int64_t gi = (l < u.rows_in(pc) ? u.row0(pc) + l : u.start) * u.H + u.h;
         pg = u.g[gi];
         pb = u.beta[gi];
     }
-    // Convert the prefetched K and Q rows to fp16 (V stays bf16; rows past nv
-    // are zeroed), store K in buffer set nb, keep V and Q, scan the log-decay
-    // (wave p = 0).
-    __device__ void convert(Smem &sm, int nb, int nv, int p, int l, int r16, int q) {
+    // Phase 3: K and Q of the chunk in the registers (nv rows) converted to
+    // fp16 (rows past nv zeroed) and stored in buffer set nb, with the
+    // per-token scalars (wave p = 0); each stream's registers then take the
+    // loads of chunk pn.
+    __device__ void stage_kq(Smem &sm, int nb, int nv, int p, int l, int r16, int q, const Unit &u, int pn) {
         to_fp16_rows(pK, 16 * p + r16, nv);
         store_rows_kv(sm.K[nb], pK, 16 * p + r16, q);
-        mask_rows(pV, 16 * p + r16, nv);
+        load_k(u, pn, p, r16, q);
         to_fp16_rows(pQ, 16 * p + r16, nv);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            hV[s] = pV[s];
-            hQ[s] = pQ[s];
+        store_rows_q(sm.Q[nb], pQ, 16 * p + r16, q);
+        load_q(u, pn, p, r16, q);
+        if (p == 0) {
+            scan(nv, l);
+            store_scalars(sm, nb, p, l);
+            load_gates(u, pn, l);
         }
-        if (p == 0) scan(nv, l);
+    }
+    // Phase 1: V of the chunk in the registers (nv rows, the rest zeroed) to
+    // LDS, then the loads of chunk pn.
+    __device__ void stage_v(Smem &sm, int nv, int p, int r16, int q, const Unit &u, int pn) {
+        mask_rows(pV, 16 * p + r16, nv);
+        store_rows_kv(sm.V, pV, 16 * p + r16, q);
+        load_v(u, pn, p, r16, q);
     }
     // The per-token scalars of the staged chunk from g and beta (wave p = 0,
     // lane l = token l; rows past nv take g = 0, beta = 0).
@@ -439,11 +454,6 @@ struct Producer {
         }
     }
 
-    __device__ void store_v(Smem &sm, int p, int r16, int q) { store_rows_kv(sm.V, hV, 16 * p + r16, q); }
-    __device__ void store_q(Smem &sm, int nb, int p, int l, int r16, int q) {
-        store_rows_q(sm.Q[nb], hQ, 16 * p + r16, q);
-        store_scalars(sm, nb, p, l);
-    }
 
     // Phase 1 for the chunk in buffer set nb: the Gram tiles of row block P of
     // K K^T (-> the diagonal block of N in LDS, the off-diagonal ones kept in
@@ -843,10 +853,11 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             pr.store_q_pre(sm, 0, w, l);
             pr.prefetch_pre(u, 1, w, l);
         } else {
-            pr.prefetch(u, 0, w, l, r16, qd);
-            pr.convert(sm, 0, u.rows_in(0), w, l, r16, qd);
-            pr.store_q(sm, 0, w, l, r16, qd);
-            pr.prefetch(u, 1, w, l, r16, qd);
+            pr.load_k(u, 0, w, r16, qd);
+            pr.load_q(u, 0, w, r16, qd);
+            pr.load_v(u, 0, w, r16, qd);
+            if (w == 0) pr.load_gates(u, 0, l);
+            pr.stage_kq(sm, 0, u.rows_in(0), w, l, r16, qd, u, 1);
         }
         __syncthreads();
         // Period c (c = -1 .. nch-1) prepares chunk c+1 and stages chunk c+2;
@@ -856,7 +867,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             if constexpr (kPreop)                      // V of chunk c+1
                 pr.store_v_pre(sm, w, l);
             else
-                pr.store_v(sm, w, r16, qd);
+                pr.stage_v(sm, u.rows_in(c + 1), w, r16, qd, u, c + 2);
             switch (w) {
             case 0: pr.gram<0>(sm, nb, r16, qd); break;
             case 1: pr.gram<1>(sm, nb, r16, qd); break;
@@ -906,17 +917,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 pr.prefetch_gates(u, c + 3, l);
                 __builtin_amdgcn_s_setprio(0);
             } else {
-                // the rows of chunk c+2 converted beside the consumers' W/U
-                // step, this phase's longer work: K and Q go to the buffers
-                // nobody reads in phase 3, V waits for phase 1
-                pr.convert(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd);
-                pr.store_q(sm, nb ^ 1, w, l, r16, qd);
-                // Every load in flight has been consumed by now; saying so
-                // here keeps the compiler from placing a wait after the new
-                // loads (the counter drains in order, so such a wait would
-                // hold the wave for their full latency).
-                __builtin_amdgcn_s_waitcnt(kVmcnt0);
-                pr.prefetch(u, c + 3, w, l, r16, qd);
+                // K and Q of chunk c+2 staged beside the consumers' W/U step
+                // (into the buffers nobody reads in phase 3), and the loads of
+                // chunk c+3
+                pr.stage_kq(sm, nb ^ 1, u.rows_in(c + 2), w, l, r16, qd, u, c + 3);
             }
             __syncthreads();
         }
