@@ -1067,6 +1067,17 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                         }
             }
         }
+        // The largest |S| of the state entering chunk c + 1, for the scale of
+        // the next W/U step.  With the gated norm it is taken here and held
+        // (the compiler guards that form's reads of state registers with a
+        // wait on the vector-memory counter, which in phase 3 would also wait
+        // for this chunk's output stores); the other forms take it at the end
+        // of phase 2, off the recurrence's chain.
+        float msl = 0.f;
+        if constexpr (kGated) {
+            msl = lane_max_s();
+            asm volatile("" : "+v"(msl));
+        }
         __syncthreads();
 
         // ======== phase 2: O = diag(exp G) Q S + A D (S as it entered the chunk) ========
@@ -1229,7 +1240,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 }
             }
         }
-        const float msl = lane_max_s();   // the state entering chunk c + 1
+        if constexpr (!kGated) msl = lane_max_s();
         __syncthreads();
         // ======== phase 3: W and U of the next chunk ========
         if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, Ur, S, sc, msl);
