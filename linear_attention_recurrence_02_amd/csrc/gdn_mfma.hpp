@@ -169,13 +169,19 @@ __device__ __forceinline__ float wave_prefix_sum(float x) {
     x = dpp_add<0x143, 0xc>(x);   // row_bcast:31 into rows 2, 3
     return x;
 }
+// The maxima below take IEEE maximum (a NaN operand gives NaN) rather than
+// maxNum: maxNum must first quiet each operand that a product may have left
+// signalling, one extra instruction per value, where maximum maps to gfx950's
+// three-operand v_maximum3_f32 with |.| folded into its operand modifiers.
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Maximum of a non-negative value over the 64 lanes of a wave (DPP moves as in
 // wave_prefix_sum, lanes without a source contributing 0), returned to every
 // lane.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_max(float v) {
     const int t = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, true);
-    return __builtin_fmaxf(v, __builtin_bit_cast(float, t));
+    return fmax_ieee(v, __builtin_bit_cast(float, t));
 }
 __device__ __forceinline__ float wave_max_nonneg(float x) {
     x = dpp_max<0x111, 0xf>(x);   // row_shr:1
@@ -188,8 +194,8 @@ __device__ __forceinline__ float wave_max_nonneg(float x) {
 }
 // Largest |x| of a lane's tile values.
 __device__ __forceinline__ float absmax4(f32x4 x, float m) {
-    return __builtin_fmaxf(__builtin_fmaxf(__builtin_fmaxf(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])),
-                                           __builtin_fmaxf(__builtin_fabsf(x[2]), __builtin_fabsf(x[3]))), m);
+    return fmax_ieee(fmax_ieee(fmax_ieee(__builtin_fabsf(x[0]), __builtin_fabsf(x[1])), m),
+                     fmax_ieee(__builtin_fabsf(x[2]), __builtin_fabsf(x[3])));
 }
 
 // Bound on the scale exponents, so that a change of scale is one exact

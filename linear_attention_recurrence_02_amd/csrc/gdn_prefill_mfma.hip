@@ -459,12 +459,14 @@ struct Producer {
     // K K^T (-> the diagonal block of N in LDS, the off-diagonal ones kept in
     // Nop) and of column block IB = 3 - P of K Q^T (-> A, kept in Ah).  Masked
     // decay factors take exp2(-inf) = 0 rather than a branch.
-    template <int P>
+    template <int P, bool kHoist>
     __device__ void gram(Smem &sm, int nb, int r16, int q) {
         constexpr int IB = 3 - P;
         constexpr float kNegInf = -__builtin_huge_valf();
-        r16 = opaque(r16);
-        q = opaque(q);
+        if constexpr (!kHoist) {
+            r16 = opaque(r16);
+            q = opaque(q);
+        }
         const f16 *Kn = sm.K[nb], *Qn = sm.Q[nb];
         const float *G2 = sm.G2[nb], *Bt = sm.Bt[nb];
         constexpr int JM = P > IB ? P : IB;   // K row blocks read: 0..JM
@@ -585,10 +587,12 @@ struct Producer {
     // substitution (row r16 per lane; the four lane groups repeat it) or by
     // block doubling (invert_doubling), T_PP, P_P and P'_P to LDS, and
     // M_Pj = T_PP N_Pj for j < P.
-    template <int P, bool kDoubling>
+    template <int P, bool kDoubling, bool kHoist>
     __device__ void solve(Smem &sm, int nb, int r16, int q) {
-        r16 = opaque(r16);
-        q = opaque(q);
+        if constexpr (!kHoist) {
+            r16 = opaque(r16);
+            q = opaque(q);
+        }
         const float *Bt = sm.Bt[nb], *EG = sm.EG[nb];
         f32x4 y4;       // T_PP[r16][4q..4q+3]
         if constexpr (kDoubling) {
@@ -737,7 +741,7 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2],
             Uo[i][cc] = mfma_bf(pu[i], catb(vx[i][cc], vx[i][cc]), zero4());
             mx = absmax4(Uo[i][cc], mx);
         }
-    const int nx = choose_scale(0.f, sc, wave_max_nonneg(__builtin_fmaxf(ms * pow2i(-sc), mx)));
+    const int nx = choose_scale(0.f, sc, wave_max_nonneg(fmax_ieee(ms * pow2i(-sc), mx)));
     if (nx != sc) {
         const float f = pow2i(nx - sc);
 #pragma unroll
@@ -845,6 +849,11 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             *reinterpret_cast<f32x4 *>(&sm.A[1][i]) = zero4();
         }
         Producer pr;
+        // Lane-constant masks and offsets of the Gram and inverse steps are
+        // hoisted out of the chunk loop (scalar lane masks and a few registers)
+        // where the registers allow it; the substitution and pre-operation
+        // forms need their registers and recompute them in every period.
+        constexpr bool kHoist = kDoubling && !kPreop;
         if constexpr (kPreop) {
             pr.load_weights(u, l);
             pr.prefetch_pre(u, 0, w, l);
@@ -869,10 +878,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             else
                 pr.stage_v(sm, u.rows_in(c + 1), w, r16, qd, u, c + 2);
             switch (w) {
-            case 0: pr.gram<0>(sm, nb, r16, qd); break;
-            case 1: pr.gram<1>(sm, nb, r16, qd); break;
-            case 2: pr.gram<2>(sm, nb, r16, qd); break;
-            default: pr.gram<3>(sm, nb, r16, qd); break;
+            case 0: pr.gram<0, kHoist>(sm, nb, r16, qd); break;
+            case 1: pr.gram<1, kHoist>(sm, nb, r16, qd); break;
+            case 2: pr.gram<2, kHoist>(sm, nb, r16, qd); break;
+            default: pr.gram<3, kHoist>(sm, nb, r16, qd); break;
             }
             __syncthreads();
             // Phase 2's longest work: with the pre-operations the producers'
@@ -887,10 +896,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                 if (w == 3) __builtin_amdgcn_s_setprio(1);
             }
             switch (w) {
-            case 0: pr.solve<0, kDoubling>(sm, nb, r16, qd); break;
-            case 1: pr.solve<1, kDoubling>(sm, nb, r16, qd); break;
-            case 2: pr.solve<2, kDoubling>(sm, nb, r16, qd); break;
-            default: pr.solve<3, kDoubling>(sm, nb, r16, qd); break;
+            case 0: pr.solve<0, kDoubling, kHoist>(sm, nb, r16, qd); break;
+            case 1: pr.solve<1, kDoubling, kHoist>(sm, nb, r16, qd); break;
+            case 2: pr.solve<2, kDoubling, kHoist>(sm, nb, r16, qd); break;
+            default: pr.solve<3, kDoubling, kHoist>(sm, nb, r16, qd); break;
             }
             // K of chunk c+2 goes to the buffer nobody reads in phases 2 and 3
             if constexpr (kPreop) {

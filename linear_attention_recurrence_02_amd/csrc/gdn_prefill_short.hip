@@ -263,7 +263,7 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i) ms = absmax4(S[i][1], absmax4(S[i][0], ms));
             const float mu = absmax4(U[1], absmax4(U[0], 0.f));
-            const float m = wave_max_nonneg(__builtin_fmaxf(ms * pow2i(-sc_exp), mu));
+            const float m = wave_max_nonneg(fmax_ieee(ms * pow2i(-sc_exp), mu));
             const int nx = choose_scale(0.f, sc_exp, m);
             if (nx != sc_exp) {
                 const float f = pow2i(nx - sc_exp);
