@@ -42,7 +42,9 @@ __device__ __forceinline__ bf16x8 catb(bf16x4 a, bf16x4 b) {
 // x's relative rounding error 2^-11; written as hi + lo, with hi = fp16(x) and
 // lo = fp16(x - hi), the pair holds x to about 2^-22 (relative to x, for hi
 // normal).  A product with one split operand is one K = 32 product of
-// [hi lo] with [b; b]; with both split, the lo * lo term is dropped.
+// [hi lo] with [b; b]; with both split, either (hi + lo) b_hi and hi b_lo
+// (the lo * lo term dropped) or, where the [hi lo] operand serves both,
+// (hi + lo) b_hi and (hi + lo) b_lo (prod_split).
 struct h4x2 {
     f16x4 hi, lo;
 };
@@ -74,6 +76,14 @@ struct b4x2 {
 __device__ __forceinline__ b4x2 split_b4(f32x4 x) {
     const bf16x4 hi = __builtin_convertvector(x, bf16x4);
     return b4x2{hi, __builtin_convertvector(x - __builtin_convertvector(hi, f32x4), bf16x4)};
+}
+
+// c + x y with both operands split: (x_hi + x_lo) y_hi and (x_hi + x_lo) y_lo,
+// two K = 32 products sharing the [hi lo] operand (the lo * lo term, about
+// 2^-22 of the product, comes with them).
+__device__ __forceinline__ f32x4 prod_split(h4x2 x, h4x2 y, f32x4 c) {
+    const f16x8 xa = cat(x.hi, x.lo);
+    return mfma(xa, cat(y.lo, y.lo), mfma(xa, cat(y.hi, y.hi), c));
 }
 
 // Exact powers of two as floats, for exponents in [-126, 127].

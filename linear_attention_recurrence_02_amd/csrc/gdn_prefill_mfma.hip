@@ -547,9 +547,9 @@ struct Producer {
     // T R and its transpose R^T T^T.  T and U = T^T are both kept as result
     // tiles (lane (c = r16, q) holds T[4q+e][c] and T[c][4q+e]): a result tile
     // is a B operand as it is, and read as an A operand it is its own
-    // transpose.  Operands are split into fp16 hi + lo pairs (the lo * lo term
-    // dropped), sums are fp32.  Returns the U tile: columns 4q..4q+3 of row r16
-    // of T_PP.
+    // transpose.  Operands are split into fp16 hi + lo pairs, sums are fp32;
+    // C_b is taken negated, so that each step accumulates onto T's tiles.
+    // Returns the U tile: columns 4q..4q+3 of row r16 of T_PP.
     template <int P>
     __device__ f32x4 invert_doubling(const Smem &sm, int r16, int q) {
         const float *Nr = sm.NR[P];
@@ -563,22 +563,18 @@ struct Producer {
             Tt[e] = (i == r16 ? 1.f : 0.f) - ((r16 & 1) == 0 && i == r16 + 1 ? nsub : 0.f);
             Ut[e] = (i == r16 ? 1.f : 0.f) - ((r16 & 1) == 1 && i == r16 - 1 ? nrow[e] : 0.f);
         }
-        // x y with both split: (x_hi + x_lo) y_hi + x_hi y_lo
-        auto prod = [](h4x2 x, h4x2 y) {
-            return mfma16(x.hi, y.lo, mfma(cat(x.hi, x.lo), cat(y.hi, y.hi), zero4()));
-        };
 #pragma unroll
         for (int b = 2; b <= 8; b *= 2) {
-            f32x4 cb;   // C_b[r16][4q+e]: rows in the lower half of a 2b block, columns in its upper half
+            f32x4 cb;   // -C_b[r16][4q+e]: rows in the lower half of a 2b block, columns in its upper half
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int j = 4 * q + e;
-                cb[e] = ((r16 / b) & 1) && j / b == r16 / b - 1 ? nrow[e] : 0.f;
+                cb[e] = ((r16 / b) & 1) && j / b == r16 / b - 1 ? -nrow[e] : 0.f;
             }
-            const h4x2 R = split_h4(prod(split_h4(cb), split_h4(Tt)));   // C_b T
+            const h4x2 R = split_h4(prod_split(split_h4(cb), split_h4(Tt), zero4()));   // -C_b T
             const h4x2 uh = split_h4(Ut);
-            Tt -= prod(uh, R);                                            // T C_b T
-            Ut -= prod(R, uh);                                            // (T C_b T)^T
+            Tt = prod_split(uh, R, Tt);                                  // T - T C_b T
+            Ut = prod_split(R, uh, Ut);                                  // its transpose
         }
         return Ut;
     }
@@ -674,8 +670,7 @@ struct Producer {
             const h4x2 tb = split_h4(y4);
 #pragma unroll
             for (int jb = 0; jb < P; ++jb) {
-                const f32x4 mt = mfma16(Nop[jb].hi, tb.lo,
-                                        mfma(cat(Nop[jb].hi, Nop[jb].lo), cat(tb.hi, tb.hi), zero4()));
+                const f32x4 mt = prod_split(Nop[jb], tb, zero4());
                 const h4x2 m = split_h4(-mt);
                 *reinterpret_cast<f16x4 *>(&sm.M[0][oblk(P, jb)][r16 * BS + 4 * q]) = m.hi;
                 *reinterpret_cast<f16x4 *>(&sm.M[1][oblk(P, jb)][r16 * BS + 4 * q]) = m.lo;
@@ -772,16 +767,16 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2],
                 au[cc] = mfma(cat(mj.hi, mj.lo), cat(Ur[j][cc].hi, Ur[j][cc].hi), au[cc]);
             }
         }
-        // ... and M_hi U_lo, two blocks j to a product
+        // ... and M U_lo: M_hi of two blocks j to a product, or (hi + lo) of one
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             if (i == 1) {
-                au[cc] = mfma16(mm[oblk(1, 0)].hi, Ur[0][cc].lo, au[cc]);
+                au[cc] = mfma(cat(mm[oblk(1, 0)].hi, mm[oblk(1, 0)].lo), cat(Ur[0][cc].lo, Ur[0][cc].lo), au[cc]);
             } else if (i == 2) {
                 au[cc] = mfma(cat(mm[oblk(2, 0)].hi, mm[oblk(2, 1)].hi), cat(Ur[0][cc].lo, Ur[1][cc].lo), au[cc]);
             } else if (i == 3) {
                 au[cc] = mfma(cat(mm[oblk(3, 0)].hi, mm[oblk(3, 1)].hi), cat(Ur[0][cc].lo, Ur[1][cc].lo), au[cc]);
-                au[cc] = mfma16(mm[oblk(3, 2)].hi, Ur[2][cc].lo, au[cc]);
+                au[cc] = mfma(cat(mm[oblk(3, 2)].hi, mm[oblk(3, 2)].lo), cat(Ur[2][cc].lo, Ur[2][cc].lo), au[cc]);
             }
         }
 #pragma unroll
