@@ -104,8 +104,9 @@ constexpr int AS = C + 4;         // fp16 row stride of A (token-major)
 constexpr int BS = 16 + 8;        // fp16 row stride of the 16 x 16 blocks T_ii, P_i, P'_i, M_ij
 constexpr int NS = 20;            // fp32 row stride of the diagonal blocks of N
 // How the diagonal blocks of (I + N)^-1 are formed unless the caller names a
-// method: block doubling on the matrix cores (true) or fp32 back substitution
-// (launches that leave most CUs idle take substitution, substitution_pays).
+// method: block doubling on the matrix cores (true) or fp32 back substitution.
+// Doubling measured 2-6% faster at every launch size from 4 to 512 units of
+// 4096 tokens (its producers also keep their lane masks out of the chunk loop).
 constexpr bool kDefaultDoubling = true;
 
 // LDS layouts.  Each array's row stride (and, for K, V and W, an XOR of the
@@ -1271,16 +1272,6 @@ bool rank_longest_first_pays(const PrefillArgs &a) {
     return cus > 0 && a.N * a.H <= 4 * static_cast<int64_t>(cus);
 }
 
-// Whether the default form of a launch should find the diagonal blocks by
-// fp32 back substitution instead of block doubling: a uniform batch of at
-// most one unit per two CUs, which leaves most of the chip idle.  Measured at
-// 4096 tokens: substitution takes 0.92, 0.94, 0.95, 0.97 and 0.99 of the
-// doubling time with 4, 16, 32, 64 and 128 units, and 1.01 with 256 and 512.
-bool substitution_pays(const PrefillArgs &a) {
-    const int cus = compute_units();
-    return !a.cu_seqlens && cus > 0 && 2 * a.N * a.H <= static_cast<int64_t>(cus);
-}
-
 template <typename OutT>
 void launch_typed(void (*kern)(const bf16 *, const bf16 *, const bf16 *, const float *, const float *,
                                const float *, const int32_t *, int64_t, int64_t, int64_t, OutT *,
@@ -1297,14 +1288,13 @@ void launch_typed(void (*kern)(const bf16 *, const bf16 *, const bf16 *, const f
 
 hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     const bool rank = rank_longest_first_pays(a);
-    // The inverse method: the caller's, else doubling, save where substitution
-    // pays; the plain, gated and fp32-O forms of one launch take the same one,
-    // so that they share their arithmetic.  (The longest-first order is
-    // compiled into the default doubling form only; the pre-operations always
-    // use doubling: their producers set the period, and substitution there
-    // measured 4.0 ms against 2.2 ms on 8 x 16384 x 32.)
-    const bool dbl = a.inverse == kInverseDoubling ||
-                     (a.inverse == kInverseDefault && kDefaultDoubling && !substitution_pays(a));
+    // The inverse method: the caller's, else the default; the plain, gated and
+    // fp32-O forms take the same one, so that they share their arithmetic.
+    // (The longest-first order is compiled into the default doubling form
+    // only; the pre-operations always use doubling: their producers set the
+    // period, and substitution there measured 4.0 ms against 2.2 ms on
+    // 8 x 16384 x 32.)
+    const bool dbl = a.inverse == kInverseDoubling || (a.inverse == kInverseDefault && kDefaultDoubling);
     if (a.conv_w)   // the pre-operations fused into the chunk load
         launch_typed<bf16>(rank ? prefill_mfma_kernel<false, true, true, bf16, true>
                                 : prefill_mfma_kernel<false, true, false, bf16, true>, a, stream);
