@@ -46,12 +46,14 @@
 //     prefetched into registers a period earlier; K and Q converted to fp16,
 //     V kept as bf16).
 //   Each chunk period has three barrier-separated phases:
-//     1: consumers D, state update (chunk c)  | producers Gram tiles (c+1),
-//                                            |   store V (c+1)
+//     1: consumers D, state update (chunk c)  | producers store V (c+1), then
+//                                            |   load V (c+2); Gram tiles (c+1)
 //     2: consumers O (chunk c)               | producers T_ii, P_i, M_ij (c+1)
 //     3: consumers W, U (chunk c+1)          | producers store A (c+1); convert
-//                                            |   c+2, store its K, Q and
-//                                            |   scalars; prefetch c+3
+//                                            |   c+2's K and Q, store them and
+//                                            |   the scalars; each stream's
+//                                            |   loads for c+3 go out as soon
+//                                            |   as its registers are free
 //   Each array is written in a phase in which nobody reads it: K, Q and the
 //   per-token scalars are double-buffered, everything else is single.
 //   The two roles run as two separate loops under a wave-uniform branch and
