@@ -263,11 +263,12 @@ def bench_decode_preop(torch, gdn, inputs, steps):
     return out
 
 
-def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
+def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None, columns=None):
     """The prompt form over workload w; with gate = (z, norm_w, eps) the form
     with the gated RMS norm on the output (gdn_chunk_prefill_gated); with
     segment_len the segmented form (gdn_chunk_prefill_segmented; its
-    workspace is allocated before the timed calls)."""
+    workspace is allocated before the timed calls); with columns a
+    GDN_COLUMNS_* choice (gdn_chunk_prefill_ex)."""
     O = torch.empty_like(w.v)
     N = w.q.shape[0] if w.cu_seqlens is None else w.cu_seqlens.numel() - 1
     S_T = torch.empty((N, w.q.shape[2], DK, DV), dtype=torch.float32, device="cuda")
@@ -283,7 +284,7 @@ def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
                                             workspace=ws, O=O, S_T=S_T)
         elif gate is None:
             gdn.gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, w.chunk,
-                                  O=O, S_T=S_T)
+                                  O=O, S_T=S_T, columns=columns)
         else:
             gdn.gdn_chunk_prefill_gated(w.q, w.k, w.v, w.g, w.beta, *gate, w.S0,
                                         w.cu_seqlens, w.chunk, Y=O, S_T=S_T)
@@ -309,7 +310,9 @@ def bench_prefill(torch, gdn, w, iters, warmup, gate=None, segment_len=None):
         nbytes += tokens * H * DV * esz          # the gate rows z
     return {
         "workload": w.name + ("_gated_norm" if gate is not None else "")
-                    + (f"_segmented_{segment_len}" if segment_len is not None else ""),
+                    + (f"_segmented_{segment_len}" if segment_len is not None else "")
+                    + ({gdn.GDN_COLUMNS_WHOLE: "_whole_columns",
+                        gdn.GDN_COLUMNS_SPLIT: "_split_columns"}.get(columns, "")),
         "arith": PREFILL_ARITH if esz == 2 else "fp32 arithmetic (vector kernel)",
         "tokens": tokens, "heads": H, "chunk": w.chunk,
         "seconds": t, "tokens_per_s": tokens / t,
@@ -639,12 +642,20 @@ def main():
                     "prefill_short_verify",
                     source_digest("gdn_prefill_short.hip", "gdn_mfma.hpp"))
             if w.name == "long_prefill":
-                # the same workload with each sequence cut into 16 segments
-                rs = bench_prefill(torch, gdn, w, args.prefill_iters, 2, segment_len=256)
-                log(f"prefill {rs['workload']}: {rs['tokens_per_s']:.3e} tok/s, "
-                    f"{rs['seconds']*1e3:.3f} ms, MFMA {100*rs['mfma_frac']:.1f}%, "
-                    f"HBM {100*rs['hbm_frac']:.1f}%")
-                pre[rs["workload"]] = rs
+                # the default splits each (sequence, head) over two workgroups of
+                # 64 value columns (16 units on 256 CUs); the unsplit form beside
+                # it, then the segmented form
+                rw = bench_prefill(torch, gdn, w, args.prefill_iters, 2,
+                                   columns=gdn.GDN_COLUMNS_WHOLE)
+                log(f"prefill {rw['workload']}: {rw['tokens_per_s']:.3e} tok/s, "
+                    f"{rw['seconds']*1e3:.3f} ms")
+                pre[rw["workload"]] = rw
+                for seg_len in (256, 512):
+                    rs = bench_prefill(torch, gdn, w, args.prefill_iters, 2, segment_len=seg_len)
+                    log(f"prefill {rs['workload']}: {rs['tokens_per_s']:.3e} tok/s, "
+                        f"{rs['seconds']*1e3:.3f} ms, MFMA {100*rs['mfma_frac']:.1f}%, "
+                        f"HBM {100*rs['hbm_frac']:.1f}%")
+                    pre[rs["workload"]] = rs
                 # a packed serving batch: one 16384-token prompt among 31 of 256
                 # tokens (not one of the specified workloads: it shows where the
                 # packed segmented form pays)

@@ -78,6 +78,14 @@ typedef enum {
     GDN_INVERSE_DOUBLING = 2        /* exact block doubling on the matrix cores */
 } gdn_inverse;
 
+/* How the chunk-64 matrix-core prompt kernel spreads one (sequence, head)
+ * over workgroups (see gdn_chunk_prefill_ex). */
+typedef enum {
+    GDN_COLUMNS_DEFAULT = 0,        /* the library's choice */
+    GDN_COLUMNS_WHOLE = 1,          /* one workgroup per (sequence, head) */
+    GDN_COLUMNS_SPLIT = 2           /* two workgroups of 64 value columns each */
+} gdn_columns;
+
 /* Library ABI version (increments on any signature change). */
 int gdn_version(void);
 
@@ -145,19 +153,33 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
  * (GDN_INVERSE_DOUBLING) and applies the block structure above it by block
  * forward substitution.  GDN_INVERSE_SUBSTITUTION forms the diagonal blocks by
  * fp32 back substitution instead.  Both reach the same result up to rounding.
- * The choice applies to bf16 inputs at chunk 64 (the matrix-core kernel), and
- * naming it keeps such calls on that kernel even for batches of short
- * sequences; the other configurations substitute column by column and ignore
- * it.
+ *
+ * It also chooses how a (sequence, head) is spread over workgroups.  In that
+ * statement of the chunk form every value column j of O, D and the state
+ * depends only on column j of V and of S0, so the 128 columns can be walked
+ * by separate workgroups that each repeat the key-side work (the Gram tiles,
+ * the triangular inverse).  GDN_COLUMNS_SPLIT runs two workgroups of 64
+ * columns per (sequence, head): each walks the chunks with half the
+ * state-side work, which shortens the serial chain of a call that leaves CUs
+ * idle (few sequences and heads) at the price of repeating the key-side work.
+ * GDN_COLUMNS_DEFAULT splits exactly when the split launch still fits the
+ * device's CUs at once (2 B_or_N H <= CUs); gdn_chunk_prefill takes that
+ * default.
+ *
+ * Both choices apply to bf16 inputs at chunk 64 (the matrix-core kernel), and
+ * naming either (anything but a DEFAULT) keeps such calls on that kernel even
+ * for batches of short sequences; the other configurations substitute column
+ * by column and ignore them.
  *
  *   inverse     a gdn_inverse value (else GDN_ERR_UNSUPPORTED).
+ *   columns     a gdn_columns value (else GDN_ERR_UNSUPPORTED).
  *   Every other argument: as for gdn_chunk_prefill.
  */
 int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dtype,
                          const float *g, const float *beta, const float *S0,
                          const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
-                         int64_t dk, int64_t dv, int64_t chunk, int inverse, void *O,
-                         float *S_T, void *stream);
+                         int64_t dk, int64_t dv, int64_t chunk, int inverse, int columns,
+                         void *O, float *S_T, void *stream);
 
 /*
  * gdn_chunk_prefill_segmented -- gdn_chunk_prefill with each sequence cut into

@@ -26,6 +26,7 @@ EXPORTED = ("gdn_version", "gdn_status_string", "gdn_chunk_prefill", "gdn_chunk_
             "gdn_chunk_prefill_gated", "gdn_prefill_states", "gdn_preop", "gdn_decode_step",
             "gdn_decode_step_ex", "gdn_decode_step_preop", "gdn_chunk_prefill_preop")
 GDN_INVERSE_DEFAULT, GDN_INVERSE_SUBSTITUTION, GDN_INVERSE_DOUBLING = 0, 1, 2
+GDN_COLUMNS_DEFAULT, GDN_COLUMNS_WHOLE, GDN_COLUMNS_SPLIT = 0, 1, 2
 GDN_STATE_CACHED, GDN_STATE_STREAMING = 0, 1
 
 _lib = None
@@ -61,7 +62,8 @@ def load_library(path: Optional[str] = None):
                               i64, i64, i64, ctypes.c_float, vp, vp, vp, vp, vp, vp]
     lib.gdn_preop.restype = ctypes.c_int
     lib.gdn_chunk_prefill_ex.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64, i64,
-                                         i64, i64, i64, i64, ctypes.c_int, vp, vp, vp]
+                                         i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, vp,
+                                         vp]
     lib.gdn_chunk_prefill_ex.restype = ctypes.c_int
     lib.gdn_chunk_prefill_segmented.argtypes = [vp, vp, vp, ctypes.c_int, vp, vp, vp, vp, i64,
                                                 i64, i64, i64, i64, i64, i64, vp, i64, vp, vp,
@@ -141,13 +143,15 @@ def _stream(stream) -> ctypes.c_void_p:
 
 
 def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
-                      O=None, S_T=None, stream=None, inverse=None, out_dtype=None):
+                      O=None, S_T=None, stream=None, inverse=None, columns=None,
+                      out_dtype=None):
     """Chunkwise-parallel prompt form over whole sequences.
 
     q, k, v: [B, T, H, 128] (bf16 or fp32; packed batches B = 1);
     g, beta: [B, T, H] fp32; S0: [N, H, 128, 128] fp32 or None;
     cu_seqlens: int32 [N+1] device offsets or None.
-    inverse: None (gdn_chunk_prefill) or a GDN_INVERSE_* value
+    inverse, columns: both None (gdn_chunk_prefill), or GDN_INVERSE_* and
+    GDN_COLUMNS_* values, None standing for the DEFAULT one
     (gdn_chunk_prefill_ex).
     out_dtype: O's dtype; q's by default, or torch.float32 for bf16 inputs
     (GDN_BF16_F32_OUT).
@@ -180,10 +184,12 @@ def gdn_chunk_prefill(q, k, v, g, beta, S0=None, cu_seqlens=None, chunk=64, *,
             _ptr(S0, torch.float32, "S0"), _ptr(cu_seqlens, torch.int32, "cu_seqlens"),
             N, T, H, dk, dv, int(chunk))
     out = (_ptr(O, name="O"), _ptr(S_T, torch.float32, "S_T"), _stream(stream))
-    if inverse is None:
+    if inverse is None and columns is None:
         st = load_library().gdn_chunk_prefill(*args, *out)
     else:
-        st = load_library().gdn_chunk_prefill_ex(*args, int(inverse), *out)
+        st = load_library().gdn_chunk_prefill_ex(
+            *args, GDN_INVERSE_DEFAULT if inverse is None else int(inverse),
+            GDN_COLUMNS_DEFAULT if columns is None else int(columns), *out)
     _check(st)
     return O, S_T
 

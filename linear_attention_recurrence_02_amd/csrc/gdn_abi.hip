@@ -340,10 +340,13 @@ int gdn_chunk_prefill(const void *q, const void *k, const void *v, int io_dtype,
 int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dtype,
                          const float *g, const float *beta, const float *S0,
                          const int32_t *cu_seqlens, int64_t B_or_N, int64_t T, int64_t H,
-                         int64_t dk, int64_t dv, int64_t chunk, int inverse, void *O,
-                         float *S_T, void *stream) {
+                         int64_t dk, int64_t dv, int64_t chunk, int inverse, int columns,
+                         void *O, float *S_T, void *stream) {
     if (inverse != GDN_INVERSE_DEFAULT && inverse != GDN_INVERSE_SUBSTITUTION &&
         inverse != GDN_INVERSE_DOUBLING)
+        return GDN_ERR_UNSUPPORTED;
+    if (columns != GDN_COLUMNS_DEFAULT && columns != GDN_COLUMNS_WHOLE &&
+        columns != GDN_COLUMNS_SPLIT)
         return GDN_ERR_UNSUPPORTED;
     gdn::PrefillArgs a{};
     int64_t tok_bytes = 0;
@@ -354,6 +357,10 @@ int gdn_chunk_prefill_ex(const void *q, const void *k, const void *v, int io_dty
     if (inverse != GDN_INVERSE_DEFAULT) {
         a.inverse = inverse == GDN_INVERSE_DOUBLING ? gdn::kInverseDoubling
                                                     : gdn::kInverseSubstitution;
+        a.short_ok = false;
+    }
+    if (columns != GDN_COLUMNS_DEFAULT) {
+        a.columns = columns == GDN_COLUMNS_SPLIT ? gdn::kColumnsSplit : gdn::kColumnsWhole;
         a.short_ok = false;
     }
     return launch_prefill(a, stream);

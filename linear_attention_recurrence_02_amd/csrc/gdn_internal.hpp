@@ -14,6 +14,10 @@ constexpr int kInverseDefault = 0;        // the kernel's own choice
 constexpr int kInverseSubstitution = 1;   // back substitution on the vector ALUs
 constexpr int kInverseDoubling = 2;       // block doubling on the matrix cores
 
+constexpr int kColumnsDefault = 0;        // the launch's own choice
+constexpr int kColumnsWhole = 1;          // one workgroup per (sequence, head)
+constexpr int kColumnsSplit = 2;          // two, of 64 value columns each
+
 // A validated prompt-form call.  Token rows are counted in units of H heads:
 // the element (row r, head h, dim i) of q/k/v/O sits at ((r * H) + h) * 128 + i.
 struct PrefillArgs {
@@ -39,6 +43,9 @@ struct PrefillArgs {
     // How the matrix-core kernel forms the diagonal 16 x 16 blocks of
     // (I + N)^-1 (the vector kernel always substitutes column by column).
     int inverse = kInverseDefault;
+    // Whether the matrix-core kernel splits each unit's value columns over two
+    // workgroups (the other kernels ignore it).
+    int columns = kColumnsDefault;
     // Whether a batch of short sequences may take the 16-token kernel (off
     // when the caller names the matrix-core kernel's inverse method).
     bool short_ok = true;

@@ -693,26 +693,29 @@ struct Producer {
     }
 };
 
-// Columns [32p, 32p+32) of W and of U for the chunk in buffer set nb, block by
-// block (run by consumer wave p); stores -W (dk-major) in LDS and returns U in
-// the result-tile layout, Uo[i][cc] = U rows 16i + 4q + e, column 32p + 16cc + r16,
-// at the wave's scale for the chunk.  That scale is chosen here, from the
+// Columns [32p, 32p+32) of W and columns [vcol, vcol + 16 NCC) of U for the
+// chunk in buffer set nb, block by block (run by consumer wave p); stores -W
+// (dk-major) in LDS and returns U in the result-tile layout, Uo[i][cc] = U rows
+// 16i + 4q + e, column vcol + 16cc + r16, at the wave's scale for the chunk.
+// Every wave forms its 32 columns of W whatever NCC is: the products W S of
+// each wave run over all 128 of them.  That scale is chosen here, from the
 // largest |X| of the direct terms X_i = P'_i V_i (bf16 products, unscaled) and
 // `ms`, the lane's largest |S| at the current scale 2^sc (S being the state
 // that enters the chunk); S is rescaled when the scale changes.  W's chain is
 // W_i = P_i K_i - sum_j M_ij W_j with P and M split and W single; U's chain
 // U_i = X_i - sum_j M_ij U_j with M and U split.
-__device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2], f32x4 (*S)[2], int &sc,
-                                        float ms) {
+template <int NCC>
+__device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, int vcol, f32x4 (*Uo)[NCC],
+                                        f32x4 (*S)[NCC], int &sc, float ms) {
     const int lane = fresh_lane_id(), r16 = lane & 15, q = lane >> 4;
     const int trk = (4 * q + (r16 >> 2)) * KS + ((4 * (r16 & 3)) ^ ksw(4 * q));
     const f16 *kb = sm.K[nb] + trk + 32 * p;
-    const f16 *vb = reinterpret_cast<const f16 *>(sm.V) + trk + 32 * p;
+    const f16 *vb = reinterpret_cast<const f16 *>(sm.V) + trk + vcol;
     const int co = r16 * BS + 4 * q;
     // Everything but the previous blocks' W and U is known before the
     // substitution starts: read it all first.
     f16x4 kx[4][2];
-    bf16x4 vx[4][2];
+    bf16x4 vx[4][NCC];
     f16x8 pw[4];
     bf16x8 pu[4];
     h4x2 mm[6];
@@ -721,7 +724,7 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2],
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             kx[i][cc] = rd_tr(kb + 16 * i * KS + 16 * cc);
-            vx[i][cc] = __builtin_bit_cast(bf16x4, rd_tr(vb + 16 * i * KS + 16 * cc));
+            if (cc < NCC) vx[i][cc] = __builtin_bit_cast(bf16x4, rd_tr(vb + 16 * i * KS + 16 * cc));
         }
         pw[i] = cat(rd4(&sm.P[0][i][co]), rd4(&sm.P[1][i][co]));
         pu[i] = catb(*reinterpret_cast<const bf16x4 *>(&sm.Pv[0][i][co]),
@@ -735,7 +738,7 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2],
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int cc = 0; cc < NCC; ++cc) {
             Uo[i][cc] = mfma_bf(pu[i], catb(vx[i][cc], vx[i][cc]), zero4());
             mx = absmax4(Uo[i][cc], mx);
         }
@@ -743,22 +746,21 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2],
     if (nx != sc) {
         const float f = pow2i(nx - sc);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            S[i][0] *= f;
-            S[i][1] *= f;
-        }
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int cc = 0; cc < NCC; ++cc) S[i][cc] *= f;
         sc = nx;
     }
     const float up = pow2i(sc);
     f16x4 Wr[3][2];
-    h4x2 Ur[3][2];
+    h4x2 Ur[3][NCC];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        f32x4 aw[2], au[2];
+        f32x4 aw[2], au[NCC];
 #pragma unroll
         for (int cc = 0; cc < 2; ++cc) {
             aw[cc] = mfma(pw[i], cat(kx[i][cc], kx[i][cc]), zero4());   // P_i K_i
-            au[cc] = Uo[i][cc] * up;
+            if (cc < NCC) au[cc] = Uo[i][cc] * up;
         }
         // - M_ij W_j and - M_ij U_j (M is stored negated): the hi products ...
 #pragma unroll
@@ -767,12 +769,12 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2],
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 aw[cc] = mfma(cat(mj.hi, mj.lo), cat(Wr[j][cc], Wr[j][cc]), aw[cc]);
-                au[cc] = mfma(cat(mj.hi, mj.lo), cat(Ur[j][cc].hi, Ur[j][cc].hi), au[cc]);
+                if (cc < NCC) au[cc] = mfma(cat(mj.hi, mj.lo), cat(Ur[j][cc].hi, Ur[j][cc].hi), au[cc]);
             }
         }
         // ... and M U_lo: M_hi of two blocks j to a product, or (hi + lo) of one
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) {
+        for (int cc = 0; cc < NCC; ++cc) {
             if (i == 1) {
                 au[cc] = mfma(cat(mm[oblk(1, 0)].hi, mm[oblk(1, 0)].lo), cat(Ur[0][cc].lo, Ur[0][cc].lo), au[cc]);
             } else if (i == 2) {
@@ -787,15 +789,15 @@ __device__ __forceinline__ void wu_step(Smem &sm, int nb, int p, f32x4 (*Uo)[2],
             const f16x4 w16 = h4(aw[cc]);
             if (i < 3) {
                 Wr[i < 3 ? i : 0][cc] = w16;
-                Ur[i < 3 ? i : 0][cc] = split_h4(au[cc]);
+                if (cc < NCC) Ur[i < 3 ? i : 0][cc] = split_h4(au[cc]);
             }
             *reinterpret_cast<f16x4 *>(&sm.W[(32 * p + 16 * cc + r16) * WS + 16 * i + ((4 * q) ^ wsw(r16))]) = neg(w16);
-            Uo[i][cc] = au[cc];
+            if (cc < NCC) Uo[i][cc] = au[cc];
         }
     }
 }
 
-template <bool kGated, bool kDoubling, bool kRank, typename OutT, bool kPreop = false>
+template <bool kGated, bool kDoubling, bool kRank, typename OutT, bool kPreop = false, int NCC = 2>
 __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     const bf16 *__restrict__ q, const bf16 *__restrict__ k, const bf16 *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta,
@@ -803,6 +805,13 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     int64_t H, OutT *__restrict__ O, float *__restrict__ S_T, const bf16 *__restrict__ z,
     const float *__restrict__ norm_w, float eps, const float *__restrict__ conv_w,
     const bf16 *__restrict__ fifo, float ceps) {
+    // NCC = 1: the value columns of each (sequence, head) are split over two
+    // workgroups of 64 columns (each consumer wave then owns 16 of them), for
+    // launches that would leave most CUs idle.  The columns of S, U, D and O
+    // are exactly independent; the producers' work (staging, Gram tiles,
+    // inverse) and W are repeated in both workgroups.
+    static_assert(NCC == 1 || NCC == 2, "value tiles per consumer wave");
+    static_assert(NCC == 2 || (!kGated && !kRank && !kPreop), "split forms");
     __shared__ Smem sm;
 
     const int tid = threadIdx.x;
@@ -818,7 +827,23 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     // A packed batch of sequences of mixed lengths is walked longest first
     // (in the instantiation the launch picks for it), so that the long ones do
     // not start last and set the end of the launch.
-    int64_t seq = blockIdx.x / H;
+    // Workgroup -> unit (and column half).  The two halves of a unit read the
+    // same key and query rows: when the unit count is a multiple of 8 they are
+    // workgroups b and b + 8, which the dispatcher's round robin over the 8
+    // XCDs puts on the same XCD (and L2).
+    int64_t bid = blockIdx.x;
+    int half = 0;
+    if constexpr (NCC == 1) {
+        const uint32_t b = blockIdx.x, units = gridDim.x >> 1;
+        if ((units & 7u) == 0) {
+            half = (b >> 3) & 1;
+            bid = ((b >> 4) << 3) | (b & 7u);
+        } else {
+            half = b & 1;
+            bid = b >> 1;
+        }
+    }
+    int64_t seq = bid / H;
     if constexpr (kRank) {
         // the lengths are staged in the first key buffer, which the producers
         // first write after the barrier below
@@ -829,7 +854,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         __syncthreads();
         seq = pick;
     }
-    const int64_t unit = seq * H + blockIdx.x % H;
+    const int64_t unit = seq * H + bid % H;
     Unit u;
     u.q = q; u.k = k; u.v = v; u.g = g; u.beta = beta;
     u.H = H;
@@ -938,21 +963,24 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     }
 
     // ======================= consumer waves =======================
-    // S[i][c] holds state rows 16i+4q+e, column 32w+16c+r16, at scale 2^sc.
-    f32x4 S[8][2];
+    // S[i][c] holds state rows 16i+4q+e, column col0+16c+r16, at scale 2^sc.
+    const int col0 = NCC == 2 ? 32 * w : 64 * half + 16 * w;
+    f32x4 S[8][NCC];
     int sc = 0;
     if (S0) {
         const float *S0u = S0 + unit * (D * D);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < NCC; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    S[i][c][e] = S0u[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16];
+                    S[i][c][e] = S0u[(16 * i + 4 * qd + e) * D + col0 + 16 * c + r16];
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) S[i][0] = S[i][1] = zero4();
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int c = 0; c < NCC; ++c) S[i][c] = zero4();
     }
     float *STu = S_T + unit * (D * D);
     auto store_state = [&]() {
@@ -960,10 +988,10 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int c = 0; c < 2; ++c)
+            for (int c = 0; c < NCC; ++c)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    STu[(16 * i + 4 * qd + e) * D + 32 * w + 16 * c + r16] = S[i][c][e] * un;
+                    STu[(16 * i + 4 * qd + e) * D + col0 + 16 * c + r16] = S[i][c][e] * un;
     };
     if (nch == 0) {
         store_state();
@@ -973,7 +1001,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     auto lane_max_s = [&]() {
         float m = 0.f;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) m = absmax4(S[i][1], absmax4(S[i][0], m));
+        for (int i = 0; i < 8; ++i) m = absmax4(S[i][NCC - 1], absmax4(S[i][0], m));
         return m;
     };
     if (kGated && tid < D) sm.NW[tid] = norm_w[tid];
@@ -983,8 +1011,8 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
     // W/U step of chunk 0
     __syncthreads();
     __syncthreads();
-    f32x4 Ur[4][2];
-    wu_step(sm, 0, w, Ur, S, sc, lane_max_s());
+    f32x4 Ur[4][NCC];
+    wu_step<NCC>(sm, 0, w, col0, Ur, S, sc, lane_max_s());
     __syncthreads();
 
     const uint32_t HD = static_cast<uint32_t>(H) * D;
@@ -996,7 +1024,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 
         // ======== phase 1: D = U - W S; S <- exp(G_C) S + K^T diag(exp(G_C - G)) D ========
         // (all at the wave's scale: U and S carry it, so D does)
-        f16x8 Sh[4][2], Dh[2][2], Dl[2][2];
+        f16x8 Sh[4][NCC], Dh[2][NCC], Dl[2][NCC];
         {
             const f16 *Wc = sm.W + trw;
             auto ld_w = [&](int s, f16x8 *dst) {
@@ -1016,15 +1044,15 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             };
             f16x8 wa[2][4];
             ld_w(0, wa[0]);
-            f32x4 Dt[4][2];
+            f32x4 Dt[4][NCC];
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) Dt[m][cc] = Ur[m][cc];
+                for (int cc = 0; cc < NCC; ++cc) Dt[m][cc] = Ur[m][cc];
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) Sh[s][cc] = cat(h4(S[2 * s][cc]), h4(S[2 * s + 1][cc]));
+                for (int cc = 0; cc < NCC; ++cc) Sh[s][cc] = cat(h4(S[2 * s][cc]), h4(S[2 * s + 1][cc]));
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 if (s < 3) ld_w(s + 1, wa[(s + 1) & 1]);
@@ -1032,20 +1060,20 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) Dt[m][cc] = mfma(wa[s & 1][m], Sh[s][cc], Dt[m][cc]);
+                    for (int cc = 0; cc < NCC; ++cc) Dt[m][cc] = mfma(wa[s & 1][m], Sh[s][cc], Dt[m][cc]);
             }
             f16x8 ka[2][4];
             ld_k(0, ka[0]);
             ld_k(1, ka[0] + 2);
             fence();
-            f16x8 Dp[2][2], Dq[2][2];   // the decayed D, hi and lo
+            f16x8 Dp[2][NCC], Dq[2][NCC];   // the decayed D, hi and lo
             const float *EC = sm.EC[cur];
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&EC[32 * s2 + 4 * qd]);
                 const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&EC[32 * s2 + 16 + 4 * qd]);
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) {
+                for (int cc = 0; cc < NCC; ++cc) {
                     const h4x2 d0 = split_h4(Dt[2 * s2][cc]), d1 = split_h4(Dt[2 * s2 + 1][cc]);
                     Dh[s2][cc] = cat(d0.hi, d1.hi);
                     Dl[s2][cc] = cat(d0.lo, d1.lo);
@@ -1058,7 +1086,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int cc = 0; cc < 2; ++cc) S[i][cc] *= eC;
+                for (int cc = 0; cc < NCC; ++cc) S[i][cc] *= eC;
 #pragma unroll
             for (int ib = 0; ib < 4; ++ib) {
                 if (ib < 3) {
@@ -1071,7 +1099,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
                     for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-                        for (int cc = 0; cc < 2; ++cc) {
+                        for (int cc = 0; cc < NCC; ++cc) {
                             S[2 * ib + ii][cc] = mfma(ka[ib & 1][2 * ii + s2], Dp[s2][cc], S[2 * ib + ii][cc]);
                             S[2 * ib + ii][cc] = mfma(ka[ib & 1][2 * ii + s2], Dq[s2][cc], S[2 * ib + ii][cc]);
                         }
@@ -1108,27 +1136,29 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         // reload from scratch would wait for every store the wave has in
         // flight, the output stores included.
         char *const obase = reinterpret_cast<char *>(O + (u.row0(c) * H + u.h) * D);
-        const uint32_t olane = (static_cast<uint32_t>(r16) * HD + 32 * w + 4 * qd) * sizeof(OutT);
+        const uint32_t olane = (static_cast<uint32_t>(r16) * HD + col0 + 4 * qd) * sizeof(OutT);
         auto orow = [&](int m, int cc) {
             return obase + static_cast<uint32_t>(16 * m) * HD * sizeof(OutT) + olane + 16 * cc * sizeof(OutT);
         };
-        f32x4 Ot[4][2];           // Ot[m][cc]: O[16m + r16][32w + 16cc + 4q + e]
+        f32x4 Ot[4][NCC];         // Ot[m][cc]: O[16m + r16][col0 + 16cc + 4q + e]
         {
-            bf16x4 zr[4][2];
+            bf16x4 zr[4][NCC];
             if constexpr (kGated) {
                 const char *zc = reinterpret_cast<const char *>(z + (u.row0(c) * H + u.h) * D);
-                const uint32_t zlane = (32 * w + 4 * qd) * sizeof(bf16);
+                const uint32_t zlane = (col0 + 4 * qd) * sizeof(bf16);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     const int t = 16 * m + r16;
                     const uint32_t off = static_cast<uint32_t>(t < cnv ? t : 0) * HD * sizeof(bf16) + zlane;
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc)
+                    for (int cc = 0; cc < NCC; ++cc)
                         zr[m][cc] = *reinterpret_cast<const bf16x4 *>(zc + off + 16 * cc * sizeof(bf16));
                 }
             }
 #pragma unroll
-            for (int m = 0; m < 4; ++m) Ot[m][0] = Ot[m][1] = zero4();
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int cc = 0; cc < NCC; ++cc) Ot[m][cc] = zero4();
             const f16 *Qc = sm.Q[cur] + r16 * QS + 4 * qd;
             auto ld_q = [&](int s, f16x8 *dst) {
 #pragma unroll
@@ -1146,13 +1176,13 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) Ot[m][cc] = mfma(Sh[s][cc], qb[s & 1][m], Ot[m][cc]);
+                    for (int cc = 0; cc < NCC; ++cc) Ot[m][cc] = mfma(Sh[s][cc], qb[s & 1][m], Ot[m][cc]);
             }
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
                 const float eg = sm.EG[cur][16 * m + r16];
-                Ot[m][0] *= eg;
-                Ot[m][1] *= eg;
+#pragma unroll
+                for (int cc = 0; cc < NCC; ++cc) Ot[m][cc] *= eg;
             }
             {
                 const f16 *Ah = sm.A[0] + r16 * AS + 4 * qd, *Al = sm.A[1] + r16 * AS + 4 * qd;
@@ -1163,7 +1193,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                         const f16x8 ah = cat(rd4(Ah + 16 * m * AS + 32 * s2), rd4(Ah + 16 * m * AS + 32 * s2 + 16));
                         const f16x8 al = cat(rd4(Al + 16 * m * AS + 32 * s2), rd4(Al + 16 * m * AS + 32 * s2 + 16));
 #pragma unroll
-                        for (int cc = 0; cc < 2; ++cc) {
+                        for (int cc = 0; cc < NCC; ++cc) {
                             Ot[m][cc] = mfma(Dh[s2][cc], ah, Ot[m][cc]);
                             Ot[m][cc] = mfma(Dl[s2][cc], ah, Ot[m][cc]);
                             Ot[m][cc] = mfma(Dh[s2][cc], al, Ot[m][cc]);
@@ -1173,19 +1203,18 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
             {
                 const float un = pow2i(-sc);
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    Ot[m][0] *= un;
-                    Ot[m][1] *= un;
-                }
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int cc = 0; cc < NCC; ++cc) Ot[m][cc] *= un;
             }
             if constexpr (kGated) {
-                const f32x4 nw0 = *reinterpret_cast<const f32x4 *>(&sm.NW[32 * w + 4 * qd]);
-                const f32x4 nw1 = *reinterpret_cast<const f32x4 *>(&sm.NW[32 * w + 16 + 4 * qd]);
+                const f32x4 nw0 = *reinterpret_cast<const f32x4 *>(&sm.NW[col0 + 4 * qd]);
+                const f32x4 nw1 = *reinterpret_cast<const f32x4 *>(&sm.NW[col0 + 16 + 4 * qd]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
                     float ss = 0.f;
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc)
+                    for (int cc = 0; cc < NCC; ++cc)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) ss += Ot[m][cc][e] * Ot[m][cc][e];
                     // lanes r16 + 16 q of the four lane groups hold one row
@@ -1193,7 +1222,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     ss += __shfl_xor(ss, 32);
                     if (qd == 0) sm.NP[16 * m + r16][w] = ss;
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
+                    for (int cc = 0; cc < NCC; ++cc) {
                         const f32x4 zf = __builtin_convertvector(zr[m][cc], f32x4);
                         const f32x4 nw = cc ? nw1 : nw0;
 #pragma unroll
@@ -1230,7 +1259,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     const float rs = __builtin_amdgcn_rsqf(ms + eps);
                     if (rr < cnv - 16 * m) {
 #pragma unroll
-                        for (int cc = 0; cc < 2; ++cc)
+                        for (int cc = 0; cc < NCC; ++cc)
                             *reinterpret_cast<bf16x4 *>(orow(m, cc)) = __builtin_convertvector(Ot[m][cc] * rs, bf16x4);
                     }
                 }
@@ -1240,7 +1269,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
                     const int t = 16 * m + r16;
                     if (O && t < cnv) {
 #pragma unroll
-                        for (int cc = 0; cc < 2; ++cc) {
+                        for (int cc = 0; cc < NCC; ++cc) {
                             if constexpr (sizeof(OutT) == 4)
                                 *reinterpret_cast<f32x4 *>(orow(m, cc)) = Ot[m][cc];
                             else
@@ -1253,7 +1282,7 @@ __global__ __launch_bounds__(512) void prefill_mfma_kernel(
         if constexpr (!kGated) msl = lane_max_s();
         __syncthreads();
         // ======== phase 3: W and U of the next chunk ========
-        if (c + 1 < nch) wu_step(sm, (c + 1) & 1, w, Ur, S, sc, msl);
+        if (c + 1 < nch) wu_step<NCC>(sm, (c + 1) & 1, w, col0, Ur, S, sc, msl);
         __syncthreads();
     }
     store_state();
@@ -1274,13 +1303,27 @@ bool rank_longest_first_pays(const PrefillArgs &a) {
     return cus > 0 && a.N * a.H <= 4 * static_cast<int64_t>(cus);
 }
 
+// Whether the value columns of each (sequence, head) should be split over two
+// workgroups: when even then the launch's workgroups all run at once (two per
+// unit on at most the device's CUs), each unit's chain of chunks then runs on
+// two CUs with half the consumer work per chunk.  The gated norm needs a whole
+// output row in one workgroup, and the pre-operations would be repeated, so
+// those forms are never split.
+bool split_columns(const PrefillArgs &a) {
+    if (a.z || a.conv_w || 2 * a.N * a.H > int64_t(0x7fffffff)) return false;
+    if (a.columns == kColumnsSplit) return true;
+    if (a.columns == kColumnsWhole) return false;
+    const int cus = compute_units();
+    return cus > 0 && 2 * a.N * a.H <= static_cast<int64_t>(cus);
+}
+
 template <typename OutT>
 void launch_typed(void (*kern)(const bf16 *, const bf16 *, const bf16 *, const float *, const float *,
                                const float *, const int32_t *, int64_t, int64_t, int64_t, OutT *,
                                float *, const bf16 *, const float *, float, const float *,
                                const bf16 *, float),
-                  const PrefillArgs &a, hipStream_t stream) {
-    const dim3 grid(static_cast<unsigned>(a.N * a.H)), block(512);
+                  const PrefillArgs &a, hipStream_t stream, int per_unit = 1) {
+    const dim3 grid(static_cast<unsigned>(a.N * a.H * per_unit)), block(512);
     kern<<<grid, block, 0, stream>>>(
         static_cast<const bf16 *>(a.q), static_cast<const bf16 *>(a.k),
         static_cast<const bf16 *>(a.v), a.g, a.beta, a.S0, a.cu_seqlens, a.N, a.T, a.H,
@@ -1297,7 +1340,16 @@ hipError_t launch_prefill_mfma(const PrefillArgs &a, hipStream_t stream) {
     // period, and substitution there measured 4.0 ms against 2.2 ms on
     // 8 x 16384 x 32.)
     const bool dbl = a.inverse == kInverseDoubling || (a.inverse == kInverseDefault && kDefaultDoubling);
-    if (a.conv_w)   // the pre-operations fused into the chunk load
+    if (split_columns(a)) {
+        if (a.out_f32)
+            launch_typed<float>(dbl ? prefill_mfma_kernel<false, true, false, float, false, 1>
+                                    : prefill_mfma_kernel<false, false, false, float, false, 1>,
+                                a, stream, 2);
+        else
+            launch_typed<bf16>(dbl ? prefill_mfma_kernel<false, true, false, bf16, false, 1>
+                                   : prefill_mfma_kernel<false, false, false, bf16, false, 1>,
+                               a, stream, 2);
+    } else if (a.conv_w)   // the pre-operations fused into the chunk load
         launch_typed<bf16>(rank ? prefill_mfma_kernel<false, true, true, bf16, true>
                                 : prefill_mfma_kernel<false, true, false, bf16, true>, a, stream);
     else if (a.out_f32)

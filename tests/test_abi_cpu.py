@@ -112,7 +112,7 @@ def test_prefill_states_validation(lib):
 
 
 def test_prefill_ex_validation(lib):
-    def ex(inverse, **kw):
+    def ex(inverse, columns=binding.GDN_COLUMNS_DEFAULT, **kw):
         args = dict(q=A, k=A + 64 * MB, v=A + 128 * MB, dtype=1, g=A + 192 * MB,
                     beta=A + 200 * MB, S0=A + 256 * MB, cu=None, N=2, T=64, H=2, dk=128,
                     dv=128, chunk=64, O=A + 512 * MB, S_T=A + 768 * MB)
@@ -120,14 +120,20 @@ def test_prefill_ex_validation(lib):
         a = args
         return lib.gdn_chunk_prefill_ex(a["q"], a["k"], a["v"], a["dtype"], a["g"], a["beta"],
                                         a["S0"], a["cu"], a["N"], a["T"], a["H"], a["dk"],
-                                        a["dv"], a["chunk"], inverse, a["O"], a["S_T"], None)
+                                        a["dv"], a["chunk"], inverse, columns, a["O"], a["S_T"],
+                                        None)
     assert ex(3) == binding.GDN_ERR_UNSUPPORTED
     assert ex(-1) == binding.GDN_ERR_UNSUPPORTED
+    assert ex(binding.GDN_INVERSE_DEFAULT, 3) == binding.GDN_ERR_UNSUPPORTED
+    assert ex(binding.GDN_INVERSE_DEFAULT, -1) == binding.GDN_ERR_UNSUPPORTED
     assert ex(binding.GDN_INVERSE_DOUBLING, q=None) == binding.GDN_ERR_INVALID_ARG
     assert ex(binding.GDN_INVERSE_SUBSTITUTION, O=A) == binding.GDN_ERR_ALIAS
+    assert ex(binding.GDN_INVERSE_DEFAULT, binding.GDN_COLUMNS_SPLIT, O=A) == binding.GDN_ERR_ALIAS
     for inv in (binding.GDN_INVERSE_DEFAULT, binding.GDN_INVERSE_SUBSTITUTION,
                 binding.GDN_INVERSE_DOUBLING):
-        assert ex(inv, N=0) == binding.GDN_OK
+        for col in (binding.GDN_COLUMNS_DEFAULT, binding.GDN_COLUMNS_WHOLE,
+                    binding.GDN_COLUMNS_SPLIT):
+            assert ex(inv, col, N=0) == binding.GDN_OK
 
 
 def test_prefill_segmented_validation(lib):

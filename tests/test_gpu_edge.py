@@ -30,7 +30,7 @@ import torch
 import oracle
 from linear_attention_recurrence_02_amd import inputs
 from linear_attention_recurrence_02_amd.binding import (
-    GDN_INVERSE_DOUBLING, GDN_INVERSE_SUBSTITUTION, gdn_chunk_prefill,
+    GDN_COLUMNS_WHOLE, GDN_INVERSE_DOUBLING, GDN_INVERSE_SUBSTITUTION, gdn_chunk_prefill,
     gdn_chunk_prefill_gated, gdn_chunk_prefill_segmented, gdn_decode_step,
     gdn_prefill_states)
 from metrics import (TOL_BF16, bf16_half_ulp, bf16_output_ok, f64, gated_output_ok, spans_of,
@@ -127,6 +127,11 @@ def run_path_(path, w, out_dtype=None):
     if path == "chunk64_substitution":
         return gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, 64,
                                  inverse=GDN_INVERSE_SUBSTITUTION, out_dtype=out_dtype)
+    if path == "chunk64_whole":
+        # this batch's 8 units are split over two workgroups each by default;
+        # the unsplit form on the same cases
+        return gdn_chunk_prefill(w.q, w.k, w.v, w.g, w.beta, w.S0, w.cu_seqlens, 64,
+                                 columns=GDN_COLUMNS_WHOLE, out_dtype=out_dtype)
     if path == "short16":
         # the same sequences followed by empty ones, so that the batch averages at
         # most 16 rows per sequence and takes the 16-token kernel
@@ -149,9 +154,9 @@ def run_path_(path, w, out_dtype=None):
     raise ValueError(path)
 
 
-PATHS = ("chunk64_doubling", "chunk64_substitution", "short16", "vector32", "segmented",
-         "token_states", "chunk64_doubling_f32out", "chunk64_substitution_f32out",
-         "short16_f32out", "vector32_f32out")
+PATHS = ("chunk64_doubling", "chunk64_substitution", "chunk64_whole", "short16", "vector32",
+         "segmented", "token_states", "chunk64_doubling_f32out", "chunk64_substitution_f32out",
+         "chunk64_whole_f32out", "short16_f32out", "vector32_f32out")
 
 
 @pytest.mark.parametrize("case", list(CASES))
