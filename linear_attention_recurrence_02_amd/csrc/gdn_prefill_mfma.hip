@@ -63,8 +63,9 @@
 // A null v stands for zero values and a null O for no output rows (the
 // segmented form's state-map runs).
 // Template variants: kGated fuses the block's gated RMS norm into the output
-// step (the gate rows fetched into LDS a period ahead; the consumer waves
-// exchange per-row sums through LDS); kDoubling picks the T_ii method; kRank
+// step (each consumer wave loads its gate rows into registers at the start of
+// phase 2; the four consumer waves exchange per-row sums of O^2 through LDS);
+// kDoubling picks the T_ii method; kRank
 // walks a packed batch longest first (each workgroup ranks the sequence
 // lengths before the roles split, one barrier that both roles execute);
 // kPreop runs the block's pre-operations (causal conv over the FIFO window,
@@ -74,7 +75,10 @@
 // raw projections: each producer lane holds two channels of its block's rows
 // and of the three rows before them, so the conv window stays in the lane; K's
 // pre-operations run in phase 2 after the inverse chain, q's and v's in
-// phase 3 beside the consumers' W/U step.
+// phase 3 beside the consumers' W/U step; NCC = 1 splits the value columns of
+// each (sequence, head) over two workgroups of 64 columns (consumer waves of
+// 16 columns each, the producers' work and W repeated in both), for launches
+// whose workgroups then still all fit on the CUs at once.
 // Precision.  The state, the accumulators, U and the per-token scalars are
 // fp32.  K and Q enter the products as fp16 copies of the bf16 inputs, V as
 // the bf16 input itself (in bf16 products against P').  Correlated keys (the
