@@ -17,9 +17,12 @@
 // Work split: one 128-thread workgroup per (sequence, head); thread j owns
 // column j of the state (128 fp32 registers, S[i][j] for all i) and of D, so the
 // forward substitution for D runs down one column per thread with no barrier.
-// The chunk's K and Q (fp32, rows padded to 129 words so that the Gram phase's
-// row-strided reads hit distinct LDS banks), D, N and the masked decayed
-// QK^T live in LDS.
+// The chunk's K and Q (fp32, rows padded to 132 words: 16-byte rows, so that
+// the per-token products, which every thread reads in the same order, take
+// them four words at a time), D, N and the masked decayed QK^T live in LDS.
+// The chunk's V is staged into D's rows as they are loaded (thread j stages
+// and later overwrites only column j), so the per-token loop reads no global
+// memory; the per-token products k_t.S and q_t.S each sum four partial chains.
 //
 // A null v stands for zero values and a null O for no output rows.
 //
@@ -35,7 +38,7 @@ namespace gdn {
 namespace {
 
 constexpr int kThreads = 128;
-constexpr int kRow = kHeadDim + 1;   // padded LDS row stride for K and Q
+constexpr int kRow = kHeadDim + 4;   // LDS row stride for K and Q (16-byte rows)
 
 template <typename IO, typename OutT, int C, bool kGated>
 __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
@@ -44,7 +47,8 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t T,
     int64_t H, OutT *__restrict__ O, float *__restrict__ S_T, const IO *__restrict__ z,
     const float *__restrict__ norm_w, float eps) {
-    __shared__ float sK[C * kRow], sQ[C * kRow];
+    __shared__ __attribute__((aligned(16))) float sK[C * kRow];   // rows read as float4
+    __shared__ __attribute__((aligned(16))) float sQ[C * kRow];
     __shared__ float sD[C * kHeadDim];
     __shared__ float sN[C * C], sA[C * C];
     __shared__ double sG[C];
@@ -69,14 +73,16 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
 
         for (int idx = j; idx < C * kHeadDim; idx += kThreads) {
             const int t = idx / kHeadDim, i = idx % kHeadDim;
-            float kv = 0.f, qv = 0.f;
+            float kv = 0.f, qv = 0.f, vv = 0.f;
             if (t < nv) {
                 const int64_t off = ((row0 + t) * H + h) * kHeadDim + i;
                 kv = to_f32(k[off]);
                 qv = to_f32(q[off]);
+                if (v) vv = to_f32(v[off]);
             }
             sK[t * kRow + i] = kv;
             sQ[t * kRow + i] = qv;
+            sD[t * kHeadDim + i] = vv;   // column i is thread i's: it reads v_t there, then writes D
         }
         if (j < C) {
             const bool ok = j < nv;
@@ -119,14 +125,20 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
 
         // Column j: right-hand side, forward substitution, output rows.
         for (int t = 0; t < C; ++t) {
-            float ks = 0.f, qs = 0.f;
-            const float *kt = &sK[t * kRow], *qt = &sQ[t * kRow];
+            float ka[4] = {0.f, 0.f, 0.f, 0.f}, qa[4] = {0.f, 0.f, 0.f, 0.f};
+            const float4 *kt = reinterpret_cast<const float4 *>(&sK[t * kRow]);
+            const float4 *qt = reinterpret_cast<const float4 *>(&sQ[t * kRow]);
 #pragma unroll
-            for (int i = 0; i < kHeadDim; ++i) {
-                ks += kt[i] * S[i];
-                qs += qt[i] * S[i];
+            for (int i4 = 0; i4 < kHeadDim / 4; ++i4) {
+                const float4 a = kt[i4], b = qt[i4];
+                ka[0] += a.x * S[4 * i4];     qa[0] += b.x * S[4 * i4];
+                ka[1] += a.y * S[4 * i4 + 1]; qa[1] += b.y * S[4 * i4 + 1];
+                ka[2] += a.z * S[4 * i4 + 2]; qa[2] += b.z * S[4 * i4 + 2];
+                ka[3] += a.w * S[4 * i4 + 3]; qa[3] += b.w * S[4 * i4 + 3];
             }
-            const float vt = v && t < nv ? to_f32(v[((row0 + t) * H + h) * kHeadDim + j]) : 0.f;
+            const float ks = (ka[0] + ka[1]) + (ka[2] + ka[3]);
+            const float qs = (qa[0] + qa[1]) + (qa[2] + qa[3]);
+            const float vt = sD[t * kHeadDim + j];
             float r = sB[t] * (vt - sEG[t] * ks);
             for (int s = 0; s < t; ++s) r -= sN[t * C + s] * sD[s * kHeadDim + j];
             sD[t * kHeadDim + j] = r;
@@ -156,9 +168,15 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
         for (int i = 0; i < kHeadDim; ++i) S[i] *= eC;
         for (int t = 0; t < C; ++t) {
             const float wt = sEC[t] * sD[t * kHeadDim + j];
-            const float *kt = &sK[t * kRow];
+            const float4 *kt = reinterpret_cast<const float4 *>(&sK[t * kRow]);
 #pragma unroll
-            for (int i = 0; i < kHeadDim; ++i) S[i] += kt[i] * wt;
+            for (int i4 = 0; i4 < kHeadDim / 4; ++i4) {
+                const float4 a = kt[i4];
+                S[4 * i4] += a.x * wt;
+                S[4 * i4 + 1] += a.y * wt;
+                S[4 * i4 + 2] += a.z * wt;
+                S[4 * i4 + 3] += a.w * wt;
+            }
         }
         __syncthreads();   // LDS is rewritten by the next chunk
     }
