@@ -14,15 +14,18 @@
 // page's token_valid padding), so a partial last chunk leaves S exactly as after
 // the last real token.
 //
-// Work split: one 128-thread workgroup per (sequence, head); thread j owns
-// column j of the state (128 fp32 registers, S[i][j] for all i) and of D, so the
-// forward substitution for D runs down one column per thread with no barrier.
-// The chunk's K and Q (fp32, rows padded to 132 words: 16-byte rows, so that
-// the per-token products, which every thread reads in the same order, take
-// them four words at a time), D, N and the masked decayed QK^T live in LDS.
-// The chunk's V is staged into D's rows as they are loaded (thread j stages
-// and later overwrites only column j), so the per-token loop reads no global
-// memory; the per-token products k_t.S and q_t.S each sum four partial chains.
+// Work split: one 512-thread workgroup per (sequence, head).  Column j of the
+// state (and of D and O) belongs to the four lanes of one quad; lane p of the
+// quad holds the 32 state rows whose 16-byte groups are p, p + 4, ..., p + 28
+// (rows 16m + 4p .. 16m + 4p + 3, m = 0..7), so each product of a key or query
+// row with the column is four partial sums of 32 terms, added across the quad
+// by two DPP exchanges.  The forward substitution for D runs down the column
+// token by token inside the quad (every lane computes the same value; lane 0
+// writes it to LDS), with no barrier.  The chunk's K and Q (fp32, 16-byte
+// rows of 132 words: the four lanes of a quad read four distinct bank groups),
+// D, N and the masked decayed Q K^T live in LDS; the chunk's V is staged into
+// D's rows with K and Q, so the per-token loop reads no global memory.  The
+// Gram entries are computed the same way, one entry per quad.
 //
 // A null v stands for zero values and a null O for no output rows.
 //
@@ -37,8 +40,34 @@
 namespace gdn {
 namespace {
 
-constexpr int kThreads = 128;
-constexpr int kRow = kHeadDim + 4;   // LDS row stride for K and Q (16-byte rows)
+constexpr int kThreads = 512;                      // 8 waves, 128 quads
+constexpr int kQuads = kThreads / 4;
+constexpr int kRows = kHeadDim / 4;                // state rows per lane
+constexpr int kRow = kHeadDim + 4;                 // LDS row stride of K and Q (16-byte rows)
+
+// Sum over the four lanes of a quad, returned to all four (the same bits in
+// each: both steps add two values whose order does not change the sum).
+__device__ __forceinline__ float quad_sum(float x) {
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xb1, 0xf, 0xf, false));   // quad_perm [1,0,3,2]
+    x += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4e, 0xf, 0xf, false));   // quad_perm [2,3,0,1]
+    return x;
+}
+
+// Lane p's part of the product of a 128-word LDS row (16-byte aligned) with
+// the 32 values x it holds for its state rows: four partial chains.
+__device__ __forceinline__ float part_dot(const float *row, const float *x, int p) {
+    const float4 *r4 = reinterpret_cast<const float4 *>(row);
+    float a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int m = 0; m < kRows / 4; ++m) {
+        const float4 r = r4[4 * m + p];
+        a[0] += r.x * x[4 * m];
+        a[1] += r.y * x[4 * m + 1];
+        a[2] += r.z * x[4 * m + 2];
+        a[3] += r.w * x[4 * m + 3];
+    }
+    return (a[0] + a[1]) + (a[2] + a[3]);
+}
 
 template <typename IO, typename OutT, int C, bool kGated>
 __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
@@ -47,7 +76,8 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     const float *__restrict__ S0, const int32_t *__restrict__ cu_seqlens, int64_t T,
     int64_t H, OutT *__restrict__ O, float *__restrict__ S_T, const IO *__restrict__ z,
     const float *__restrict__ norm_w, float eps) {
-    __shared__ __attribute__((aligned(16))) float sK[C * kRow];   // rows read as float4
+    static_assert((C * C) % kQuads == 0, "Gram entries per quad");
+    __shared__ __attribute__((aligned(16))) float sK[C * kRow];
     __shared__ __attribute__((aligned(16))) float sQ[C * kRow];
     __shared__ float sD[C * kHeadDim];
     __shared__ float sN[C * C], sA[C * C];
@@ -55,42 +85,69 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
     __shared__ float sg[C], sB[C], sEG[C], sEC[C];
     __shared__ float sRed[2][kThreads / 64];
 
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wv = tid >> 6;
+    const int j = 16 * wv + (lane >> 2);           // the quad's state column
+    const int p = lane & 3;                        // the lane's row part
+    auto row_of = [&](int m) { return 16 * (m >> 2) + 4 * p + (m & 3); };
     const int64_t unit = blockIdx.x;
     const int64_t n = unit / H, h = unit % H;
-    const int j = threadIdx.x;
     int64_t start, len;
     sequence_span(cu_seqlens, n, T, start, len);
 
     const float nw = kGated ? norm_w[j] : 0.f;
-    float S[kHeadDim];
+    float S[kRows];
     const float *S0u = S0 ? S0 + unit * (kHeadDim * kHeadDim) : nullptr;
 #pragma unroll
-    for (int i = 0; i < kHeadDim; ++i) S[i] = S0u ? S0u[i * kHeadDim + j] : 0.f;
+    for (int m = 0; m < kRows; ++m) S[m] = S0u ? S0u[row_of(m) * kHeadDim + j] : 0.f;
+
+    // The rows of a chunk (zero past the sequence's end) are loaded into
+    // registers a chunk ahead: thread tid holds elements tid + 512 e of the
+    // chunk's C x 128 K, Q and V, and (tid < C) token tid's g and beta.
+    constexpr int kPer = C * kHeadDim / kThreads;
+    float xk[kPer], xq[kPer], xv[kPer], xg = 0.f, xb = 0.f;
+    auto fetch = [&](int64_t c0n) {
+        const int64_t rem = len - c0n;
+        const int nvn = static_cast<int>(rem < 0 ? 0 : (rem < C ? rem : C));
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = tid + kThreads * e, t = idx / kHeadDim, i = idx % kHeadDim;
+            xk[e] = xq[e] = xv[e] = 0.f;
+            if (t < nvn) {
+                const int64_t off = ((start + c0n + t) * H + h) * kHeadDim + i;
+                xk[e] = to_f32(k[off]);
+                xq[e] = to_f32(q[off]);
+                if (v) xv[e] = to_f32(v[off]);
+            }
+        }
+        if (tid < C) {
+            const bool ok = tid < nvn;
+            xg = ok ? g[(start + c0n + tid) * H + h] : 0.f;
+            xb = ok ? beta[(start + c0n + tid) * H + h] : 0.f;
+        }
+    };
+    if (len > 0) fetch(0);
 
     for (int64_t c0 = 0; c0 < len; c0 += C) {
         const int nv = static_cast<int>(len - c0 < C ? len - c0 : C);
         const int64_t row0 = start + c0;   // first token row of this chunk
 
-        for (int idx = j; idx < C * kHeadDim; idx += kThreads) {
-            const int t = idx / kHeadDim, i = idx % kHeadDim;
-            float kv = 0.f, qv = 0.f, vv = 0.f;
-            if (t < nv) {
-                const int64_t off = ((row0 + t) * H + h) * kHeadDim + i;
-                kv = to_f32(k[off]);
-                qv = to_f32(q[off]);
-                if (v) vv = to_f32(v[off]);
-            }
-            sK[t * kRow + i] = kv;
-            sQ[t * kRow + i] = qv;
-            sD[t * kHeadDim + i] = vv;   // column i is thread i's: it reads v_t there, then writes D
+        // stage the chunk's rows (V into D's rows, where each column is
+        // overwritten by its own quad), then load the next chunk's
+#pragma unroll
+        for (int e = 0; e < kPer; ++e) {
+            const int idx = tid + kThreads * e, t = idx / kHeadDim, i = idx % kHeadDim;
+            sK[t * kRow + i] = xk[e];
+            sQ[t * kRow + i] = xq[e];
+            sD[t * kHeadDim + i] = xv[e];
         }
-        if (j < C) {
-            const bool ok = j < nv;
-            sg[j] = ok ? g[(row0 + j) * H + h] : 0.f;
-            sB[j] = ok ? beta[(row0 + j) * H + h] : 0.f;
+        if (tid < C) {
+            sg[tid] = xg;
+            sB[tid] = xb;
         }
+        if (c0 + C < len) fetch(c0 + C);
         __syncthreads();
-        if (j == 0) {
+        if (tid == 0) {
             double acc = 0.0;
             for (int t = 0; t < C; ++t) {
                 acc += static_cast<double>(sg[t]);
@@ -98,84 +155,95 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
             }
         }
         __syncthreads();
-        if (j < C) {
-            sEG[j] = static_cast<float>(exp(sG[j]));
-            sEC[j] = static_cast<float>(exp(sG[C - 1] - sG[j]));
+        if (tid < C) {
+            sEG[tid] = static_cast<float>(exp(sG[tid]));
+            sEC[tid] = static_cast<float>(exp(sG[C - 1] - sG[tid]));
         }
-        // Gram entries (t, s) for s <= t, with the decay applied on the fp32 sums.
-        for (int e = j; e < C * C; e += kThreads) {
+        // Gram entries (t, s), one per quad at a time, with the decay applied on
+        // the fp32 sums; entries above the diagonal are zero.
+        for (int e = tid >> 2; e < C * C; e += kQuads) {
             const int t = e / C, s = e % C;
-            float nn = 0.f, aa = 0.f;
+            float kk = 0.f, qk = 0.f;
             if (s <= t) {
-                float kk = 0.f, qk = 0.f;
-                const float *kt = &sK[t * kRow], *qt = &sQ[t * kRow], *ks = &sK[s * kRow];
-#pragma unroll 16
-                for (int i = 0; i < kHeadDim; ++i) {
-                    kk += kt[i] * ks[i];
-                    qk += qt[i] * ks[i];
+                const float4 *kt = reinterpret_cast<const float4 *>(&sK[t * kRow]);
+                const float4 *qt = reinterpret_cast<const float4 *>(&sQ[t * kRow]);
+                const float4 *ks = reinterpret_cast<const float4 *>(&sK[s * kRow]);
+#pragma unroll
+                for (int m = 0; m < kRows / 4; ++m) {
+                    const float4 a = kt[4 * m + p], b = qt[4 * m + p], c = ks[4 * m + p];
+                    kk += a.x * c.x + a.y * c.y + a.z * c.z + a.w * c.w;
+                    qk += b.x * c.x + b.y * c.y + b.z * c.z + b.w * c.w;
                 }
-                const float E = expf(static_cast<float>(sG[t] - sG[s]));
-                aa = E * qk;
-                nn = s < t ? sB[t] * (E * kk) : 0.f;
             }
-            sN[e] = nn;
-            sA[e] = aa;
+            kk = quad_sum(kk);
+            qk = quad_sum(qk);
+            if (p == 0) {
+                float nn = 0.f, aa = 0.f;
+                if (s <= t) {
+                    const float E = expf(static_cast<float>(sG[t] - sG[s]));
+                    aa = E * qk;
+                    nn = s < t ? sB[t] * (E * kk) : 0.f;
+                }
+                sN[e] = nn;
+                sA[e] = aa;
+            }
         }
         __syncthreads();
 
-        // Column j: right-hand side, forward substitution, output rows.
+        // Column j, token by token: right-hand side, forward substitution, output.
         for (int t = 0; t < C; ++t) {
-            float ka[4] = {0.f, 0.f, 0.f, 0.f}, qa[4] = {0.f, 0.f, 0.f, 0.f};
-            const float4 *kt = reinterpret_cast<const float4 *>(&sK[t * kRow]);
-            const float4 *qt = reinterpret_cast<const float4 *>(&sQ[t * kRow]);
-#pragma unroll
-            for (int i4 = 0; i4 < kHeadDim / 4; ++i4) {
-                const float4 a = kt[i4], b = qt[i4];
-                ka[0] += a.x * S[4 * i4];     qa[0] += b.x * S[4 * i4];
-                ka[1] += a.y * S[4 * i4 + 1]; qa[1] += b.y * S[4 * i4 + 1];
-                ka[2] += a.z * S[4 * i4 + 2]; qa[2] += b.z * S[4 * i4 + 2];
-                ka[3] += a.w * S[4 * i4 + 3]; qa[3] += b.w * S[4 * i4 + 3];
+            const int64_t oi = ((row0 + t) * H + h) * kHeadDim + j;
+            float zf = 0.f;
+            if constexpr (kGated) {
+                if (p == 0 && t < nv) zf = to_f32(z[oi]);
             }
-            const float ks = (ka[0] + ka[1]) + (ka[2] + ka[3]);
-            const float qs = (qa[0] + qa[1]) + (qa[2] + qa[3]);
+            const float ks = quad_sum(part_dot(&sK[t * kRow], S, p));
+            const float qs = quad_sum(part_dot(&sQ[t * kRow], S, p));
             const float vt = sD[t * kHeadDim + j];
             float r = sB[t] * (vt - sEG[t] * ks);
-            for (int s = 0; s < t; ++s) r -= sN[t * C + s] * sD[s * kHeadDim + j];
-            sD[t * kHeadDim + j] = r;
             float o = sEG[t] * qs;
-            for (int s = 0; s <= t; ++s) o += sA[t * C + s] * sD[s * kHeadDim + j];
-            const int64_t oi = ((row0 + t) * H + h) * kHeadDim + j;
+#pragma unroll 4
+            for (int s = 0; s < t; ++s) {
+                const float ds = sD[s * kHeadDim + j];
+                r -= sN[t * C + s] * ds;
+                o += sA[t * C + s] * ds;
+            }
+            o += sA[t * C + t] * r;
+            if (p == 0) sD[t * kHeadDim + j] = r;
             if constexpr (kGated) {
-                float ss = o * o;
+                // the row's sum of o^2 over its 128 columns: one value per quad
+                float ss = p == 0 ? o * o : 0.f;
 #pragma unroll
-                for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
-                if ((j & 63) == 0) sRed[t & 1][j >> 6] = ss;
+                for (int off = 32; off >= 4; off >>= 1) ss += __shfl_xor(ss, off);
+                if (lane == 0) sRed[t & 1][wv] = ss;
                 __syncthreads();
-                const float ms = (sRed[t & 1][0] + sRed[t & 1][1]) * (1.f / kHeadDim);
-                if (t < nv) {
-                    const float zf = to_f32(z[oi]);
+                float tot = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < kThreads / 64; ++w2) tot += sRed[t & 1][w2];
+                const float ms = tot * (1.f / kHeadDim);
+                if (p == 0 && t < nv) {
                     const float silu = zf / (1.f + expf(-zf));
                     O[oi] = from_f32<OutT>(nw * (o / sqrtf(ms + eps)) * silu);
                 }
             } else {
-                if (O && t < nv) O[oi] = from_f32<OutT>(o);
+                if (O && p == 0 && t < nv) O[oi] = from_f32<OutT>(o);
             }
         }
 
         // Carry the state to the end of the chunk.
         const float eC = sEG[C - 1];
 #pragma unroll
-        for (int i = 0; i < kHeadDim; ++i) S[i] *= eC;
+        for (int m = 0; m < kRows; ++m) S[m] *= eC;
         for (int t = 0; t < C; ++t) {
             const float wt = sEC[t] * sD[t * kHeadDim + j];
             const float4 *kt = reinterpret_cast<const float4 *>(&sK[t * kRow]);
 #pragma unroll
-            for (int i4 = 0; i4 < kHeadDim / 4; ++i4) {
-                const float4 a = kt[i4];
-                S[4 * i4] += a.x * wt;
-                S[4 * i4 + 1] += a.y * wt;
-                S[4 * i4 + 2] += a.z * wt;
-                S[4 * i4 + 3] += a.w * wt;
+            for (int m = 0; m < kRows / 4; ++m) {
+                const float4 a = kt[4 * m + p];
+                S[4 * m] += a.x * wt;
+                S[4 * m + 1] += a.y * wt;
+                S[4 * m + 2] += a.z * wt;
+                S[4 * m + 3] += a.w * wt;
             }
         }
         __syncthreads();   // LDS is rewritten by the next chunk
@@ -183,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
 
     float *STu = S_T + unit * (kHeadDim * kHeadDim);
 #pragma unroll
-    for (int i = 0; i < kHeadDim; ++i) STu[i * kHeadDim + j] = S[i];
+    for (int m = 0; m < kRows; ++m) STu[row_of(m) * kHeadDim + j] = S[m];
 }
 
 template <typename IO, typename OutT, int C>
