@@ -20,8 +20,9 @@
 // (rows 16m + 4p .. 16m + 4p + 3, m = 0..7), so each product of a key or query
 // row with the column is four partial sums of 32 terms, added across the quad
 // by two DPP exchanges.  The forward substitution for D runs down the column
-// token by token inside the quad (every lane computes the same value; lane 0
-// writes it to LDS), with no barrier.  The chunk's K and Q (fp32, 16-byte
+// token by token inside the quad (every lane computes the same value and
+// stores it to LDS, so that no lane depends on another's store), with no
+// barrier.  The chunk's K and Q (fp32, 16-byte
 // rows of 132 words: the four lanes of a quad read four distinct bank groups),
 // D, N and the masked decayed Q K^T live in LDS; the chunk's V is staged into
 // D's rows with K and Q, so the per-token loop reads no global memory.  The
@@ -209,7 +210,9 @@ __global__ __launch_bounds__(kThreads) void prefill_valu_kernel(
                 o += sA[t * C + s] * ds;
             }
             o += sA[t * C + t] * r;
-            if (p == 0) sD[t * kHeadDim + j] = r;
+            // every lane of the quad stores the value it computed (the same in all
+            // four), so each lane later reads only its own stores of D
+            sD[t * kHeadDim + j] = r;
             if constexpr (kGated) {
                 // the row's sum of o^2 over its 128 columns: one value per quad
                 float ss = p == 0 ? o * o : 0.f;
