@@ -195,7 +195,10 @@ __global__ __launch_bounds__(256, 2) void prefill_short_kernel(
                         btt[e] * (__builtin_amdgcn_exp2f(r16 < t ? g2t[e] - g2j : kNegInf) * acc[e]);
                 }
                 // T = (I + N)^-1, column r16 per lane: T_ic = [i == c] - sum_{j<i} N_ij T_jc.
-                // (the wave's own LDS writes above complete before its reads)
+                // The rows read below were stored by other lanes of this wave: the
+                // wave's LDS operations complete in order, and the fence keeps the
+                // compiler from moving the reads above the stores.
+                __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
                 float tc[CS];
 #pragma unroll
                 for (int i = 0; i < CS; ++i) {
