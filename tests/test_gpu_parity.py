@@ -14,6 +14,7 @@ import torch
 import oracle
 from linear_attention_recurrence_02_amd import inputs
 from linear_attention_recurrence_02_amd.binding import (GdnError, gdn_chunk_prefill,
+                                                        gdn_chunk_prefill_gated,
                                                         gdn_decode_step)
 from metrics import (TOL_BF16, TOL_F32, bf16_output_ok, spans_of, worst_slice_error)
 
@@ -233,6 +234,24 @@ def test_prefill_is_deterministic():
     a = run_prefill(w)
     b = run_prefill(w)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_vector_kernel_is_deterministic(chunk):
+    """The vector-ALU prompt kernel (fp32 inputs) bitwise equal from run to run,
+    plain and with the gated norm (each state column is shared by the four
+    lanes of a quad, which exchange partial sums and keep D in LDS)."""
+    w = inputs.prefill_workload(2, 150, 3, chunk=chunk, io_dtype=torch.float32, seed=19,
+                                device=DEV)
+    a = run_prefill(w)
+    b = run_prefill(w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    z, nw, eps = inputs.norm_gate(w, seed=19)
+    ya, sa = gdn_chunk_prefill_gated(w.q, w.k, w.v, w.g, w.beta, z, nw, eps, w.S0, None, chunk)
+    yb, sb = gdn_chunk_prefill_gated(w.q, w.k, w.v, w.g, w.beta, z, nw, eps, w.S0, None, chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(ya, yb) and torch.equal(sa, sb)
+    assert torch.equal(sa, a[1])       # the gated form's state is the plain form's
 
 
 def test_prefill_one_token_matches_decode_step():
