@@ -38,12 +38,15 @@ def check(w, O, S_T, label, S0=None):
         assert es <= TOL_BF16, es
 
 
-def test_long_workload_segmented():
-    # 1 x 4096 tokens x 16 heads in 16 segments of 256 tokens
+@pytest.mark.parametrize("L", [256, 512])
+def test_long_workload_segmented(L):
+    # 1 x 4096 tokens x 16 heads in 16 segments of 256 tokens (256 segment-heads,
+    # one workgroup each) or 8 of 512 (128 segment-heads, whose prompt-kernel
+    # runs split each unit's value columns over two workgroups)
     w = inputs.long_prefill(device=DEV)
-    O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, 64, 256)
+    O, S_T = gdn_chunk_prefill_segmented(w.q, w.k, w.v, w.g, w.beta, w.S0, 64, L)
     torch.cuda.synchronize()
-    check(w, O, S_T, "long, 16 segments")
+    check(w, O, S_T, f"long, segments of {L}")
 
 
 @pytest.mark.parametrize("T,L", [(1000, 64), (1000, 256), (1000, 384), (1000, 512), (2100, 64)])
